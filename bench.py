@@ -1,0 +1,205 @@
+"""Throughput benchmark: FP32 SGEMM GFLOP/s on one MI355X and % of FP32 peak.
+
+One step is one sgemm_f32 call (the whole hot path) on the 4096^3 workload
+(alpha = 1, beta = 0, A and B uniform in [-1, 1), seeded), inputs already in
+HBM. W untimed warm-up steps, then K timed steps between a device
+synchronisation on each side; per-step kernel durations come from HIP events
+recorded on the launch stream. Prints ONE JSON line.
+
+Extra objects on that line:
+  roofline     - the GEMM kernel's achieved FLOP/s (2*M*N*K per launch / mean
+                 launch duration from the events) against MI355X's FP32 matrix
+                 peak (157.3 TFLOP/s), plus HBM traffic per launch from the
+                 committed rocprofv3 counter summary when it was taken on the
+                 current kernel source (else null).
+  cpu_baseline - the FP64 CPU oracle timed on this host's cores over a bounded
+                 sample of the same workload (whole output rows).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload S4096]
+                  [--variant auto|mfma_128x128|...] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP32_PEAK_TFLOPS = 157.3        # MI355X dense FP32 (matrix and packed-vector) peak
+FP32_VALU_PEAK_TFLOPS = 78.6    # unpacked v_fma_f32: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["fp32_gemm_tuning_amd/csrc/mfma.hip", "fp32_gemm_tuning_amd/csrc/valu_main.hip",
+                  "fp32_gemm_tuning_amd/csrc/common.hpp", "fp32_gemm_tuning_amd/csrc/ladder.hip"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(variant_name: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    was taken on other kernel sources, another kernel or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    if rec.get("kernel") != variant_name or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(w, A, B, C0, budget_s: float = 12.0):
+    """Time the oracle on whole output rows until ~budget_s of CPU work."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    chunk = max(threads * 4, 16)
+    done, t_total = 0, 0.0
+    while done < w.M and t_total < budget_s:
+        rows = np.arange(done, min(w.M, done + chunk))
+        t0 = time.perf_counter()
+        oracle.sgemm_ref_rows(A, B, C0, w.alpha, w.beta, rows)
+        t_total += time.perf_counter() - t0
+        done += rows.size
+        chunk = min(chunk * 2, w.M)
+    gflops = 2.0 * done * w.N * w.K / t_total / 1e9
+    return {"value": round(gflops, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.M} output rows of {w.name} ({w.M}x{w.N}x{w.K}), "
+                      f"FP64 accumulation, {t_total:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this SGEMM runs on a single MI355X; multi-GPU sharding is a design note only)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp32_gemm_tuning_amd as sg
+    from datagen import HEADLINE, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload or HEADLINE]
+    A, B, C0 = make_inputs(w)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.from_numpy(C0).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    if args.variant == "auto":
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        rc, vid = sg.sgemm_f32_plan(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC, w.N, cus)
+        assert rc == 0
+        call = lambda: sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC, w.N, sp)
+    else:
+        vid = sg.sgemm_f32_variant_by_name(args.variant)
+        if vid < 0:
+            print(f"unknown variant {args.variant}", file=sys.stderr)
+            return 2
+        call = lambda: sg.sgemm_f32_variant(vid, w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N,
+                                            w.beta, dC, w.N, sp)
+    vname = sg.sgemm_f32_variant_name(vid)
+
+    for _ in range(args.warmup):
+        rc = call()
+        if rc != 0:
+            print(f"sgemm_f32 failed: {rc} {sg.sgemm_f32_strerror(rc)}", file=sys.stderr)
+            return 1
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        rc = call()
+        ends[i].record(stream)
+        if rc != 0:
+            print(f"sgemm_f32 failed: {rc}", file=sys.stderr)
+            return 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+    region_ms = starts[0].elapsed_time(ends[-1])
+    ms_per_step = region_ms / K
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e9
+    kernel_ms = float(durs.mean())
+    achieved_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    is_valu = vname in ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa",
+                        "valu_main")
+    peak = FP32_VALU_PEAK_TFLOPS if is_valu else FP32_PEAK_TFLOPS
+    traffic = stored_traffic(vname, w.name)
+
+    out = {
+        "metric": "FP32 SGEMM GFLOP/s at N=4096 on 1 MI355X; % of FP32 peak",
+        "value": round(value, 1),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"sgemm {w.name} M=N=K={w.M}" if w.M == w.N == w.K else
+                   f"sgemm {w.name} M={w.M} N={w.N} K={w.K}",
+                   "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+                   "layout": "row-major, packed lda=K ldb=N ldc=N",
+                   "inputs": f"{w.dist}, seeds {w.seed_a}/{w.seed_b}",
+                   "kernel": vname},
+        "pct_of_fp32_peak": round(100.0 * value / 1e3 / FP32_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "alu" if is_valu else "mfma",
+                     "achieved": round(achieved_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved_tflops / peak, 4), "traffic": traffic,
+                     "kernel_ms_mean": round(kernel_ms, 4),
+                     "kernel_ms_min": round(float(durs.min()), 4),
+                     "flops_per_launch": int(flops)},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B, C0)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,185 @@
+"""Python binding of libsgemm_f32 (FP32 SGEMM for MI355X / gfx950).
+
+Argument marshalling only: every entry point forwards to the C ABI declared
+in include/sgemm_f32.h, and every step of the product runs in the library's
+HIP kernels. PyTorch, when used, only supplies device memory (``data_ptr``)
+and streams. If the shared library has not been built this package raises on
+import: there is no fallback implementation.
+
+C-ABI mirrors (same names, same argument order; matrices may be torch tensors
+or raw device addresses as ints; they return the C status code):
+    sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None)
+    sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None)
+    sgemm_f32_plan(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus) -> (code, variant)
+    sgemm_f32_num_variants(), sgemm_f32_variant_name(v), sgemm_f32_variant_by_name(s),
+    sgemm_f32_strerror(code), sgemm_f32_kernel_info(v) -> dict
+
+Tensor helper:
+    gemm(A, B, C, alpha=1.0, beta=0.0, variant=None, stream=None)
+        C <- alpha*A@B + beta*C for row-major float32 CUDA tensors; raises SgemmError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsgemm_f32.so")
+
+OK = 0
+ERR_VARIANT = -100
+ERR_UNSUPPORTED = -101
+ERR_TOO_LARGE = -102
+ERR_DEVICE = -103
+
+VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", "valu_main",
+            "mfma_128x128", "mfma_64x64", "mfma_skinny")
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, code: int, where: str = "sgemm_f32"):
+        self.code = int(code)
+        super().__init__(f"{where} returned {code}: {sgemm_f32_strerror(code)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m fp32_gemm_tuning_amd.build or __graft_entry__.build()); "
+            "there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, f32, vp, c_int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+    gemm_args = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64]
+    lib.sgemm_f32.argtypes = gemm_args + [vp]
+    lib.sgemm_f32.restype = c_int
+    lib.sgemm_f32_variant.argtypes = [c_int] + gemm_args + [vp]
+    lib.sgemm_f32_variant.restype = c_int
+    lib.sgemm_f32_plan.argtypes = gemm_args + [c_int, ctypes.POINTER(c_int)]
+    lib.sgemm_f32_plan.restype = c_int
+    lib.sgemm_f32_num_variants.argtypes = []
+    lib.sgemm_f32_num_variants.restype = c_int
+    lib.sgemm_f32_variant_name.argtypes = [c_int]
+    lib.sgemm_f32_variant_name.restype = ctypes.c_char_p
+    lib.sgemm_f32_variant_by_name.argtypes = [ctypes.c_char_p]
+    lib.sgemm_f32_variant_by_name.restype = c_int
+    lib.sgemm_f32_strerror.argtypes = [c_int]
+    lib.sgemm_f32_strerror.restype = ctypes.c_char_p
+    ip = ctypes.POINTER(c_int)
+    lib.sgemm_f32_kernel_info.argtypes = [c_int, ip, ip, ip, ip, ip]
+    lib.sgemm_f32_kernel_info.restype = c_int
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream, *tensors) -> int:
+    if stream is None:
+        for t in tensors:
+            if t is not None and not isinstance(t, int) and getattr(t, "is_cuda", False):
+                import torch
+                return int(torch.cuda.current_stream(t.device).cuda_stream)
+        return 0
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return int(_lib.sgemm_f32(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B),
+                              int(ldb), float(beta), _ptr(C), int(ldc), _stream(stream, C, A, B)))
+
+
+def sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None) -> int:
+    return int(_lib.sgemm_f32_variant(int(variant), int(M), int(N), int(K), float(alpha), _ptr(A),
+                                      int(lda), _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+                                      _stream(stream, C, A, B)))
+
+
+def sgemm_f32_plan(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus) -> Tuple[int, int]:
+    v = ctypes.c_int(-2)
+    rc = _lib.sgemm_f32_plan(int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B),
+                             int(ldb), float(beta), _ptr(C), int(ldc), int(num_cus),
+                             ctypes.byref(v))
+    return int(rc), int(v.value)
+
+
+def sgemm_f32_num_variants() -> int:
+    return int(_lib.sgemm_f32_num_variants())
+
+
+def sgemm_f32_variant_name(variant: int) -> Optional[str]:
+    s = _lib.sgemm_f32_variant_name(int(variant))
+    return None if s is None else s.decode()
+
+
+def sgemm_f32_variant_by_name(name: str) -> int:
+    return int(_lib.sgemm_f32_variant_by_name(name.encode()))
+
+
+def sgemm_f32_strerror(code: int) -> str:
+    return _lib.sgemm_f32_strerror(int(code)).decode()
+
+
+def sgemm_f32_kernel_info(variant: int) -> dict:
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    rc = _lib.sgemm_f32_kernel_info(int(variant), *[ctypes.byref(v) for v in vals])
+    if rc != 0:
+        raise SgemmError(rc, "sgemm_f32_kernel_info")
+    keys = ("threads", "lds_bytes", "regs", "scratch_bytes", "wg_per_cu")
+    return dict(zip(keys, (v.value for v in vals)))
+
+
+def _variant_id(variant) -> Optional[int]:
+    if variant is None:
+        return None
+    if isinstance(variant, str):
+        v = sgemm_f32_variant_by_name(variant)
+        if v < 0:
+            raise ValueError(f"unknown variant {variant!r}")
+        return v
+    return int(variant)
+
+
+def _ld(t, rows: int, cols: int, name: str) -> int:
+    if str(t.dtype) != "torch.float32":
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major with unit column stride")
+    return max(int(t.stride(0)) if rows > 1 else cols, cols, 1)
+
+
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=None, stream=None):
+    """C <- alpha * A @ B + beta * C on row-major float32 CUDA tensors (in place)."""
+    M, K = int(A.shape[0]), int(A.shape[1])
+    N = int(B.shape[1])
+    lda = _ld(A, M, K, "A")
+    ldb = _ld(B, K, N, "B")
+    ldc = _ld(C, M, N, "C")
+    for t, n in ((A, "A"), (B, "B"), (C, "C")):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+    v = _variant_id(variant)
+    if v is None:
+        rc = sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    else:
+        rc = sgemm_f32_variant(v, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    if rc != 0:
+        raise SgemmError(rc)
+    return C

@@ -1,0 +1,260 @@
+// C-ABI entry points of libsgemm_f32: argument checks, quick returns, the
+// host-side choice of kernel variant, and the launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "sgemm_f32.h"
+
+namespace sgemm {
+
+static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
+    &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
+    &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny,
+};
+
+static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+static int64_t max1(int64_t v) { return v > 1 ? v : 1; }
+
+// Argument checks in signature order; returns -i for the first bad argument i
+// (M = 1). A and B must be valid only when they are read (M, N, K > 0 and
+// alpha != 0); C only when it is written (M, N > 0).
+static int validate(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, const float* C, int64_t ldc) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
+    const bool writes_c = M > 0 && N > 0;
+    if (reads_ab && (A == nullptr || misaligned4(A))) return -5;
+    if (lda < max1(K)) return -6;
+    if (reads_ab && (B == nullptr || misaligned4(B))) return -7;
+    if (ldb < max1(N)) return -8;
+    if (writes_c && (C == nullptr || misaligned4(C))) return -10;
+    if (ldc < max1(N)) return -11;
+    return 0;
+}
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Variant choice. Following the pages' tile selection ("Optimizing Matrix
+// Multiply on CUDA, Part 2", "Selecting Among Three Kernels"; "Part 1",
+// "Small and Odd Sizes"), the host estimates the work of the busiest compute
+// unit for each candidate and takes the smallest: with T tiles dealt out to C
+// compute units, the busiest one gets ceil(T / C) tiles, each costing
+// BM * BN * K / efficiency, where efficiency is the candidate's measured
+// per-tile throughput relative to mfma_128 (a small tile re-reads more of A
+// and B per flop and issues fewer MFMAs between barriers).
+// ---------------------------------------------------------------------------
+struct Candidate {
+    int variant;
+    int bm, bn;
+    double efficiency;
+};
+
+static const Candidate kCandidates[] = {
+    {SGEMM_F32_MFMA_128, 128, 128, 1.00},
+    {SGEMM_F32_MFMA_64, 64, 64, 0.65},
+};
+// At or below this many rows the skinny kernel (HBM-bound regime) is used.
+static const int64_t kSkinnyMaxM = 32;
+
+static int choose(int64_t M, int64_t N, int64_t K, int num_cus) {
+    if (num_cus < 1) num_cus = 1;
+    if (M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
+    int best = -1;
+    double best_cost = 0.0;
+    for (const Candidate& c : kCandidates) {
+        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+        const double cost = (double)cdiv(tiles, num_cus) * c.bm * c.bn * (double)K / c.efficiency;
+        if (best < 0 || cost < best_cost) {
+            best = c.variant;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+// ---------------------------------------------------------------------------
+// Per-device compute-unit count, queried once per device.
+// ---------------------------------------------------------------------------
+static constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cus[kMaxDevices];
+
+static int device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SGEMM_F32_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int cached = g_cus[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *cus = cached;
+            return 0;
+        }
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return SGEMM_F32_ERR_DEVICE;
+    if (dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+    *cus = n;
+    return 0;
+}
+
+int xcd_remap_enabled() {
+    static std::atomic<int> v{-1};
+    int cur = v.load(std::memory_order_relaxed);
+    if (cur < 0) {
+        const char* e = getenv("SGEMM_F32_XCD_REMAP");
+        cur = (e && e[0] == '0') ? 0 : 1;
+        v.store(cur, std::memory_order_relaxed);
+    }
+    return cur;
+}
+
+static Args make_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float beta, float* C, int64_t ldc) {
+    Args a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.M = (int32_t)M;
+    a.N = (int32_t)N;
+    a.K = (int32_t)K;
+    a.alpha = alpha;
+    a.beta = beta;
+    return a;
+}
+
+static int run(int forced, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+               int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+               void* stream) {
+    if (forced >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    int rc = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return 0;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const Args a = make_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    if (K == 0 || alpha == 0.0f) {
+        const hipError_t e = launch_scale(a, s);
+        return e == hipSuccess ? 0 : (int)e;
+    }
+    int v = forced;
+    if (v < 0) {
+        int cus = 0;
+        rc = device_cus(&cus);
+        if (rc) return rc;
+        v = choose(M, N, K, cus);
+        // Shapes beyond a kernel's 32-bit buffer offsets fall back to the
+        // plain-pointer register-tiled rung.
+        if (kTable[v]->check(a) != 0) v = SGEMM_F32_REG_2D;
+    }
+    const Variant& var = *kTable[v];
+    rc = var.check(a);
+    if (rc) return rc;
+    const hipError_t e = var.launch(a, s);
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+}  // namespace sgemm
+
+using namespace sgemm;
+
+extern "C" {
+
+SGEMM_F32_API int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                            int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                            int64_t ldc, void* stream) {
+    return run(-1, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+SGEMM_F32_API int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, float alpha,
+                                    const float* A, int64_t lda, const float* B, int64_t ldb,
+                                    float beta, float* C, int64_t ldc, void* stream) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    return run(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                                 int64_t lda, const float* B, int64_t ldb, float beta,
+                                 const float* C, int64_t ldc, int num_cus, int* variant) {
+    (void)beta;
+    int rc = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc) return rc;
+    if (variant == nullptr) return -12;
+    if (M == 0 || N == 0 || K == 0 || alpha == 0.0f) {
+        *variant = -1;
+        return 0;
+    }
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
+    const Args a = make_args(M, N, K, alpha, A, lda, B, ldb, beta, const_cast<float*>(C), ldc);
+    int v = choose(M, N, K, num_cus);
+    if (kTable[v]->check(a) != 0) v = SGEMM_F32_REG_2D;
+    *variant = v;
+    return 0;
+}
+
+SGEMM_F32_API int sgemm_f32_num_variants(void) { return SGEMM_F32_NUM_VARIANTS; }
+
+SGEMM_F32_API const char* sgemm_f32_variant_name(int variant) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return nullptr;
+    return kTable[variant]->name;
+}
+
+SGEMM_F32_API int sgemm_f32_variant_by_name(const char* name) {
+    if (name == nullptr) return -1;
+    for (int i = 0; i < SGEMM_F32_NUM_VARIANTS; ++i)
+        if (std::strcmp(kTable[i]->name, name) == 0) return i;
+    return -1;
+}
+
+SGEMM_F32_API const char* sgemm_f32_strerror(int code) {
+    switch (code) {
+        case 0: return "success";
+        case -1: return "argument 1 (M) is negative";
+        case -2: return "argument 2 (N) is negative";
+        case -3: return "argument 3 (K) is negative";
+        case -5: return "argument 5 (A) is NULL or not 4-byte aligned";
+        case -6: return "argument 6 (lda) is smaller than max(1, K)";
+        case -7: return "argument 7 (B) is NULL or not 4-byte aligned";
+        case -8: return "argument 8 (ldb) is smaller than max(1, N)";
+        case -10: return "argument 10 (C) is NULL or not 4-byte aligned";
+        case -11: return "argument 11 (ldc) is smaller than max(1, N)";
+        case -12: return "output pointer is NULL";
+        case SGEMM_F32_ERR_VARIANT: return "variant id out of range";
+        case SGEMM_F32_ERR_UNSUPPORTED: return "variant cannot run this shape or alignment";
+        case SGEMM_F32_ERR_TOO_LARGE: return "a size exceeds what the kernel can index";
+        case SGEMM_F32_ERR_DEVICE: return "no usable HIP device";
+        default: break;
+    }
+    if (code > 0) return hipGetErrorString((hipError_t)code);
+    return "unknown error";
+}
+
+SGEMM_F32_API int sgemm_f32_kernel_info(int variant, int* threads, int* lds_bytes, int* regs,
+                                        int* scratch_bytes, int* wg_per_cu) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SGEMM_F32_ERR_DEVICE;
+    const Variant& v = *kTable[variant];
+    hipFuncAttributes attr;
+    hipError_t e = hipFuncGetAttributes(&attr, v.kernel);
+    if (e != hipSuccess) return (int)e;
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, v.kernel, v.threads, 0);
+    if (e != hipSuccess) return (int)e;
+    if (threads) *threads = v.threads;
+    if (lds_bytes) *lds_bytes = (int)attr.sharedSizeBytes;
+    if (regs) *regs = attr.numRegs;
+    if (scratch_bytes) *scratch_bytes = (int)attr.localSizeBytes;
+    if (wg_per_cu) *wg_per_cu = occ;
+    return 0;
+}
+
+}  // extern "C"

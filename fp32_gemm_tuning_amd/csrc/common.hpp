@@ -1,0 +1,96 @@
+// Shared pieces of the gfx950 SGEMM kernels: the argument block, the
+// epilogue, buffer-resource loads with out-of-range-reads-zero, and the
+// workgroup -> output-tile mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm {
+
+// One GEMM problem, passed by value as the kernel argument block.
+// Row-major: A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j].
+struct Args {
+    const float* A;
+    const float* B;
+    float* C;
+    int64_t lda, ldb, ldc;
+    int32_t M, N, K;
+    float alpha, beta;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Epilogue for one output: C = alpha*acc + beta*C0, where C0 is read only
+// when beta != 0 (so an uninitialised C cannot leak NaN into the result).
+__device__ __forceinline__ void store_out(const Args& a, int64_t i, int64_t j, float acc) {
+    float* p = a.C + i * a.ldc + j;
+    float v = a.alpha * acc;
+    if (a.beta != 0.0f) v = __builtin_fmaf(a.beta, *p, v);
+    *p = v;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources. A raw buffer load whose byte offset is at or past the
+// resource's num_records returns zeros instead of touching memory, which is
+// how the tiled kernels fill the parts of a tile that hang off the matrix:
+// every masked element gets the offset OOB, far past any extent the host
+// allows (extents are checked to stay below 2^31 bytes).
+// ---------------------------------------------------------------------------
+constexpr uint32_t OOB = 0x80000000u;
+// Third descriptor word for gfx9-family raw buffers: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int RSRC_FLAGS = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, (int)bytes,
+                                             RSRC_FLAGS);
+}
+
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup id -> (tile row, tile column).
+//
+// MI355X spreads consecutive workgroup ids of a dispatch round-robin over its
+// 8 XCDs, each with its own L2. The mapping first renumbers ids so that each
+// XCD receives one contiguous range of logical ids, then walks the tile grid
+// in column-major order within bands of `group_m` tile rows, so that the
+// workgroups that run together on one XCD cover a compact block of C and
+// share their A row panels and B column panels in that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int NUM_XCD = 8;
+
+__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int group_m,
+                                        bool xcd_remap, int& tm, int& tn) {
+    const int T = tiles_m * tiles_n;
+    int L = wg;
+    if (xcd_remap) {
+        const int x = wg % NUM_XCD, idx = wg / NUM_XCD;
+        const int q = T / NUM_XCD, r = T % NUM_XCD;
+        L = x * q + (x < r ? x : r) + idx;
+    }
+    const int per_group = group_m * tiles_n;
+    const int g = L / per_group;
+    const int first_m = g * group_m;
+    const int rows = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in = L - g * per_group;
+    tm = first_m + in % rows;
+    tn = in / rows;
+}
+
+// LDS swizzle for a 16-float row of an untransposed A tile read with 16-byte
+// loads: 16-byte chunk q of row r is stored at chunk q ^ swz16(r). With 8
+// consecutive lanes on 8 consecutive rows (fragment reads) or 4 lanes per row
+// on 2-4 consecutive rows (tile fills), every 16-byte access of a lane group
+// lands in a distinct bank group for both a 32-bank and a 64-bank LDS.
+__device__ __forceinline__ int swz16(int r) { return ((r >> 2) ^ (r & 2)) & 3; }
+
+}  // namespace sgemm

@@ -1,0 +1,457 @@
+// FP32 matrix-core SGEMM kernels for gfx950 (true FP32 MFMA: FP32 operands,
+// FP32 accumulate; no reduced-precision input types).
+//
+// SGEMM is a dense contraction, so on CDNA4 it belongs on the matrix cores:
+// v_mfma_f32_32x32x2_f32 multiplies a 32x2 by a 2x32 block and accumulates a
+// 32x32 block (4096 FLOP per wave instruction); v_mfma_f32_16x16x4_f32 does
+// 16x4 by 4x16 into 16x16 (2048 FLOP). The pages' CUDA-core ladder (block
+// tile in shared memory, per-thread register patch, double buffering; see
+// "Optimizing Matrix Multiply on CUDA, Part 2", "Overlapping Loads and
+// Computation") maps onto this as: block tile in LDS, per-wave accumulator
+// blocks held in registers, one MFMA per (row block, column block, k pair).
+//
+// Operand layouts (one wave, lane l):
+//   32x32x2: A operand lane l = A[l%32][l/32], B operand = B[l/32][l%32],
+//            result register r of lane l = C[8*(r/4) + 4*(l/32) + r%4][l%32].
+//   16x16x4: A operand lane l = A[l%16][l/16], B operand = B[l/16][l%16],
+//            result register r of lane l = C[4*(l/16) + r][l%16].
+// The k index inside one MFMA is only a summation index, so each half (or
+// quarter) of the wave walks its own contiguous run of k: lane l feeds the
+// instruction's k slot l/32 (l/16) from k = 8*(l/32) + s (4*(l/16) + s) at
+// step s. A lane's A values for a slice are then 8 (4) consecutive floats of
+// one row of the untransposed A tile, read with 16-byte LDS loads, and no
+// transposed copy of A is needed; the B values are single floats of one row
+// of the B tile, consecutive across lanes.
+//
+// Edges: every global read goes through a buffer resource; masked elements
+// get an out-of-range offset and read as zero, so partial tiles need no
+// branches in the K loop; only the final stores are guarded.
+#include "kernels.hpp"
+#include "sgemm_f32.h"
+
+namespace sgemm {
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The LDS tile fill of one K slice: global -> registers (issued early), then
+// registers -> LDS after the current slice's math. VEC: 16-byte chunks (needs
+// K, N, lda, ldb multiples of 4 and 16-byte aligned A, B); otherwise 4-byte
+// elements with per-element masks.
+template <int BM, int BN, int BK, int NT, bool VEC>
+struct TileFill {
+    static constexpr int BNP = BN + 4;  // B tile pitch in floats
+    static constexpr int A_ELEMS = BM * BK / NT;   // floats of A per lane per slice
+    static constexpr int B_ELEMS = BK * BN / NT;
+    static_assert(A_ELEMS % 4 == 0 && B_ELEMS % 4 == 0, "tile/threads mismatch");
+    static_assert(BK == 16, "A tile rows are 4 swizzled 16-byte chunks");
+
+    f32x4 ra[A_ELEMS / 4];
+    f32x4 rb[B_ELEMS / 4];
+
+    // Global -> registers for slice starting at k0.
+    __device__ __forceinline__ void load(const Args& a, int t, int m0, int n0, int k0,
+                                         int rows_valid, int cols_valid) {
+        const int kk = (a.K - k0) < BK ? (a.K - k0) : BK;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+            a.B + (int64_t)k0 * a.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
+        if (VEC) {
+#pragma unroll
+            for (int p = 0; p < A_ELEMS / 4; ++p) {
+                const int c = t + NT * p, row = c >> 2, q = c & 3;
+                const bool ok = row < rows_valid && 4 * q + 4 <= kk;
+                ra[p] = buf_load4(rA, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
+            }
+#pragma unroll
+            for (int p = 0; p < B_ELEMS / 4; ++p) {
+                const int c = t + NT * p, krow = c / (BN / 4), nq = c % (BN / 4);
+                const bool ok = krow < kk && 4 * nq + 4 <= cols_valid;
+                rb[p] = buf_load4(rB, ok ? (uint32_t)((krow * (int)a.ldb + 4 * nq) * 4) : OOB);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < A_ELEMS; ++p) {
+                const int e = t + NT * p, row = e / BK, kq = e % BK;
+                const bool ok = row < rows_valid && kq < kk;
+                ra[p >> 2][p & 3] = buf_load1(rA, ok ? (uint32_t)((row * (int)a.lda + kq) * 4) : OOB);
+            }
+#pragma unroll
+            for (int p = 0; p < B_ELEMS; ++p) {
+                const int e = t + NT * p, krow = e / BN, n = e % BN;
+                const bool ok = krow < kk && n < cols_valid;
+                rb[p >> 2][p & 3] = buf_load1(rB, ok ? (uint32_t)((krow * (int)a.ldb + n) * 4) : OOB);
+            }
+        }
+    }
+
+    // Registers -> LDS. As: BM rows of 16 floats, 16-byte chunk q of row r at
+    // chunk q ^ swz16(r). Bs: BK rows of BN floats at pitch BNP.
+    __device__ __forceinline__ void store(float* As, float* Bs, int t) const {
+        if (VEC) {
+#pragma unroll
+            for (int p = 0; p < A_ELEMS / 4; ++p) {
+                const int c = t + NT * p, row = c >> 2, q = c & 3;
+                *(f32x4*)&As[row * BK + ((q ^ swz16(row)) << 2)] = ra[p];
+            }
+#pragma unroll
+            for (int p = 0; p < B_ELEMS / 4; ++p) {
+                const int c = t + NT * p, krow = c / (BN / 4), nq = c % (BN / 4);
+                *(f32x4*)&Bs[krow * BNP + 4 * nq] = rb[p];
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < A_ELEMS; ++p) {
+                const int e = t + NT * p, row = e / BK, kq = e % BK;
+                As[row * BK + ((((kq >> 2) ^ swz16(row)) << 2) | (kq & 3))] = ra[p >> 2][p & 3];
+            }
+#pragma unroll
+            for (int p = 0; p < B_ELEMS; ++p) {
+                const int e = t + NT * p, krow = e / BN, n = e % BN;
+                Bs[krow * BNP + n] = rb[p >> 2][p & 3];
+            }
+        }
+    }
+};
+
+// ===========================================================================
+// mfma_128: 128x128 block tile, BK = 16, 256 lanes = 4 waves in a 2x2 grid,
+// each wave a 64x64 sub-tile = 2x2 blocks of 32x32 accumulated with
+// v_mfma_f32_32x32x2_f32 (64 accumulator registers per lane). Double-buffered
+// LDS: slice s+1 is loaded into registers while slice s is multiplied, then
+// stored into the other LDS buffer; one barrier per slice.
+// ===========================================================================
+constexpr int M128_BM = 128, M128_BN = 128, M128_BK = 16, M128_GROUP_M = 8;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_mfma128(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    constexpr int BM = M128_BM, BN = M128_BN, BK = M128_BK;
+    using Fill = TileFill<BM, BN, BK, 256, VEC>;
+    constexpr int BNP = Fill::BNP;
+    __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BNP];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // LDS read offsets of this lane's fragments (floats).
+    int aoff[2][2], boff[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int row = wm * 64 + bi * 32 + c;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) aoff[bi][u] = row * BK + (((2 * h + u) ^ swz16(row)) << 2);
+    }
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) boff[bj] = (8 * h) * BNP + wn * 64 + bj * 32 + c;
+
+    const int nslices = (a.K + BK - 1) / BK;
+    Fill fill;
+    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
+    fill.store(As[0], Bs[0], t);
+    __syncthreads();
+
+    for (int s = 0; s < nslices; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
+
+        const float* Ac = As[cur];
+        const float* Bc = Bs[cur];
+        float af[2][8], bf[2][8];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const f32x4 lo = *(const f32x4*)&Ac[aoff[bi][0]];
+            const f32x4 hi = *(const f32x4*)&Ac[aoff[bi][1]];
+            af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
+            af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+        }
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+
+        if (s + 1 < nslices) fill.store(As[cur ^ 1], Bs[cur ^ 1], t);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = wm * 64 + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int j = wn * 64 + bj * 32 + c;
+                if (i < rows_valid && j < cols_valid)
+                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+            }
+}
+
+// Host-side limits shared by the tiled MFMA kernels: per-slice buffer extents
+// must stay below 2^31 bytes.
+static bool extents_ok(const Args& a, int BM, int BN, int BK) {
+    const int64_t ea = ((int64_t)(BM - 1) * a.lda + BK) * 4;
+    const int64_t eb = ((int64_t)(BK - 1) * a.ldb + BN) * 4;
+    return ea < (int64_t)OOB && eb < (int64_t)OOB;
+}
+
+static bool vec_ok(const Args& a) {
+    return !((a.K & 3) || (a.N & 3) || (a.lda & 3) || (a.ldb & 3) || !aligned16(a.A) ||
+             !aligned16(a.B));
+}
+
+static int check_mfma128(const Args& a) {
+    if (!extents_ok(a, M128_BM, M128_BN, M128_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, M128_BM) * cdiv(a.N, M128_BN);
+    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_mfma128(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, M128_BM), tn = (int)cdiv(a.N, M128_BN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
+    if (vec_ok(a))
+        hipLaunchKernelGGL(k_mfma128<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL(k_mfma128<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
+                          (const void*)k_mfma128<true>, 256};
+
+// ===========================================================================
+// mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2
+// blocks of 16x16 accumulated with v_mfma_f32_16x16x4_f32. Four times as many
+// tiles as mfma_128 for shapes whose 128x128 grid leaves compute units idle.
+// ===========================================================================
+constexpr int M64_BM = 64, M64_BN = 64, M64_BK = 16, M64_GROUP_M = 8;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_mfma64(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    constexpr int BM = M64_BM, BN = M64_BN, BK = M64_BK;
+    using Fill = TileFill<BM, BN, BK, 256, VEC>;
+    constexpr int BNP = Fill::BNP;
+    __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BNP];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M64_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int g = lane >> 4, c = lane & 15;
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int aoff[2], boff[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int row = wm * 32 + bi * 16 + c;
+        aoff[bi] = row * BK + ((g ^ swz16(row)) << 2);
+    }
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) boff[bj] = (4 * g) * BNP + wn * 32 + bj * 16 + c;
+
+    const int nslices = (a.K + BK - 1) / BK;
+    Fill fill;
+    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
+    fill.store(As[0], Bs[0], t);
+    __syncthreads();
+
+    for (int s = 0; s < nslices; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
+        const float* Ac = As[cur];
+        const float* Bc = Bs[cur];
+        f32x4 af[2];
+        float bf[2][4];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) af[bi] = *(const f32x4*)&Ac[aoff[bi]];
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[bi][k], bf[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+        if (s + 1 < nslices) fill.store(As[cur ^ 1], Bs[cur ^ 1], t);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = wm * 32 + bi * 16 + 4 * g + r;
+                const int j = wn * 32 + bj * 16 + c;
+                if (i < rows_valid && j < cols_valid)
+                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+            }
+}
+
+static int check_mfma64(const Args& a) {
+    if (!extents_ok(a, M64_BM, M64_BN, M64_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, M64_BM) * cdiv(a.N, M64_BN);
+    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_mfma64(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, M64_BM), tn = (int)cdiv(a.N, M64_BN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
+    if (vec_ok(a))
+        hipLaunchKernelGGL(k_mfma64<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL(k_mfma64<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfma64 = {"mfma_64x64", check_mfma64, launch_mfma64, (const void*)k_mfma64<true>,
+                         256};
+
+// ===========================================================================
+// mfma_skinny: for few rows (near-GEMV, e.g. 16 x 8192 x 8192, where B is
+// read once and the shape is bound by HBM bandwidth). A workgroup owns a
+// 16x32 tile of C and all of K; its 16 waves each take one contiguous 1/16 of
+// K, so 16 independent streams of B loads are in flight per compute unit.
+// Operands go straight from global memory into MFMA registers (no LDS tile):
+// lane l of a wave reads row k = 4*(l/16) + s of its K run at column l%16 of
+// each 16-column block, 64 contiguous bytes per quarter-wave, and a 16-byte
+// run of 4 consecutive k of row l%16 of A. At the end the 16 partial tiles
+// are summed in a fixed order through LDS (deterministic) and the epilogue
+// writes C.
+// ===========================================================================
+constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KU = 64;  // k per unrolled step
+
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int kchunk) {
+    __shared__ float red[SK_WAVES][2][4][64];
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int m0 = tm * SK_BM, n0 = tn * SK_BN;
+    const int rows_valid = (a.M - m0) < SK_BM ? (a.M - m0) : SK_BM;
+    const int cols_valid = (a.N - n0) < SK_BN ? (a.N - n0) : SK_BN;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    const int kbeg = w * kchunk;
+    const int kend = (a.K - kbeg) < kchunk ? a.K : kbeg + kchunk;
+
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = kbeg; k0 < kend; k0 += SK_KU) {
+        const int kk = (a.K - k0) < SK_KU ? (a.K - k0) : SK_KU;  // rows present in memory
+        const int klim = kend - k0;                              // rows this wave owns
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+            a.B + (int64_t)k0 * a.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
+        f32x4 af[SK_KU / 16];
+        float b0[SK_KU / 4], b1[SK_KU / 4];
+#pragma unroll
+        for (int u = 0; u < SK_KU / 16; ++u) {
+            const int kq = 16 * u + 4 * g;  // this lane's 4 consecutive k
+            if (VEC) {
+                const bool ok = c < rows_valid && kq + 4 <= klim;
+                af[u] = buf_load4(rA, ok ? (uint32_t)((c * (int)a.lda + kq) * 4) : OOB);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = c < rows_valid && kq + e < klim;
+                    af[u][e] = buf_load1(rA, ok ? (uint32_t)((c * (int)a.lda + kq + e) * 4) : OOB);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kr = kq + e;
+                const bool okr = kr < klim;
+                const uint32_t base = (uint32_t)(kr * (int)a.ldb) * 4;
+                b0[4 * u + e] = buf_load1(rB, okr && c < cols_valid ? base + c * 4 : OOB);
+                b1[4 * u + e] = buf_load1(rB, okr && c + 16 < cols_valid ? base + (c + 16) * 4 : OOB);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SK_KU / 16; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b0[4 * u + e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b1[4 * u + e], acc1, 0, 0, 0);
+            }
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        red[w][0][r][lane] = acc0[r];
+        red[w][1][r][lane] = acc1[r];
+    }
+    __syncthreads();
+    if (threadIdx.x < SK_BM * SK_BN) {
+        const int i = threadIdx.x / SK_BN, j = threadIdx.x % SK_BN;
+        const int bj = j >> 4, src = (i >> 2) * 16 + (j & 15), r = i & 3;
+        float v = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < SK_WAVES; ++ww) v += red[ww][bj][r][src];
+        if (i < rows_valid && j < cols_valid) store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+    }
+}
+
+static int skinny_kchunk(const Args& a) {
+    // Equal K runs per wave, each a multiple of 16.
+    const int64_t per = cdiv(a.K, SK_WAVES);
+    return (int)(cdiv(per, 16) * 16);
+}
+
+static int check_skinny(const Args& a) {
+    const int64_t ea = ((int64_t)(SK_BM - 1) * a.lda + SK_KU) * 4;
+    const int64_t eb = ((int64_t)(SK_KU - 1) * a.ldb + SK_BN) * 4;
+    if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, SK_BM) * cdiv(a.N, SK_BN);
+    return tiles <= max_workgroups(1024) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_skinny(const Args& a, hipStream_t s) {
+    const int tn = (int)cdiv(a.N, SK_BN);
+    const dim3 grid((unsigned)(cdiv(a.M, SK_BM) * tn)), block(1024);
+    const bool vec = !((a.K & 3) || (a.lda & 3) || !aligned16(a.A));
+    if (vec)
+        hipLaunchKernelGGL(k_mfma_skinny<true>, grid, block, 0, s, a, tn, skinny_kchunk(a));
+    else
+        hipLaunchKernelGGL(k_mfma_skinny<false>, grid, block, 0, s, a, tn, skinny_kchunk(a));
+    return hipGetLastError();
+}
+
+Variant kMfmaSkinny = {"mfma_skinny", check_skinny, launch_skinny,
+                             (const void*)k_mfma_skinny<true>, 1024};
+
+}  // namespace sgemm

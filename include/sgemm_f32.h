@@ -1,0 +1,153 @@
+/*
+ * sgemm_f32 -- single-precision general matrix multiply for AMD MI355X (gfx950).
+ *
+ *   C = alpha * A * B + beta * C          (row-major, FP32 in, FP32 accumulate, FP32 out)
+ *
+ * The operation is the one every source page builds toward: each output
+ * C[i][j] is alpha times the K-term dot product of row i of A and column j of
+ * B, plus beta times the old C[i][j] ("GEMM from scratch", Module 02, "One
+ * Thread Per Output"; "Optimizing Matrix Multiply on CUDA, Part 1", "Counting
+ * the Work"). The arithmetic is plain FP32 -- no TF32-style or reduced
+ * precision inputs ("100 Days of GPU, Day 44", "The honest target": FP32 in,
+ * FP32 compute type, FP32 out). The status-code return mirrors the library
+ * call those pages score against (Day 44, "Five paths, one table").
+ *
+ * Layout (all three matrices row-major, element (r, c) at base[r * ld + c]):
+ *   A : M x K, leading dimension lda >= max(1, K)
+ *   B : K x N, leading dimension ldb >= max(1, N)
+ *   C : M x N, leading dimension ldc >= max(1, N)
+ * A, B and C are device pointers owned by the caller; they must be 4-byte
+ * aligned. C must not overlap A or B. The library allocates no memory on the
+ * call path and keeps no per-call state.
+ *
+ * Semantics the pages leave open (BLAS conventions):
+ *   - M == 0 or N == 0: returns 0 and touches no memory.
+ *   - K == 0 or alpha == 0: A and B are not read; C = beta * C.
+ *   - beta == 0: C is write-only (its old contents, even NaN, are ignored).
+ *   - Summation order is unspecified; results are deterministic for a given
+ *     device, variant and input (no atomics). FP32 fused multiply-adds are used.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronizing.
+ *
+ * Return codes (int):
+ *     0                     success
+ *    -i  (i = 1..11)        argument i of sgemm_f32 is invalid, counting M as 1:
+ *                           1 M<0, 2 N<0, 3 K<0, 5 A null or misaligned,
+ *                           6 lda too small, 7 B null or misaligned, 8 ldb too
+ *                           small, 10 C null or misaligned, 11 ldc too small.
+ *                           (A, B, C are only required when they are read or
+ *                           written.) sgemm_f32_variant uses the same numbers.
+ *    SGEMM_F32_ERR_VARIANT      variant id out of range
+ *    SGEMM_F32_ERR_UNSUPPORTED  the forced variant cannot run this shape or
+ *                               alignment (e.g. a 16-byte-load rung with a
+ *                               leading dimension that is not a multiple of 4)
+ *    SGEMM_F32_ERR_TOO_LARGE    a size exceeds what the kernel can index
+ *    SGEMM_F32_ERR_DEVICE       no usable HIP device
+ *   > 0                     a hipError_t reported by the HIP runtime at launch
+ *
+ * Thread safety: all entry points are reentrant.
+ */
+#ifndef SGEMM_F32_H
+#define SGEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SGEMM_F32_API __attribute__((visibility("default")))
+#else
+#define SGEMM_F32_API
+#endif
+
+#define SGEMM_F32_OK 0
+#define SGEMM_F32_ERR_VARIANT (-100)
+#define SGEMM_F32_ERR_UNSUPPORTED (-101)
+#define SGEMM_F32_ERR_TOO_LARGE (-102)
+#define SGEMM_F32_ERR_DEVICE (-103)
+
+/* Kernel variants. The first six are the rungs of the pages' optimisation
+ * ladder, rebuilt for wave64; the rest are the gfx950 kernels the automatic
+ * dispatch chooses from. Every variant computes the same product. */
+enum sgemm_f32_variant_id {
+    /* one lane per output, consecutive lanes walk down a column of C
+       ("GEMM from scratch", Module 02) */
+    SGEMM_F32_NAIVE = 0,
+    /* consecutive lanes take consecutive columns of C (Module 03) */
+    SGEMM_F32_COALESCED = 1,
+    /* 16x16 tiles of A and B staged in LDS (Module 04; Day 44 step 3) */
+    SGEMM_F32_LDS_TILED = 2,
+    /* each lane owns a column of 8 outputs (Module 05; Day 44 step 4) */
+    SGEMM_F32_REG_1D = 3,
+    /* 128x128 block tile, 8x8 outputs per lane (Module 05; Day 44 step 5;
+       Part 1, "Stage 3: Register Tiling") */
+    SGEMM_F32_REG_2D = 4,
+    /* plus 16-byte loads and a transposed A tile, unpadded (Module 06;
+       Day 44 step 6); needs 16-byte aligned rows */
+    SGEMM_F32_VEC4_TRANSA = 5,
+    /* vector-FMA main kernel: wave64 warp tiles, double-buffered K loop,
+       conflict-free transposed A tile (Part 2 of "Optimizing Matrix
+       Multiply on CUDA") */
+    SGEMM_F32_VALU_MAIN = 6,
+    /* FP32 matrix-core kernel, 128x128 block tile (v_mfma_f32_32x32x2_f32) */
+    SGEMM_F32_MFMA_128 = 7,
+    /* FP32 matrix-core kernel, 64x64 block tile for shapes with few 128x128
+       tiles (v_mfma_f32_16x16x4_f32) */
+    SGEMM_F32_MFMA_64 = 8,
+    /* FP32 matrix-core kernel for M <= a few tens of rows (near-GEMV): 16-row
+       tiles, the K loop split across the waves of a workgroup */
+    SGEMM_F32_MFMA_SKINNY = 9,
+    SGEMM_F32_NUM_VARIANTS = 10
+};
+
+/* C = alpha*A*B + beta*C, kernel chosen automatically (see sgemm_f32_plan). */
+SGEMM_F32_API int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                            int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+                            int64_t ldc, void *stream);
+
+/* Same operation and return codes, with the kernel forced to `variant`. */
+SGEMM_F32_API int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, float alpha,
+                                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                                    float beta, float *C, int64_t ldc, void *stream);
+
+/* The variant sgemm_f32 would launch for these arguments on a device with
+ * `num_cus` compute units. Host-only: reads no memory through A, B or C (only
+ * their addresses, for alignment) and makes no HIP call. Writes the variant
+ * id to *variant and returns 0, or returns the same argument errors as
+ * sgemm_f32 (-12 if variant is NULL). For a quick-return case (M, N == 0,
+ * K == 0 or alpha == 0) *variant is set to -1. */
+SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
+                                 int64_t lda, const float *B, int64_t ldb, float beta,
+                                 const float *C, int64_t ldc, int num_cus, int *variant);
+
+/* Number of variants (SGEMM_F32_NUM_VARIANTS). */
+SGEMM_F32_API int sgemm_f32_num_variants(void);
+
+/* Short name of a variant ("naive", ..., "mfma_skinny"), or NULL if out of range.
+ * The string is static. */
+SGEMM_F32_API const char *sgemm_f32_variant_name(int variant);
+
+/* Variant id for a name, or -1. */
+SGEMM_F32_API int sgemm_f32_variant_by_name(const char *name);
+
+/* Static description of a return code. Never NULL. */
+SGEMM_F32_API const char *sgemm_f32_strerror(int code);
+
+/* Launch shape of a variant's main kernel on the current device, as the
+ * pages print it before timing (Day 44, "Five paths, one table": registers,
+ * spills, resident blocks): workgroup size, static LDS bytes, registers per
+ * lane as the runtime reports them, scratch (spill) bytes per lane and the
+ * number of workgroups resident per compute unit. Any output pointer may be
+ * NULL. Returns 0, SGEMM_F32_ERR_VARIANT, SGEMM_F32_ERR_DEVICE or a positive
+ * hipError_t. */
+SGEMM_F32_API int sgemm_f32_kernel_info(int variant, int *threads, int *lds_bytes, int *regs,
+                                        int *scratch_bytes, int *wg_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_F32_H */

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function the public header declares, and its argument checks, names,
+error strings and variant choice behave as documented. None of these calls
+launches a kernel (argument errors and the M == 0 / N == 0 quick return are
+decided before any HIP call; sgemm_f32_plan is host-only by contract)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_tuning_amd as sg
+from datagen import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
+
+
+def _header_text():
+    return open(HEADER).read()
+
+
+def test_every_declared_function_is_exported():
+    names = re.findall(r"SGEMM_F32_API\s+[^;]*?\b(sgemm_f32\w*)\s*\(", _header_text())
+    assert len(names) >= 8
+    lib = ctypes.CDLL(sg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sgemm_f32.h but not exported"
+
+
+def test_variant_enum_matches_names():
+    enum = dict((m.group(1), int(m.group(2))) for m in
+                re.finditer(r"SGEMM_F32_(\w+)\s*=\s*(\d+)", _header_text()))
+    assert enum["NUM_VARIANTS"] == sg.sgemm_f32_num_variants() == len(sg.VARIANTS)
+    for i, name in enumerate(sg.VARIANTS):
+        assert sg.sgemm_f32_variant_name(i) == name
+        assert sg.sgemm_f32_variant_by_name(name) == i
+    assert sg.sgemm_f32_variant_name(-1) is None
+    assert sg.sgemm_f32_variant_name(len(sg.VARIANTS)) is None
+    assert sg.sgemm_f32_variant_by_name("nope") == -1
+    assert enum["MFMA_128"] == sg.VARIANTS.index("mfma_128x128")
+
+
+@pytest.mark.parametrize("code", [0, -1, -2, -3, -5, -6, -7, -8, -10, -11, -12, -100, -101,
+                                  -102, -103, -999])
+def test_strerror_is_static_text(code):
+    s = sg.sgemm_f32_strerror(code)
+    assert isinstance(s, str) and len(s) > 3
+
+
+# Fake but aligned device addresses: only their alignment is inspected on the
+# paths exercised here.
+P = 1 << 20
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4), -1),
+    ((4, -1, 4, 1.0, P, 4, P, 4, 0.0, P, 4), -2),
+    ((4, 4, -1, 1.0, P, 4, P, 4, 0.0, P, 4), -3),
+    ((4, 4, 4, 1.0, 0, 4, P, 4, 0.0, P, 4), -5),
+    ((4, 4, 4, 1.0, P + 2, 4, P, 4, 0.0, P, 4), -5),
+    ((4, 4, 8, 1.0, P, 7, P, 4, 0.0, P, 4), -6),
+    ((4, 4, 4, 1.0, P, 4, 0, 4, 0.0, P, 4), -7),
+    ((4, 5, 4, 1.0, P, 4, P, 4, 0.0, P, 5), -8),
+    ((4, 4, 4, 1.0, P, 4, P, 4, 0.0, 0, 4), -10),
+    ((4, 4, 4, 1.0, P, 4, P, 4, 0.0, P + 1, 4), -10),
+    ((4, 6, 4, 1.0, P, 4, P, 6, 0.0, P, 5), -11),
+    ((0, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 3), -11),   # ld checked even when M == 0
+])
+def test_argument_errors(args, code):
+    assert sg.sgemm_f32(*args, stream=0) == code
+    assert sg.sgemm_f32_variant(0, *args, stream=0) == code
+    assert sg.sgemm_f32_plan(*args, 256)[0] == code
+
+
+def test_unread_operands_may_be_null():
+    # M == 0 or N == 0: nothing is read or written, returns 0 without a launch
+    assert sg.sgemm_f32(0, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, stream=0) == 0
+    assert sg.sgemm_f32(4, 0, 4, 1.0, 0, 4, 0, 1, 0.0, 0, 1, stream=0) == 0
+    # K == 0 or alpha == 0: A and B not needed (plan reports the quick return)
+    assert sg.sgemm_f32_plan(4, 4, 0, 1.0, 0, 1, 0, 4, 0.5, P, 4, 256) == (0, -1)
+    assert sg.sgemm_f32_plan(4, 4, 4, 0.0, 0, 4, 0, 4, 0.5, P, 4, 256) == (0, -1)
+
+
+def test_bad_variant_id():
+    args = (4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    assert sg.sgemm_f32_variant(-1, *args, stream=0) == sg.ERR_VARIANT
+    assert sg.sgemm_f32_variant(99, *args, stream=0) == sg.ERR_VARIANT
+
+
+def _plan(M, N, K, lda=None, ldb=None, ldc=None, cus=256, off=0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    rc, v = sg.sgemm_f32_plan(M, N, K, 1.0, P + off, lda, P, ldb, 0.0, P, ldc, cus)
+    assert rc == 0
+    return sg.sgemm_f32_variant_name(v)
+
+
+def test_plan_picks_matrix_core_kernels_for_the_workloads():
+    w = WORKLOADS
+    assert _plan(4096, 4096, 4096) == "mfma_128x128"
+    assert _plan(w["S2048"].M, w["S2048"].N, w["S2048"].K) == "mfma_128x128"
+    assert _plan(w["S8192"].M, w["S8192"].N, w["S8192"].K) == "mfma_128x128"
+    assert _plan(w["S4092"].M, w["S4092"].N, w["S4092"].K) == "mfma_128x128"
+    # 96 tiles of 128x128 on 256 compute units: the 64x64 tile wins
+    assert _plan(w["R_odd"].M, w["R_odd"].N, w["R_odd"].K) == "mfma_64x64"
+    assert _plan(w["R_skinny"].M, w["R_skinny"].N, w["R_skinny"].K) == "mfma_skinny"
+    assert _plan(256, 256, 256) == "mfma_64x64"
+
+
+def test_plan_busiest_cu_rule():
+    # 1024 tiles of 128^2 on 256 CUs: 4 per CU. 64^2 tiles: 16 per CU at 0.65
+    # efficiency -> 128^2 wins. At 2 CUs the tile count no longer matters.
+    assert _plan(4096, 4096, 64, cus=256) == "mfma_128x128"
+    assert _plan(1025, 1025, 64, cus=256) == "mfma_64x64"
+
+
+def test_plan_falls_back_when_offsets_exceed_32_bits():
+    # lda so large that even a 64-row panel spans more than 2^31 bytes
+    assert _plan(256, 256, 16, lda=1 << 24) == "reg2d"
+    assert _plan(256, 256, 16, ldb=1 << 26) == "reg2d"
