@@ -84,6 +84,82 @@ def cpu_baseline(w, A, B, C0, budget_s: float = 12.0):
                       f"FP64 accumulation, {t_total:.1f} s"}
 
 
+def time_calls(call, steps: int, warmup: int, stream):
+    """(per-launch durations in ms, timed-region ms) for `steps` calls."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        rc = call()
+        if rc != 0:
+            raise RuntimeError(f"sgemm call failed with {rc}")
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        rc = call()
+        ends[i].record(stream)
+        if rc != 0:
+            raise RuntimeError(f"sgemm call failed with {rc}")
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return durs, starts[0].elapsed_time(ends[-1])
+
+
+# Ladder rungs that would take minutes at the largest sizes are timed only on
+# the smaller workloads in a sweep.
+SLOW_RUNGS = {"naive", "coalesced", "lds_tiled", "reg1d"}
+SLOW_OK = {"S256", "R_odd", "R_skinny", "S2048"}
+
+
+def sweep(args, dev) -> int:
+    import torch
+
+    import fp32_gemm_tuning_amd as sg
+    from datagen import WORKLOADS, make_inputs
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    names = list(sg.VARIANTS) if args.variants == "all" else args.variants.split(",")
+    for wname in args.workloads.split(","):
+        w = WORKLOADS[wname]
+        A, B, C0 = make_inputs(w)
+        dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C0))
+        for vname in ["auto"] + names:
+            if vname in SLOW_RUNGS and wname not in SLOW_OK:
+                continue
+            if vname == "auto":
+                call = lambda: sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta,
+                                            dC, w.N, sp)
+                cus = torch.cuda.get_device_properties(dev).multi_processor_count
+                _, vid = sg.sgemm_f32_plan(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta,
+                                           dC, w.N, cus)
+                label = "auto:" + sg.sgemm_f32_variant_name(vid)
+            else:
+                vid = sg.sgemm_f32_variant_by_name(vname)
+                call = (lambda vid=vid: sg.sgemm_f32_variant(vid, w.M, w.N, w.K, w.alpha, dA,
+                                                             w.K, dB, w.N, w.beta, dC, w.N, sp))
+                label = vname
+            slow = vname in SLOW_RUNGS
+            rc = call()
+            if rc == sg.ERR_UNSUPPORTED:     # e.g. a 16-byte-load rung on odd leading dims
+                print(json.dumps({"sweep": True, "workload": wname, "variant": label,
+                                  "skipped": sg.sgemm_f32_strerror(rc)}), flush=True)
+                continue
+            durs, region = time_calls(call, 3 if slow else args.steps,
+                                      1 if slow else args.warmup, stream)
+            kms = float(durs.mean())
+            print(json.dumps({"sweep": True, "workload": wname, "variant": label,
+                              "kernel_ms_mean": round(kms, 4),
+                              "kernel_ms_min": round(float(durs.min()), 4),
+                              "gflops": round(w.flops / (kms * 1e-3) / 1e9, 1),
+                              "pct_fp32_peak": round(100 * w.flops / (kms * 1e-3) / 1e12 /
+                                                     FP32_PEAK_TFLOPS, 2),
+                              "hbm_gbs_min_bytes": round(w.bytes_min / (kms * 1e-3) / 1e9, 1)}),
+                  flush=True)
+        del dA, dB, dC
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +168,13 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every variant on --workloads (one JSON line each)")
+    ap.add_argument("--workloads", default="S256,R_odd,R_skinny,S2048,S4092,S4096,S8192")
+    ap.add_argument("--variants", default="all")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -110,6 +193,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.calib_copy:
+        n = args.calib_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.sweep:
+        return sweep(args, dev)
     w = WORKLOADS[args.workload or HEADLINE]
     A, B, C0 = make_inputs(w)
     dA = torch.from_numpy(A).to(dev)
