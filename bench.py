@@ -84,6 +84,31 @@ def cpu_baseline(w, A, B, C0, budget_s: float = 12.0):
                       f"FP64 accumulation, {t_total:.1f} s"}
 
 
+def measured_peaks(dev, stream, cus: int) -> dict:
+    """TFLOP/s of the library's peak-rate probes (unpacked FP32 FMA and both
+    FP32 MFMA shapes), each timed with HIP events on the launch stream."""
+    import torch
+
+    import fp32_gemm_tuning_amd as sg
+    wgs = cus * 8
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    res = {}
+    for kind, name, iters in ((0, "valu_fma_f32", 4096), (1, "mfma_f32_32x32x2", 512),
+                              (2, "mfma_f32_16x16x4", 512)):
+        best = 0.0
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc, flops = sg.sgemm_f32_peak_probe(kind, wgs, iters, out, stream.cuda_stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"peak probe {name} failed: {rc}")
+            best = max(best, flops / (a.elapsed_time(b) * 1e-3) / 1e12)
+        res[name] = round(best, 2)
+    return res
+
+
 def time_calls(call, steps: int, warmup: int, stream):
     """(per-launch durations in ms, timed-region ms) for `steps` calls."""
     import numpy as np
@@ -172,6 +197,8 @@ def main() -> int:
                     help="time every variant on --workloads (one JSON line each)")
     ap.add_argument("--workloads", default="S256,R_odd,R_skinny,S2048,S4092,S4096,S8192")
     ap.add_argument("--variants", default="all")
+    ap.add_argument("--peak", action="store_true",
+                    help="only run the peak-rate probes and print them")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -203,6 +230,11 @@ def main() -> int:
         del src, dst
     if args.sweep:
         return sweep(args, dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.peak:
+        print(json.dumps({"measured_peak_tflops": measured_peaks(dev, torch.cuda.current_stream(dev),
+                                                                 cus)}), flush=True)
+        return 0
     w = WORKLOADS[args.workload or HEADLINE]
     A, B, C0 = make_inputs(w)
     dA = torch.from_numpy(A).to(dev)
@@ -212,7 +244,6 @@ def main() -> int:
     sp = stream.cuda_stream
 
     if args.variant == "auto":
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
         rc, vid = sg.sgemm_f32_plan(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC, w.N, cus)
         assert rc == 0
         call = lambda: sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC, w.N, sp)
@@ -286,6 +317,10 @@ def main() -> int:
                      "flops_per_launch": int(flops)},
         "wall_s_timed_region": round(wall, 3),
     }
+    peaks = measured_peaks(dev, stream, cus)
+    mpk = peaks["valu_fma_f32"] if is_valu else peaks["mfma_f32_32x32x2"]
+    out["measured_peak_tflops"] = peaks
+    out["roofline"]["frac_of_measured_peak"] = round(achieved_tflops / mpk, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B, C0)
     else:

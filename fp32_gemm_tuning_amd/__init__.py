@@ -47,7 +47,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -m fp32_gemm_tuning_amd.build or __graft_entry__.build()); "
+            "(python fp32_gemm_tuning_amd/build.py or __graft_entry__.build()); "
             "there is no fallback path")
     lib = ctypes.CDLL(LIB_PATH)
     i64, f32, vp, c_int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
@@ -69,6 +69,8 @@ def _load() -> ctypes.CDLL:
     ip = ctypes.POINTER(c_int)
     lib.sgemm_f32_kernel_info.argtypes = [c_int, ip, ip, ip, ip, ip]
     lib.sgemm_f32_kernel_info.restype = c_int
+    lib.sgemm_f32_peak_probe.argtypes = [c_int, c_int, c_int, vp, vp, ctypes.POINTER(ctypes.c_double)]
+    lib.sgemm_f32_peak_probe.restype = c_int
     return lib
 
 
@@ -142,6 +144,14 @@ def sgemm_f32_kernel_info(variant: int) -> dict:
         raise SgemmError(rc, "sgemm_f32_kernel_info")
     keys = ("threads", "lds_bytes", "regs", "scratch_bytes", "wg_per_cu")
     return dict(zip(keys, (v.value for v in vals)))
+
+
+def sgemm_f32_peak_probe(kind: int, workgroups: int, iters: int, out, stream=None) -> Tuple[int, float]:
+    """Launch one peak-rate kernel (include/sgemm_f32_probe.h); returns (code, FLOPs)."""
+    fl = ctypes.c_double(0.0)
+    rc = _lib.sgemm_f32_peak_probe(int(kind), int(workgroups), int(iters), _ptr(out),
+                                   _stream(stream, out), ctypes.byref(fl))
+    return int(rc), float(fl.value)
 
 
 def _variant_id(variant) -> Optional[int]:

@@ -6,7 +6,8 @@ disabled for the device code (-packed-fp32-ops). The compiler's per-kernel
 resource remarks (VGPRs, AGPRs, spills, LDS, occupancy) are saved to
 _build/resource_usage.txt.
 
-Usage:  python -m fp32_gemm_tuning_amd.build [--jobs N]
+Usage:  python fp32_gemm_tuning_amd/build.py [--jobs N]
+(run as a file: importing the package loads the library this script builds)
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsgemm_f32.so")
 ARCH = os.environ.get("SGEMM_F32_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "ladder.hip", "valu_main.hip", "mfma.hip"]
+SOURCES = ["api.hip", "ladder.hip", "valu_main.hip", "mfma.hip", "peak.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}",

@@ -93,4 +93,15 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int gr
 // lands in a distinct bank group for both a 32-bank and a 64-bank LDS.
 __device__ __forceinline__ int swz16(int r) { return ((r >> 2) ^ (r & 2)) & 3; }
 
+// The same for 32-float rows (8 chunks): 8 consecutive rows, or the even and
+// the odd rows of 16 consecutive rows, map a fixed logical chunk to distinct
+// physical chunks, and 8 lanes filling one row hit 8 distinct chunks.
+__device__ __forceinline__ int swz32(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+template <int BK>
+__device__ __forceinline__ int swz_chunk(int r) {
+    static_assert(BK == 16 || BK == 32, "A tile rows are 16 or 32 floats");
+    return BK == 16 ? swz16(r) : swz32(r);
+}
+
 }  // namespace sgemm

@@ -40,10 +40,10 @@ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 template <int BM, int BN, int BK, int NT, bool VEC>
 struct TileFill {
     static constexpr int BNP = BN + 4;  // B tile pitch in floats
+    static constexpr int CPR = BK / 4;  // 16-byte chunks per A row
     static constexpr int A_ELEMS = BM * BK / NT;   // floats of A per lane per slice
     static constexpr int B_ELEMS = BK * BN / NT;
     static_assert(A_ELEMS % 4 == 0 && B_ELEMS % 4 == 0, "tile/threads mismatch");
-    static_assert(BK == 16, "A tile rows are 4 swizzled 16-byte chunks");
 
     f32x4 ra[A_ELEMS / 4];
     f32x4 rb[B_ELEMS / 4];
@@ -59,7 +59,7 @@ struct TileFill {
         if (VEC) {
 #pragma unroll
             for (int p = 0; p < A_ELEMS / 4; ++p) {
-                const int c = t + NT * p, row = c >> 2, q = c & 3;
+                const int c = t + NT * p, row = c / CPR, q = c % CPR;
                 const bool ok = row < rows_valid && 4 * q + 4 <= kk;
                 ra[p] = buf_load4(rA, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
             }
@@ -85,14 +85,14 @@ struct TileFill {
         }
     }
 
-    // Registers -> LDS. As: BM rows of 16 floats, 16-byte chunk q of row r at
-    // chunk q ^ swz16(r). Bs: BK rows of BN floats at pitch BNP.
+    // Registers -> LDS. As: BM rows of BK floats, 16-byte chunk q of row r at
+    // chunk q ^ swz_chunk<BK>(r). Bs: BK rows of BN floats at pitch BNP.
     __device__ __forceinline__ void store(float* As, float* Bs, int t) const {
         if (VEC) {
 #pragma unroll
             for (int p = 0; p < A_ELEMS / 4; ++p) {
-                const int c = t + NT * p, row = c >> 2, q = c & 3;
-                *(f32x4*)&As[row * BK + ((q ^ swz16(row)) << 2)] = ra[p];
+                const int c = t + NT * p, row = c / CPR, q = c % CPR;
+                *(f32x4*)&As[row * BK + ((q ^ swz_chunk<BK>(row)) << 2)] = ra[p];
             }
 #pragma unroll
             for (int p = 0; p < B_ELEMS / 4; ++p) {
@@ -103,7 +103,7 @@ struct TileFill {
 #pragma unroll
             for (int p = 0; p < A_ELEMS; ++p) {
                 const int e = t + NT * p, row = e / BK, kq = e % BK;
-                As[row * BK + ((((kq >> 2) ^ swz16(row)) << 2) | (kq & 3))] = ra[p >> 2][p & 3];
+                As[row * BK + ((((kq >> 2) ^ swz_chunk<BK>(row)) << 2) | (kq & 3))] = ra[p >> 2][p & 3];
             }
 #pragma unroll
             for (int p = 0; p < B_ELEMS; ++p) {
@@ -115,19 +115,51 @@ struct TileFill {
 };
 
 // ===========================================================================
-// mfma_128: 128x128 block tile, BK = 16, 256 lanes = 4 waves in a 2x2 grid,
-// each wave a 64x64 sub-tile = 2x2 blocks of 32x32 accumulated with
-// v_mfma_f32_32x32x2_f32 (64 accumulator registers per lane). Double-buffered
-// LDS: slice s+1 is loaded into registers while slice s is multiplied, then
-// stored into the other LDS buffer; one barrier per slice.
+// Tiled FP32 MFMA kernel, generic over the block tile BM x BN and the wave
+// tile WM x WN (each wave owns WM/32 x WN/32 blocks of 32x32 accumulated
+// with v_mfma_f32_32x32x2_f32). BK-deep slices, double-buffered LDS: slice
+// s+1 is loaded into registers while slice s is multiplied, then stored
+// into the other LDS buffer; one barrier per slice.
+//
+// mfma_128x128 is BM = BN = 128 with 4 waves of 64x64 (64 accumulator
+// registers per lane), BK = 16, and an occupancy target of 4 waves per SIMD
+// (4 workgroups per compute unit, accumulators in the unified VGPR file).
 // ===========================================================================
-constexpr int M128_BM = 128, M128_BN = 128, M128_BK = 16, M128_GROUP_M = 8;
+#ifndef SGEMM_M128_BK
+#define SGEMM_M128_BK 16
+#endif
+#ifndef SGEMM_M128_WAVES_PER_EU
+#define SGEMM_M128_WAVES_PER_EU 4
+#endif
+#ifndef SGEMM_M128_BM
+#define SGEMM_M128_BM 128
+#endif
+#ifndef SGEMM_M128_BN
+#define SGEMM_M128_BN 128
+#endif
+#ifndef SGEMM_M128_WM
+#define SGEMM_M128_WM 64
+#endif
+#ifndef SGEMM_M128_WN
+#define SGEMM_M128_WN 64
+#endif
+#ifndef SGEMM_M128_GROUP_M
+#define SGEMM_M128_GROUP_M 8
+#endif
+constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
+constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
+constexpr int M128_NT = (M128_BM / M128_WM) * (M128_BN / M128_WN) * 64;
 
-template <bool VEC>
-__global__ __launch_bounds__(256) void k_mfma128(Args a, int tiles_m, int tiles_n, int xcd_remap) {
-    constexpr int BM = M128_BM, BN = M128_BN, BK = M128_BK;
-    using Fill = TileFill<BM, BN, BK, 256, VEC>;
+template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    constexpr int WAVES_N = BN / WN;
+    constexpr int NT = (BM / WM) * WAVES_N * 64;
+    constexpr int BI = WM / 32, BJ = WN / 32;
+    using Fill = TileFill<BM, BN, BK, NT, VEC>;
     constexpr int BNP = Fill::BNP;
+    constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
     __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * BNP];
 
@@ -137,27 +169,33 @@ __global__ __launch_bounds__(256) void k_mfma128(Args a, int tiles_m, int tiles_
     const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
     const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WAVES_N, wn = w % WAVES_N;
     const int h = lane >> 5, c = lane & 31;
 
-    f32x16 acc[2][2];
+    f32x16 acc[BI][BJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < BJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // LDS read offsets of this lane's fragments (floats).
-    int aoff[2][2], boff[2];
+    // LDS read offsets of this lane's fragments (floats). In sub-step u the
+    // wave covers k = 16u .. 16u+15 of the slice: lanes 0-31 (h = 0) take
+    // k = 16u + s and lanes 32-63 take 16u + 8 + s at MFMA step s = 0..7.
+    int aoff[STEPS][BI][2], boff[STEPS][BJ];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-        const int row = wm * 64 + bi * 32 + c;
+    for (int u = 0; u < STEPS; ++u) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) aoff[bi][u] = row * BK + (((2 * h + u) ^ swz16(row)) << 2);
+        for (int bi = 0; bi < BI; ++bi) {
+            const int row = wm * WM + bi * 32 + c;
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+                aoff[u][bi][v] = row * BK + (((4 * u + 2 * h + v) ^ swz_chunk<BK>(row)) << 2);
+        }
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj) boff[u][bj] = (16 * u + 8 * h) * BNP + wn * WN + bj * 32 + c;
     }
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) boff[bj] = (8 * h) * BNP + wn * 64 + bj * 32 + c;
 
     const int nslices = (a.K + BK - 1) / BK;
     Fill fill;
@@ -171,39 +209,42 @@ __global__ __launch_bounds__(256) void k_mfma128(Args a, int tiles_m, int tiles_
 
         const float* Ac = As[cur];
         const float* Bc = Bs[cur];
-        float af[2][8], bf[2][8];
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
-            const f32x4 lo = *(const f32x4*)&Ac[aoff[bi][0]];
-            const f32x4 hi = *(const f32x4*)&Ac[aoff[bi][1]];
-            af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
-            af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+        for (int u = 0; u < STEPS; ++u) {
+            float af[BI][8], bf[BJ][8];
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi) {
+                const f32x4 lo = *(const f32x4*)&Ac[aoff[u][bi][0]];
+                const f32x4 hi = *(const f32x4*)&Ac[aoff[u][bi][1]];
+                af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
+                af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+            }
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[u][bj] + k * BNP];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                           acc[bi][bj], 0, 0, 0);
         }
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-            for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
-                                                                       acc[bi][bj], 0, 0, 0);
 
         if (s + 1 < nslices) fill.store(As[cur ^ 1], Bs[cur ^ 1], t);
         __syncthreads();
     }
 
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int i = wm * 64 + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int j = wn * 64 + bj * 32 + c;
+                const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int j = wn * WN + bj * 32 + c;
                 if (i < rows_valid && j < cols_valid)
                     store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
             }
@@ -222,24 +263,30 @@ static bool vec_ok(const Args& a) {
              !aligned16(a.B));
 }
 
+// The 4-byte fill keeps more loads in flight per lane; at 4 waves per SIMD it
+// would spill, so that instantiation targets 3.
+#define M128_KERNEL(VEC)                                                                   \
+    k_mfma_tile<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK,                               \
+                (VEC) ? SGEMM_M128_WAVES_PER_EU : 3, VEC>
+
 static int check_mfma128(const Args& a) {
     if (!extents_ok(a, M128_BM, M128_BN, M128_BK)) return SGEMM_F32_ERR_TOO_LARGE;
     const int64_t tiles = cdiv(a.M, M128_BM) * cdiv(a.N, M128_BN);
-    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+    return tiles <= max_workgroups(M128_NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
 }
 
 static hipError_t launch_mfma128(const Args& a, hipStream_t s) {
     const int tm = (int)cdiv(a.M, M128_BM), tn = (int)cdiv(a.N, M128_BN);
-    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(M128_NT);
     if (vec_ok(a))
-        hipLaunchKernelGGL(k_mfma128<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+        hipLaunchKernelGGL(M128_KERNEL(true), grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     else
-        hipLaunchKernelGGL(k_mfma128<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+        hipLaunchKernelGGL(M128_KERNEL(false), grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     return hipGetLastError();
 }
 
 Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
-                          (const void*)k_mfma128<true>, 256};
+                    (const void*)M128_KERNEL(true), M128_NT};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2

@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256) void k_valu_main(Args a, int tiles_m, int tile
         if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * V_BK, rows_valid, cols_valid);
         const float* Ac = As[cur];
         const float* Bc = Bs[cur];
-#pragma unroll
+        // Partial unroll: a full unroll lets the scheduler hoist all 16 steps'
+        // LDS loads (256 registers of fragments) and drop to one wave per SIMD.
+#pragma unroll 4
         for (int k = 0; k < V_BK; ++k) {
             const f32x4 a0 = *(const f32x4*)&Ac[k * V_BM + arow];
             const f32x4 a1 = *(const f32x4*)&Ac[k * V_BM + arow + 32];

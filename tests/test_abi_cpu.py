@@ -14,6 +14,7 @@ from datagen import WORKLOADS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "sgemm_f32_probe.h")
 
 
 def _header_text():
@@ -21,8 +22,9 @@ def _header_text():
 
 
 def test_every_declared_function_is_exported():
-    names = re.findall(r"SGEMM_F32_API\s+[^;]*?\b(sgemm_f32\w*)\s*\(", _header_text())
-    assert len(names) >= 8
+    text = _header_text() + open(PROBE_HEADER).read()
+    names = re.findall(r"SGEMM_F32_API\s+[^;]*?\b(sgemm_f32\w*)\s*\(", text)
+    assert len(names) >= 9 and "sgemm_f32_peak_probe" in names
     lib = ctypes.CDLL(sg.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sgemm_f32.h but not exported"
@@ -120,3 +122,11 @@ def test_plan_falls_back_when_offsets_exceed_32_bits():
     # lda so large that even a 64-row panel spans more than 2^31 bytes
     assert _plan(256, 256, 16, lda=1 << 24) == "reg2d"
     assert _plan(256, 256, 16, ldb=1 << 26) == "reg2d"
+
+
+def test_peak_probe_argument_checks():
+    # rejected before any launch
+    assert sg.sgemm_f32_peak_probe(7, 1, 1, P)[0] == -1
+    assert sg.sgemm_f32_peak_probe(0, 0, 1, P)[0] == -2
+    assert sg.sgemm_f32_peak_probe(0, 1, 0, P)[0] == -3
+    assert sg.sgemm_f32_peak_probe(0, 1, 1, 0)[0] == -4

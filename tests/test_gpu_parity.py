@@ -218,3 +218,14 @@ def test_main_kernels_at_2048(dev, variant):
     assert rc == 0
     for rep in check_sampled(C, A, B, C0, w.M, w.N, w.K, w.alpha, w.beta, False, seed=5):
         assert rep.ok, f"{variant}: {rep}"
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_peak_probe_runs(dev, kind):
+    out = torch.zeros(256 * 256, dtype=torch.float32, device=dev)
+    print(f"[gpu] peak probe kind={kind}", flush=True)
+    rc, flops = sg.sgemm_f32_peak_probe(kind, 256, 64, out)
+    torch.cuda.synchronize()
+    assert rc == 0 and flops > 0
+    vals = out.cpu().numpy()
+    assert np.all(np.isfinite(vals)) and np.any(vals != 0.0)
