@@ -149,6 +149,27 @@ def sweep(args, dev) -> int:
         w = WORKLOADS[wname]
         A, B, C0 = make_inputs(w)
         dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C0))
+        if args.context:
+            torch.backends.cuda.matmul.allow_tf32 = False
+            C1 = dC.clone()
+
+            def ctx():
+                if w.beta != 0.0:
+                    torch.addmm(C1, dA, dB, beta=w.beta, alpha=w.alpha, out=dC)
+                else:
+                    torch.mm(dA, dB, out=dC)
+                return 0
+            durs, _ = time_calls(ctx, args.steps, args.warmup, stream)
+            kms = float(durs.mean())
+            print(json.dumps({"sweep": True, "workload": wname, "variant": "context:torch.mm fp32",
+                              "kernel_ms_mean": round(kms, 4),
+                              "kernel_ms_min": round(float(durs.min()), 4),
+                              "gflops": round(w.flops / (kms * 1e-3) / 1e9, 1),
+                              "pct_fp32_peak": round(100 * w.flops / (kms * 1e-3) / 1e12 /
+                                                     FP32_PEAK_TFLOPS, 2),
+                              "hbm_gbs_min_bytes": round(w.bytes_min / (kms * 1e-3) / 1e9, 1)}),
+                  flush=True)
+            del C1
         for vname in ["auto"] + names:
             if vname in SLOW_RUNGS and wname not in SLOW_OK:
                 continue
@@ -197,6 +218,9 @@ def main() -> int:
                     help="time every variant on --workloads (one JSON line each)")
     ap.add_argument("--workloads", default="S256,R_odd,R_skinny,S2048,S4092,S4096,S8192")
     ap.add_argument("--variants", default="all")
+    ap.add_argument("--context", action="store_true",
+                    help="in a sweep, also time torch's FP32 matmul (vendor library, "
+                         "TF32 off) as context")
     ap.add_argument("--peak", action="store_true",
                     help="only run the peak-rate probes and print them")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",

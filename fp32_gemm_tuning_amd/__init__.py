@@ -34,7 +34,8 @@ ERR_TOO_LARGE = -102
 ERR_DEVICE = -103
 
 VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", "valu_main",
-            "mfma_128x128", "mfma_64x64", "mfma_skinny")
+            "mfma_128x128", "mfma_64x64", "mfma_skinny", "mfma_64x64_k4", "mfma_direct",
+            "mfma_64x128")
 
 
 class SgemmError(RuntimeError):

@@ -13,7 +13,7 @@ namespace sgemm {
 
 static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
-    &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny,
+    &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
@@ -43,34 +43,51 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 // Variant choice. Following the pages' tile selection ("Optimizing Matrix
 // Multiply on CUDA, Part 2", "Selecting Among Three Kernels"; "Part 1",
-// "Small and Odd Sizes"), the host estimates the work of the busiest compute
-// unit for each candidate and takes the smallest: with T tiles dealt out to C
-// compute units, the busiest one gets ceil(T / C) tiles, each costing
-// BM * BN * K / efficiency, where efficiency is the candidate's measured
-// per-tile throughput relative to mfma_128 (a small tile re-reads more of A
-// and B per flop and issues fewer MFMAs between barriers).
+// "Small and Odd Sizes"), the host estimates the time of the busiest compute
+// unit for each candidate and takes the smallest. With T tiles dealt out to
+// C compute units (MI355X places workgroups breadth-first, so the busiest
+// unit holds n = ceil(T / C) of them, all resident at once), that unit does
+// n * BM * BN * (K + K0) multiply-add units -- K0 standing for the per-tile
+// first fill and epilogue -- at a rate that depends on n: one workgroup per
+// unit leaves the matrix cores waiting on fills and barriers, four keep them
+// busy. The rates are measured fractions of peak on MI355X (interleaved
+// timing of the candidates on the square and odd workloads).
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
     int bm, bn;
-    double efficiency;
+    double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 workgroups per CU
 };
 
+// Listed in order of preference when estimates tie.
 static const Candidate kCandidates[] = {
-    {SGEMM_F32_MFMA_128, 128, 128, 1.00},
-    {SGEMM_F32_MFMA_64, 64, 64, 0.65},
+    {SGEMM_F32_MFMA_128, 128, 128, {0.80, 0.85, 0.91, 0.91}},
+    {SGEMM_F32_MFMA_64x128, 64, 128, {0.70, 0.78, 0.85, 0.88}},
+    {SGEMM_F32_MFMA_64, 64, 64, {0.60, 0.70, 0.72, 0.83}},
 };
+// Per-tile cost that does not shrink with K (first fill, epilogue), in units
+// of K.
+static const double kTileOverheadK = 256.0;
 // At or below this many rows the skinny kernel (HBM-bound regime) is used.
 static const int64_t kSkinnyMaxM = 32;
+// Below this many multiply-adds launch latency dominates and the fine-tiled
+// direct kernel is fastest (e.g. 256^3).
+static const double kTinyMacs = 64.0 * 1024 * 1024;
+
+static double eff_at(const Candidate& c, int64_t n) {
+    return n <= 1 ? c.eff[0] : n == 2 ? c.eff[1] : n <= 4 ? c.eff[2] : c.eff[3];
+}
 
 static int choose(int64_t M, int64_t N, int64_t K, int num_cus) {
     if (num_cus < 1) num_cus = 1;
     if (M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
+    if ((double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
     int best = -1;
     double best_cost = 0.0;
     for (const Candidate& c : kCandidates) {
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-        const double cost = (double)cdiv(tiles, num_cus) * c.bm * c.bn * (double)K / c.efficiency;
+        const int64_t n = cdiv(tiles, num_cus);
+        const double cost = (double)n * c.bm * c.bn * ((double)K + kTileOverheadK) / eff_at(c, n);
         if (best < 0 || cost < best_cost) {
             best = c.variant;
             best_cost = cost;

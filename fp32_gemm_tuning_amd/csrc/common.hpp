@@ -56,6 +56,21 @@ __device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
+// Buffer load straight into LDS (no VGPR round trip): every lane's 16 (or 4)
+// bytes land at lds_base + 16 (or 4) * lane, lds_base being wave-uniform. Out-of-
+// range offsets write zeros, as for the register loads.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, const float* lds_base,
+                                               uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds_base), 16, (int)off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void buf_load_lds4(__amdgpu_buffer_rsrc_t r, const float* lds_base,
+                                              uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds_base), 4, (int)off, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Workgroup id -> (tile row, tile column).
 //
@@ -98,10 +113,14 @@ __device__ __forceinline__ int swz16(int r) { return ((r >> 2) ^ (r & 2)) & 3; }
 // physical chunks, and 8 lanes filling one row hit 8 distinct chunks.
 __device__ __forceinline__ int swz32(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
+// For 64-float rows (16 chunks) the row index itself spreads any 8 or 16
+// consecutive rows over distinct chunks.
+__device__ __forceinline__ int swz64(int r) { return r & 15; }
+
 template <int BK>
 __device__ __forceinline__ int swz_chunk(int r) {
-    static_assert(BK == 16 || BK == 32, "A tile rows are 16 or 32 floats");
-    return BK == 16 ? swz16(r) : swz32(r);
+    static_assert(BK == 16 || BK == 32 || BK == 64, "A tile rows are 16, 32 or 64 floats");
+    return BK == 16 ? swz16(r) : (BK == 32 ? swz32(r) : swz64(r));
 }
 
 }  // namespace sgemm

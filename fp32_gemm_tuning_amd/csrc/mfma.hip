@@ -114,6 +114,67 @@ struct TileFill {
     }
 };
 
+// The same fill with gfx950's buffer-to-LDS loads: no prefetch registers and
+// no LDS store instructions; a wave instruction writes 64 x 16 bytes (VEC) or
+// 64 x 4 bytes contiguously, so each lane computes which global element
+// belongs at its destination slot (inverting the A swizzle). B rows are not
+// padded: its fragment reads are 4-byte reads, which the LDS serves one
+// half-wave at a time, each half reading 32 consecutive floats of one row.
+template <int BM, int BN, int BK, int NT, bool VEC>
+struct TileFillDma {
+    static constexpr int BNP = BN;
+    static constexpr int CPR = BK / 4;
+    static constexpr int W = NT / 64;
+    static constexpr int EPI = VEC ? 256 : 64;          // floats per wave instruction
+    static constexpr int A_INSTR = BM * BK / EPI / W;   // per wave per slice
+    static constexpr int B_INSTR = BK * BN / EPI / W;
+    static_assert(A_INSTR * EPI * W == BM * BK && B_INSTR * EPI * W == BK * BN, "tile/wave mismatch");
+
+    __device__ __forceinline__ void issue(const Args& a, int t, int m0, int n0, int k0,
+                                          int rows_valid, int cols_valid, float* As,
+                                          float* Bs) const {
+        const int kk = (a.K - k0) < BK ? (a.K - k0) : BK;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+            a.B + (int64_t)k0 * a.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
+        const int w = t >> 6, lane = t & 63;
+#pragma unroll
+        for (int p = 0; p < A_INSTR; ++p) {
+            const int piece = w * A_INSTR + p;
+            float* dst = As + piece * EPI;
+            if (VEC) {
+                const int slot = piece * 64 + lane;       // 16-byte chunk index in As
+                const int row = slot / CPR, q = (slot % CPR) ^ swz_chunk<BK>(row);
+                const bool ok = row < rows_valid && 4 * q + 4 <= kk;
+                buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
+            } else {
+                const int f = piece * 64 + lane;          // float index in As
+                const int row = f / BK, pc = (f % BK) >> 2;
+                const int kq = ((pc ^ swz_chunk<BK>(row)) << 2) | (f & 3);
+                const bool ok = row < rows_valid && kq < kk;
+                buf_load_lds4(rA, dst, ok ? (uint32_t)((row * (int)a.lda + kq) * 4) : OOB);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_INSTR; ++p) {
+            const int piece = w * B_INSTR + p;
+            float* dst = Bs + piece * EPI;
+            if (VEC) {
+                const int slot = piece * 64 + lane;
+                const int krow = slot / (BN / 4), nq = slot % (BN / 4);
+                const bool ok = krow < kk && 4 * nq + 4 <= cols_valid;
+                buf_load_lds16(rB, dst, ok ? (uint32_t)((krow * (int)a.ldb + 4 * nq) * 4) : OOB);
+            } else {
+                const int f = piece * 64 + lane;
+                const int krow = f / BN, n = f % BN;
+                const bool ok = krow < kk && n < cols_valid;
+                buf_load_lds4(rB, dst, ok ? (uint32_t)((krow * (int)a.ldb + n) * 4) : OOB);
+            }
+        }
+    }
+};
+
 // ===========================================================================
 // Tiled FP32 MFMA kernel, generic over the block tile BM x BN and the wave
 // tile WM x WN (each wave owns WM/32 x WN/32 blocks of 32x32 accumulated
@@ -146,9 +207,21 @@ struct TileFill {
 #ifndef SGEMM_M128_GROUP_M
 #define SGEMM_M128_GROUP_M 8
 #endif
+// Scheduling knobs: raise the wave's issue priority while it runs MFMAs, and
+// fence the scheduler so all of a sub-step's fragment loads issue before its
+// MFMAs.
+#ifndef SGEMM_M128_SETPRIO
+#define SGEMM_M128_SETPRIO 0
+#endif
+#ifndef SGEMM_M128_HOIST
+#define SGEMM_M128_HOIST 0
+#endif
+// 1: fill LDS with buffer-to-LDS loads instead of a register prefetch stage.
+#ifndef SGEMM_M128_DMA
+#define SGEMM_M128_DMA 1
+#endif
 constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
 constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
-constexpr int M128_NT = (M128_BM / M128_WM) * (M128_BN / M128_WN) * 64;
 
 template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
@@ -158,10 +231,16 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int BI = WM / 32, BJ = WN / 32;
     using Fill = TileFill<BM, BN, BK, NT, VEC>;
-    constexpr int BNP = Fill::BNP;
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
+    constexpr bool DMA = SGEMM_M128_DMA != 0;
+    constexpr int BNP = DMA ? Dma::BNP : Fill::BNP;
     constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
-    __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BNP];
+    // One LDS object per stage, so that the compiler can tell the stage being
+    // filled from the stage being read.
+    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs0[BK * BNP];
+    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs1[BK * BNP];
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
@@ -197,18 +276,7 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
         for (int bj = 0; bj < BJ; ++bj) boff[u][bj] = (16 * u + 8 * h) * BNP + wn * WN + bj * 32 + c;
     }
 
-    const int nslices = (a.K + BK - 1) / BK;
-    Fill fill;
-    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
-    fill.store(As[0], Bs[0], t);
-    __syncthreads();
-
-    for (int s = 0; s < nslices; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
-
-        const float* Ac = As[cur];
-        const float* Bc = Bs[cur];
+    auto compute = [&](const float* Ac, const float* Bc) {
 #pragma unroll
         for (int u = 0; u < STEPS; ++u) {
             float af[BI][8], bf[BJ][8];
@@ -223,6 +291,12 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
             for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[u][bj] + k * BNP];
+#if SGEMM_M128_HOIST
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+#if SGEMM_M128_SETPRIO
+            __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
             for (int k = 0; k < 8; ++k)
 #pragma unroll
@@ -231,10 +305,43 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
                     for (int bj = 0; bj < BJ; ++bj)
                         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
                                                                            acc[bi][bj], 0, 0, 0);
+#if SGEMM_M128_SETPRIO
+            __builtin_amdgcn_s_setprio(0);
+#endif
         }
+    };
 
-        if (s + 1 < nslices) fill.store(As[cur ^ 1], Bs[cur ^ 1], t);
+    // One pipelined step: start filling slice s+1 into the other stage, multiply
+    // slice s from this stage, finish the fill (register stage -> LDS), barrier.
+    // With one barrier per slice and two stages, a stage is refilled only after
+    // every wave has passed the barrier that ends the slice that read it.
+    const int nslices = (a.K + BK - 1) / BK;
+    Fill fill;
+    const Dma dma;
+    auto step = [&](int s, float* Acur, float* Bcur, float* Anext, float* Bnext) {
+        if (s + 1 < nslices) {
+            if constexpr (DMA)
+                dma.issue(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid, Anext, Bnext);
+            else
+                fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
+        }
+        compute(Acur, Bcur);
+        if constexpr (!DMA) {
+            if (s + 1 < nslices) fill.store(Anext, Bnext, t);
+        }
         __syncthreads();
+    };
+
+    if constexpr (DMA) {
+        dma.issue(a, t, m0, n0, 0, rows_valid, cols_valid, As0, Bs0);
+    } else {
+        fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
+        fill.store(As0, Bs0, t);
+    }
+    __syncthreads();
+    for (int s = 0; s < nslices; s += 2) {
+        step(s, As0, Bs0, As1, Bs1);
+        if (s + 1 < nslices) step(s + 1, As1, Bs1, As0, Bs0);
     }
 
 #pragma unroll
@@ -263,30 +370,52 @@ static bool vec_ok(const Args& a) {
              !aligned16(a.B));
 }
 
-// The 4-byte fill keeps more loads in flight per lane; at 4 waves per SIMD it
-// would spill, so that instantiation targets 3.
-#define M128_KERNEL(VEC)                                                                   \
-    k_mfma_tile<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK,                               \
-                (VEC) ? SGEMM_M128_WAVES_PER_EU : 3, VEC>
+// Launch helpers for instances of k_mfma_tile. The 4-byte-fill instance keeps
+// more loads in flight per lane; at 4 waves per SIMD it would spill, so it
+// targets 3.
+template <int BM, int BN, int WM, int WN>
+struct TileInstance {
+    static constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    template <bool VEC>
+    static const void* kernel() {
+        return (const void*)k_mfma_tile<BM, BN, WM, WN, M128_BK,
+                                         VEC ? SGEMM_M128_WAVES_PER_EU : 3, VEC>;
+    }
+    static int check(const Args& a) {
+        if (!extents_ok(a, BM, BN, M128_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+        const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
+        return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+    }
+    static hipError_t launch(const Args& a, hipStream_t s) {
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
+        if (vec_ok(a))
+            hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU, true>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+        else
+            hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, 3, false>), grid, block, 0, s,
+                               a, tm, tn, xcd_remap_enabled());
+        return hipGetLastError();
+    }
+};
 
-static int check_mfma128(const Args& a) {
-    if (!extents_ok(a, M128_BM, M128_BN, M128_BK)) return SGEMM_F32_ERR_TOO_LARGE;
-    const int64_t tiles = cdiv(a.M, M128_BM) * cdiv(a.N, M128_BN);
-    return tiles <= max_workgroups(M128_NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
-}
+using Tile128 = TileInstance<M128_BM, M128_BN, M128_WM, M128_WN>;
+using Tile64x128 = TileInstance<64, 128, 32, 64>;
 
-static hipError_t launch_mfma128(const Args& a, hipStream_t s) {
-    const int tm = (int)cdiv(a.M, M128_BM), tn = (int)cdiv(a.N, M128_BN);
-    const dim3 grid((unsigned)((int64_t)tm * tn)), block(M128_NT);
-    if (vec_ok(a))
-        hipLaunchKernelGGL(M128_KERNEL(true), grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    else
-        hipLaunchKernelGGL(M128_KERNEL(false), grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    return hipGetLastError();
+static int check_mfma128(const Args& a) { return Tile128::check(a); }
+static hipError_t launch_mfma128(const Args& a, hipStream_t s) { return Tile128::launch(a, s); }
+static int check_mfma64x128(const Args& a) { return Tile64x128::check(a); }
+static hipError_t launch_mfma64x128(const Args& a, hipStream_t s) {
+    return Tile64x128::launch(a, s);
 }
 
 Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
-                    (const void*)M128_KERNEL(true), M128_NT};
+                    Tile128::kernel<true>(), Tile128::NT};
+// 64x128 tile, 4 waves of 32x64: twice the tiles of mfma_128x128 for
+// medium shapes (e.g. 2048^3, where 256 tiles of 128x128 leave one
+// workgroup per compute unit).
+Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
+                       Tile64x128::kernel<true>(), Tile64x128::NT};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2
@@ -389,6 +518,299 @@ static hipError_t launch_mfma64(const Args& a, hipStream_t s) {
 
 Variant kMfma64 = {"mfma_64x64", check_mfma64, launch_mfma64, (const void*)k_mfma64<true>,
                          256};
+
+// ===========================================================================
+// mfma_64x64_k4: a 64x64 tile whose 4 waves split every 64-deep K slice four
+// ways. Wave w multiplies k = 16w .. 16w+15 of each slice into its own full
+// 64x64 accumulator (2x2 blocks of v_mfma_f32_32x32x2_f32), so each wave
+// issues 32 MFMAs (2048 matrix-core cycles) per barrier -- four times the
+// work of mfma_64x64 -- which hides fill latency with only one or two
+// workgroups per compute unit. This is the pages' split-K idea ("Optimizing
+// Matrix Multiply on CUDA, Part 2", "Selecting Among Three Kernels") moved
+// inside the workgroup: the four partial tiles are summed through LDS in a
+// fixed order (w = 0, 1, 2, 3), so no global workspace is needed and the
+// result is deterministic.
+// ===========================================================================
+constexpr int KS_BM = 64, KS_BN = 64, KS_WAVES = 4, KS_BK = 16 * KS_WAVES, KS_GROUP_M = 8;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_mfma_ksplit(Args a, int tiles_m, int tiles_n,
+                                                     int xcd_remap) {
+    constexpr int BM = KS_BM, BN = KS_BN, BK = KS_BK;
+    using Fill = TileFill<BM, BN, BK, 256, VEC>;
+    constexpr int BNP = Fill::BNP;
+    constexpr int STAGE = BM * BK + BK * BNP;  // floats per LDS stage
+    static_assert(2 * STAGE >= KS_WAVES * 4 * 16 * 64, "reduction buffer must fit in the stages");
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, KS_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Wave w, half h: k = 16w + 8h + s (s = 0..7) of each slice.
+    const int kb = 16 * w + 8 * h;
+    int aoff[2][2], boff[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int row = bi * 32 + c;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) aoff[bi][v] = row * BK + (((kb / 4 + v) ^ swz_chunk<BK>(row)) << 2);
+    }
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) boff[bj] = kb * BNP + bj * 32 + c;
+
+    const int nslices = (a.K + BK - 1) / BK;
+    Fill fill;
+    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
+    fill.store(smem, smem + BM * BK, t);
+    __syncthreads();
+
+    for (int s = 0; s < nslices; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
+        const float* Ac = smem + cur * STAGE;
+        const float* Bc = Ac + BM * BK;
+        float af[2][8], bf[2][8];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const f32x4 lo = *(const f32x4*)&Ac[aoff[bi][0]];
+            const f32x4 hi = *(const f32x4*)&Ac[aoff[bi][1]];
+            af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
+            af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+        }
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+        if (s + 1 < nslices) {
+            float* An = smem + (cur ^ 1) * STAGE;
+            fill.store(An, An + BM * BK, t);
+        }
+        __syncthreads();
+    }
+
+    // Fixed-order reduction: every wave parks its 4 blocks in LDS as
+    // red[w][block][r][lane]; wave w then sums block w over the 4 waves.
+    float* red = smem;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[((w * 4 + bi * 2 + bj) * 16 + r) * 64 + lane] = acc[bi][bj][r];
+    __syncthreads();
+    const int bi = w >> 1, bj = w & 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float v = red[((0 * 4 + w) * 16 + r) * 64 + lane];
+#pragma unroll
+        for (int ww = 1; ww < KS_WAVES; ++ww) v += red[((ww * 4 + w) * 16 + r) * 64 + lane];
+        const int i = bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = bj * 32 + c;
+        if (i < rows_valid && j < cols_valid) store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+    }
+}
+
+static int check_ksplit(const Args& a) {
+    if (!extents_ok(a, KS_BM, KS_BN, KS_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, KS_BM) * cdiv(a.N, KS_BN);
+    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_ksplit(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, KS_BM), tn = (int)cdiv(a.N, KS_BN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
+    if (vec_ok(a))
+        hipLaunchKernelGGL(k_mfma_ksplit<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL(k_mfma_ksplit<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfmaKsplit = {"mfma_64x64_k4", check_ksplit, launch_ksplit,
+                       (const void*)k_mfma_ksplit<true>, 256};
+
+// ===========================================================================
+// mfma_direct: small and medium shapes. A workgroup of KS waves owns a TM x TN
+// tile of C; wave w takes the 16-deep k steps w, w + KS, w + 2*KS, ... and
+// accumulates the whole tile for them (TM/32 x TN/32 blocks of
+// v_mfma_f32_32x32x2_f32). Operands go straight from global memory (L2) into
+// MFMA registers -- there is no LDS tile and no barrier inside the K loop, so
+// the waves run independently and hide latency with a register double buffer
+// (step j+KS is loaded while step j is multiplied). With the k-permuted
+// operand layout a lane's A values are 8 consecutive floats of one row and its
+// B values are rows of 32 consecutive columns across the half-wave. At the end
+// the KS partial tiles are summed through LDS in the fixed order w = 0..KS-1.
+// Fine tiles (32x32) spread a few-tile shape evenly over the compute
+// units; this is the pages' split-K ("Optimizing Matrix Multiply on CUDA,
+// Part 2", "Selecting Among Three Kernels") kept inside the workgroup.
+// ===========================================================================
+#ifndef SGEMM_DIRECT_TM
+#define SGEMM_DIRECT_TM 32
+#endif
+#ifndef SGEMM_DIRECT_TN
+#define SGEMM_DIRECT_TN 32
+#endif
+#ifndef SGEMM_DIRECT_KS
+#define SGEMM_DIRECT_KS 4
+#endif
+constexpr int DR_TM = SGEMM_DIRECT_TM, DR_TN = SGEMM_DIRECT_TN, DR_KS = SGEMM_DIRECT_KS;
+constexpr int DR_GROUP_M = 8;
+
+template <int TM, int TN, bool VEC>
+struct DirectFrag {
+    static constexpr int BI = TM / 32, BJ = TN / 32;
+    float a[BI][8];
+    float b[BJ][8];
+
+    // Step starting at k0: lane (h, c) reads A[m0 + 32*bi + c][k0 + 8h + 0..7]
+    // and B[k0 + 8h + s][n0 + 32*bj + c]; everything outside the matrix reads 0.
+    __device__ __forceinline__ void load(const Args& a_, int m0, int n0, int k0, int rows_valid,
+                                         int cols_valid, int h, int c) {
+        const int kk = (a_.K - k0) < 16 ? (a_.K - k0) : 16;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            a_.A + (int64_t)m0 * a_.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a_.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+            a_.B + (int64_t)k0 * a_.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a_.ldb + cols_valid) * 4));
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi) {
+            const int row = 32 * bi + c;
+            const bool rok = row < rows_valid;
+            if (VEC) {
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const int kq = 8 * h + 4 * v;
+                    const f32x4 x = buf_load4(rA, rok && kq + 4 <= kk ? (uint32_t)((row * (int)a_.lda + kq) * 4) : OOB);
+                    a[bi][4 * v + 0] = x.x; a[bi][4 * v + 1] = x.y;
+                    a[bi][4 * v + 2] = x.z; a[bi][4 * v + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int kq = 8 * h + s;
+                    a[bi][s] = buf_load1(rA, rok && kq < kk ? (uint32_t)((row * (int)a_.lda + kq) * 4) : OOB);
+                }
+            }
+        }
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj) {
+            const int col = 32 * bj + c;
+            const bool cok = col < cols_valid;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int kr = 8 * h + s;
+                b[bj][s] = buf_load1(rB, cok && kr < kk ? (uint32_t)((kr * (int)a_.ldb + col) * 4) : OOB);
+            }
+        }
+    }
+};
+
+template <int TM, int TN, int KS, bool VEC>
+__global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, int tiles_n,
+                                                         int xcd_remap) {
+    constexpr int BI = TM / 32, BJ = TN / 32, NB = BI * BJ;
+    __shared__ float red[KS * NB * 16 * 64];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, DR_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * TM, n0 = tn * TN;
+    const int rows_valid = (a.M - m0) < TM ? (a.M - m0) : TM;
+    const int cols_valid = (a.N - n0) < TN ? (a.N - n0) : TN;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[BI][BJ];
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nsteps = (a.K + 15) / 16;
+    DirectFrag<TM, TN, VEC> cur, nxt;
+    if (w < nsteps) cur.load(a, m0, n0, 16 * w, rows_valid, cols_valid, h, c);
+    for (int j = w; j < nsteps; j += KS) {
+        if (j + KS < nsteps) nxt.load(a, m0, n0, 16 * (j + KS), rows_valid, cols_valid, h, c);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[bi][s], cur.b[bj][s],
+                                                                       acc[bi][bj], 0, 0, 0);
+        cur = nxt;
+    }
+
+    // Fixed-order reduction over the KS waves: red[w][block][r][lane].
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[((w * NB + bi * BJ + bj) * 16 + r) * 64 + lane] = acc[bi][bj][r];
+    __syncthreads();
+    for (int blk = w; blk < NB; blk += KS) {
+        const int bi = blk / BJ, bj = blk % BJ;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float v = red[((0 * NB + blk) * 16 + r) * 64 + lane];
+#pragma unroll
+            for (int ww = 1; ww < KS; ++ww) v += red[((ww * NB + blk) * 16 + r) * 64 + lane];
+            const int i = bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int jj = bj * 32 + c;
+            if (i < rows_valid && jj < cols_valid)
+                store_out(a, (int64_t)m0 + i, (int64_t)n0 + jj, v);
+        }
+    }
+}
+
+static int check_direct(const Args& a) {
+    const int64_t ea = ((int64_t)(DR_TM - 1) * a.lda + 16) * 4;
+    const int64_t eb = ((int64_t)15 * a.ldb + DR_TN) * 4;
+    if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, DR_TM) * cdiv(a.N, DR_TN);
+    return tiles <= max_workgroups(64 * DR_KS) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_direct(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, DR_TM), tn = (int)cdiv(a.N, DR_TN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(64 * DR_KS);
+    const bool vec = !((a.K & 3) || (a.lda & 3) || !aligned16(a.A));
+    if (vec)
+        hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, true>), grid, block, 0, s, a, tm, tn,
+                           xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, false>), grid, block, 0, s, a, tm, tn,
+                           xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
+                       (const void*)k_mfma_direct<DR_TM, DR_TN, DR_KS, true>, 64 * DR_KS};
 
 // ===========================================================================
 // mfma_skinny: for few rows (near-GEMV, e.g. 16 x 8192 x 8192, where B is

@@ -92,7 +92,8 @@ enum sgemm_f32_variant_id {
        conflict-free transposed A tile (Part 2 of "Optimizing Matrix
        Multiply on CUDA") */
     SGEMM_F32_VALU_MAIN = 6,
-    /* FP32 matrix-core kernel, 128x128 block tile (v_mfma_f32_32x32x2_f32) */
+    /* FP32 matrix-core kernel, 128x128 block tile (v_mfma_f32_32x32x2_f32),
+       LDS filled by buffer-to-LDS loads */
     SGEMM_F32_MFMA_128 = 7,
     /* FP32 matrix-core kernel, 64x64 block tile for shapes with few 128x128
        tiles (v_mfma_f32_16x16x4_f32) */
@@ -100,7 +101,20 @@ enum sgemm_f32_variant_id {
     /* FP32 matrix-core kernel for M <= a few tens of rows (near-GEMV): 16-row
        tiles, the K loop split across the waves of a workgroup */
     SGEMM_F32_MFMA_SKINNY = 9,
-    SGEMM_F32_NUM_VARIANTS = 10
+    /* FP32 matrix-core kernel, 64x64 tile whose 4 waves split each 64-deep K
+       slice four ways and sum their partial tiles in a fixed order (few tiles,
+       long K) */
+    SGEMM_F32_MFMA_64_K4 = 10,
+    /* FP32 matrix-core kernel for small shapes: 32x32 tiles, four
+       waves split K and load their operands straight into matrix-core
+       registers (no LDS tile, no barrier in the K loop), fixed-order
+       reduction at the end */
+    SGEMM_F32_MFMA_DIRECT = 11,
+    /* FP32 matrix-core kernel, 64x128 block tile (4 waves of 32x64,
+       v_mfma_f32_32x32x2_f32): twice the tiles of mfma_128x128 for medium
+       shapes */
+    SGEMM_F32_MFMA_64x128 = 12,
+    SGEMM_F32_NUM_VARIANTS = 13
 };
 
 /* C = alpha*A*B + beta*C, kernel chosen automatically (see sgemm_f32_plan). */
@@ -126,7 +140,7 @@ SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, c
 /* Number of variants (SGEMM_F32_NUM_VARIANTS). */
 SGEMM_F32_API int sgemm_f32_num_variants(void);
 
-/* Short name of a variant ("naive", ..., "mfma_skinny"), or NULL if out of range.
+/* Short name of a variant ("naive", ..., "mfma_64x128"), or NULL if out of range.
  * The string is static. */
 SGEMM_F32_API const char *sgemm_f32_variant_name(int variant);
 

@@ -105,23 +105,29 @@ def test_plan_picks_matrix_core_kernels_for_the_workloads():
     assert _plan(w["S2048"].M, w["S2048"].N, w["S2048"].K) == "mfma_128x128"
     assert _plan(w["S8192"].M, w["S8192"].N, w["S8192"].K) == "mfma_128x128"
     assert _plan(w["S4092"].M, w["S4092"].N, w["S4092"].K) == "mfma_128x128"
-    # 96 tiles of 128x128 on 256 compute units: the 64x64 tile wins
-    assert _plan(w["R_odd"].M, w["R_odd"].N, w["R_odd"].K) == "mfma_64x64"
+    # 96 tiles of 128x128 on 256 compute units: the 64x128 tile wins
+    assert _plan(w["R_odd"].M, w["R_odd"].N, w["R_odd"].K) == "mfma_64x128"
     assert _plan(w["R_skinny"].M, w["R_skinny"].N, w["R_skinny"].K) == "mfma_skinny"
-    assert _plan(256, 256, 256) == "mfma_64x64"
+    assert _plan(256, 256, 256) == "mfma_direct"
 
 
 def test_plan_busiest_cu_rule():
-    # 1024 tiles of 128^2 on 256 CUs: 4 per CU. 64^2 tiles: 16 per CU at 0.65
-    # efficiency -> 128^2 wins. At 2 CUs the tile count no longer matters.
-    assert _plan(4096, 4096, 64, cus=256) == "mfma_128x128"
-    assert _plan(1025, 1025, 64, cus=256) == "mfma_64x64"
+    # 4096^2: four 128^2 tiles per CU beat eight 64x128 or sixteen 64^2 tiles.
+    assert _plan(4096, 4096, 4096, cus=256) == "mfma_128x128"
+    # 1024x1536: 96 tiles of 128^2 keep 160 CUs idle; 192 of 64x128 do not.
+    assert _plan(1024, 1536, 768, cus=256) == "mfma_64x128"
+    # 8192^2: sixteen 128^2 tiles per CU.
+    assert _plan(8192, 8192, 8192, cus=256) == "mfma_128x128"
+    # a single CU: the largest tile always wins.
+    assert _plan(1000, 1000, 1000, cus=1) == "mfma_128x128"
 
 
 def test_plan_falls_back_when_offsets_exceed_32_bits():
-    # lda so large that even a 64-row panel spans more than 2^31 bytes
-    assert _plan(256, 256, 16, lda=1 << 24) == "reg2d"
+    # leading dimensions so large that even a 32-row (or 16-row) panel spans
+    # more than 2^31 bytes
+    assert _plan(256, 256, 16, lda=1 << 26) == "reg2d"
     assert _plan(256, 256, 16, ldb=1 << 26) == "reg2d"
+    assert _plan(2048, 2048, 2048, lda=1 << 24) == "reg2d"
 
 
 def test_peak_probe_argument_checks():
