@@ -35,7 +35,7 @@ ERR_DEVICE = -103
 
 VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", "valu_main",
             "mfma_128x128", "mfma_64x64", "mfma_skinny", "mfma_64x64_k4", "mfma_direct",
-            "mfma_64x128")
+            "mfma_64x128", "mfma_256x256")
 
 
 class SgemmError(RuntimeError):
@@ -50,6 +50,16 @@ def _load() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python fp32_gemm_tuning_amd/build.py or __graft_entry__.build()); "
             "there is no fallback path")
+    # One HIP runtime per process: PyTorch ships its own libamdhip64, and the
+    # library must bind to that one when both are used (device pointers and
+    # streams come from torch). Loading the library first would load the
+    # system runtime under the same soname, and torch would then bind to it
+    # and fail. Importing torch first (when it is installed) makes the
+    # dynamic linker reuse torch's runtime for the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, f32, vp, c_int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
     gemm_args = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64]

@@ -14,6 +14,7 @@ namespace sgemm {
 static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
     &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
+    &kMfma256,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
@@ -51,7 +52,9 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // first fill and epilogue -- at a rate that depends on n: one workgroup per
 // unit leaves the matrix cores waiting on fills and barriers, four keep them
 // busy. The rates are measured fractions of peak on MI355X (interleaved
-// timing of the candidates on the square and odd workloads).
+// timing of the candidates on the square and odd workloads). mfma_256x256
+// holds one workgroup per unit, so for it n counts rounds, not residents;
+// its 16 waves keep the matrix cores busy from the first round.
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
@@ -62,6 +65,7 @@ struct Candidate {
 // Listed in order of preference when estimates tie.
 static const Candidate kCandidates[] = {
     {SGEMM_F32_MFMA_128, 128, 128, {0.80, 0.85, 0.91, 0.91}},
+    {SGEMM_F32_MFMA_256, 256, 256, {0.925, 0.93, 0.93, 0.93}},
     {SGEMM_F32_MFMA_64x128, 64, 128, {0.70, 0.78, 0.85, 0.88}},
     {SGEMM_F32_MFMA_64, 64, 64, {0.60, 0.70, 0.72, 0.83}},
 };

@@ -32,7 +32,8 @@ extern Variant kNaive, kCoalesced, kLdsTiled, kReg1d, kReg2d, kVec4TransA;
 // valu_main.hip
 extern Variant kValuMain;
 // mfma.hip
-extern Variant kMfma128, kMfma64, kMfmaSkinny, kMfmaKsplit, kMfmaDirect, kMfma64x128;
+extern Variant kMfma128, kMfma64, kMfmaSkinny, kMfmaKsplit, kMfmaDirect, kMfma64x128,
+    kMfma256;
 
 // Common host checks.
 bool aligned16(const void* p);

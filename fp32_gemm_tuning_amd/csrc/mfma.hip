@@ -130,14 +130,25 @@ struct TileFillDma {
     static constexpr int B_INSTR = BK * BN / EPI / W;
     static_assert(A_INSTR * EPI * W == BM * BK && B_INSTR * EPI * W == BK * BN, "tile/wave mismatch");
 
+    // A slice starting at or past K is legal: its resources are empty and
+    // every lane's load reads as zero (the pipelined kernel issues loads for
+    // slices past the end so that every path issues the same number).
     __device__ __forceinline__ void issue(const Args& a, int t, int m0, int n0, int k0,
                                           int rows_valid, int cols_valid, float* As,
                                           float* Bs) const {
-        const int kk = (a.K - k0) < BK ? (a.K - k0) : BK;
+        // kk = number of valid k in the slice (0 past the end): no lane is
+        // then in range, and both extents stay below 2^31 bytes, so the
+        // out-of-range offset always reads zero. The base addresses may point
+        // past the matrices; nothing is read through them.
+        // (The clamp compiles to a vector instruction; readfirstlane keeps the
+        // resources in scalar registers.)
+        const int kr = a.K - k0;
+        const int kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < BK ? kr : BK));
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(
             a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(
-            a.B + (int64_t)k0 * a.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
+            a.B + (int64_t)k0 * a.ldb + n0,
+            kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4) : 0u);
         const int w = t >> 6, lane = t & 63;
 #pragma unroll
         for (int p = 0; p < A_INSTR; ++p) {
@@ -178,9 +189,9 @@ struct TileFillDma {
 // ===========================================================================
 // Tiled FP32 MFMA kernel, generic over the block tile BM x BN and the wave
 // tile WM x WN (each wave owns WM/32 x WN/32 blocks of 32x32 accumulated
-// with v_mfma_f32_32x32x2_f32). BK-deep slices, double-buffered LDS: slice
-// s+1 is loaded into registers while slice s is multiplied, then stored
-// into the other LDS buffer; one barrier per slice.
+// with v_mfma_f32_32x32x2_f32). BK-deep slices, double-buffered LDS: the
+// buffer-to-LDS loads of slice s+1 are in flight while slice s is
+// multiplied; one barrier per slice.
 //
 // mfma_128x128 is BM = BN = 128 with 4 waves of 64x64 (64 accumulator
 // registers per lane), BK = 16, and an occupancy target of 4 waves per SIMD
@@ -207,19 +218,6 @@ struct TileFillDma {
 #ifndef SGEMM_M128_GROUP_M
 #define SGEMM_M128_GROUP_M 8
 #endif
-// Scheduling knobs: raise the wave's issue priority while it runs MFMAs, and
-// fence the scheduler so all of a sub-step's fragment loads issue before its
-// MFMAs.
-#ifndef SGEMM_M128_SETPRIO
-#define SGEMM_M128_SETPRIO 0
-#endif
-#ifndef SGEMM_M128_HOIST
-#define SGEMM_M128_HOIST 0
-#endif
-// 1: fill LDS with buffer-to-LDS loads instead of a register prefetch stage.
-#ifndef SGEMM_M128_DMA
-#define SGEMM_M128_DMA 1
-#endif
 constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
 constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
 
@@ -230,10 +228,8 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int BI = WM / 32, BJ = WN / 32;
-    using Fill = TileFill<BM, BN, BK, NT, VEC>;
     using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
-    constexpr bool DMA = SGEMM_M128_DMA != 0;
-    constexpr int BNP = DMA ? Dma::BNP : Fill::BNP;
+    constexpr int BNP = Dma::BNP;
     constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
     // One LDS object per stage, so that the compiler can tell the stage being
     // filled from the stage being read.
@@ -291,12 +287,6 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
             for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[u][bj] + k * BNP];
-#if SGEMM_M128_HOIST
-            __builtin_amdgcn_sched_barrier(0);
-#endif
-#if SGEMM_M128_SETPRIO
-            __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
             for (int k = 0; k < 8; ++k)
 #pragma unroll
@@ -305,44 +295,223 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
                     for (int bj = 0; bj < BJ; ++bj)
                         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
                                                                            acc[bi][bj], 0, 0, 0);
-#if SGEMM_M128_SETPRIO
-            __builtin_amdgcn_s_setprio(0);
-#endif
         }
     };
 
-    // One pipelined step: start filling slice s+1 into the other stage, multiply
-    // slice s from this stage, finish the fill (register stage -> LDS), barrier.
-    // With one barrier per slice and two stages, a stage is refilled only after
-    // every wave has passed the barrier that ends the slice that read it.
+    // One pipelined step: start filling slice s+1 into the other stage with
+    // buffer-to-LDS loads, multiply slice s from this stage, barrier (which
+    // also waits for this wave's loads). With one barrier per slice and two
+    // stages, a stage is refilled only after every wave has passed the
+    // barrier that ends the slice that read it.
     const int nslices = (a.K + BK - 1) / BK;
-    Fill fill;
     const Dma dma;
     auto step = [&](int s, float* Acur, float* Bcur, float* Anext, float* Bnext) {
-        if (s + 1 < nslices) {
-            if constexpr (DMA)
-                dma.issue(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid, Anext, Bnext);
-            else
-                fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
-        }
+        if (s + 1 < nslices)
+            dma.issue(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid, Anext, Bnext);
         compute(Acur, Bcur);
-        if constexpr (!DMA) {
-            if (s + 1 < nslices) fill.store(Anext, Bnext, t);
-        }
         __syncthreads();
     };
 
-    if constexpr (DMA) {
-        dma.issue(a, t, m0, n0, 0, rows_valid, cols_valid, As0, Bs0);
-    } else {
-        fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
-        fill.store(As0, Bs0, t);
-    }
+    dma.issue(a, t, m0, n0, 0, rows_valid, cols_valid, As0, Bs0);
     __syncthreads();
     for (int s = 0; s < nslices; s += 2) {
         step(s, As0, Bs0, As1, Bs1);
         if (s + 1 < nslices) step(s + 1, As1, Bs1, As0, Bs0);
     }
+
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int j = wn * WN + bj * 32 + c;
+                if (i < rows_valid && j < cols_valid)
+                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+            }
+}
+
+// ===========================================================================
+// The same tile with a software-pipelined slice and an LDS ring of STAGES
+// slices. Each BK = 16 slice is split into two halves of four MFMA k-steps,
+// and every wave holds two fragment register sets, so the LDS reads of one
+// half are in flight while the MFMAs of the other half run. The workgroup
+// barrier sits between the two halves of a slice: before it, each wave has
+// finished reading the slice's stage and its own buffer-to-LDS loads of the
+// next slice have landed (loads of later slices may still be in flight);
+// after it, the loads of the slice STAGES ahead are issued into the stage
+// just released, and the first half of the next slice is read while the
+// second half of this one is multiplied. A lone wave on a SIMD then never
+// waits on an LDS round trip between MFMAs, and a global load has STAGES - 1
+// slices of time to land.
+// ===========================================================================
+template <int BI, int BJ>
+struct PartFrag {
+    f32x4 a[BI];      // A operands of the part's 4 k-steps, per row block
+    float b[BJ][4];   // B operands of the part's 4 k-steps, per column block
+};
+
+// Workgroup barrier of the LDS ring: waits until at most VMCNT of this wave's
+// vector-memory operations (buffer-to-LDS loads of later slices, issued after
+// the ones that must have landed) are outstanding and all of its LDS reads
+// are done, then synchronises the workgroup. A fence would wait for every
+// outstanding load, so the compiler is instead kept from moving memory
+// accesses across the barrier by empty asm statements with a memory clobber.
+// s_waitcnt immediate (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8.
+template <int VMCNT>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(VMCNT >= 0 && VMCNT < 64, "vmcnt field is 6 bits");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VMCNT & 15) | ((VMCNT >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    static_assert(BK == 16 || BK == 32, "slices of 16 or 32 k");
+    constexpr int P = BK / 8;   // parts of 4 MFMA k-steps per slice
+    constexpr int WAVES_N = BN / WN;
+    constexpr int NT = (BM / WM) * WAVES_N * 64;
+    constexpr int BI = WM / 32, BJ = WN / 32;
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
+    constexpr int BNP = Dma::BNP;
+    constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
+    static_assert((STAGES - 1) * G < 64, "outstanding loads exceed vmcnt");
+    // One LDS object per stage, so that the compiler can tell the stage being
+    // filled from the stages being read (unused stages are dropped).
+    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs0[BK * BNP];
+    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs1[BK * BNP];
+    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? BM * BK : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? BK * BNP : 4];
+    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? BM * BK : 4];
+    __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? BK * BNP : 4];
+    float* const Ast[4] = {As0, As1, As2, As3};
+    float* const Bst[4] = {Bs0, Bs1, Bs2, Bs3};
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+    // The tile coordinates are workgroup-uniform; the integer divisions of
+    // the tile mapping leave them in vector registers, and a buffer resource
+    // built from a vector register costs a per-lane loop around every load,
+    // so move them to scalar registers explicitly.
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+    const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w / WAVES_N, wn = w % WAVES_N;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[BI][BJ];
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Lanes 0-31 take k = s and lanes 32-63 take k = BK/2 + s at MFMA step s
+    // of the slice; part v covers steps 4v .. 4v+3, i.e. 16-byte chunk
+    // P*h + v of the lane's A row and B rows BK/2*h + 4v .. BK/2*h + 4v + 3.
+    // A fragment address of part v: arow + ((achunk ^ v) << 2), computed per
+    // read (one XOR and one shift-or, hidden under the MFMAs) rather than
+    // held in P registers per row block.
+    int arow[BI], achunk[BI], boff[BJ];
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi) {
+        const int row = wm * WM + bi * 32 + c;
+        arow[bi] = row * BK;
+        achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
+    }
+#pragma unroll
+    for (int bj = 0; bj < BJ; ++bj) boff[bj] = (BK / 2) * h * BNP + wn * WN + bj * 32 + c;
+
+    auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+            f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[boff[bj] + (4 * v + k) * BNP];
+    };
+    auto mma_part = [&](const PartFrag<BI, BJ>& f) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[bi][k], f.b[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+    };
+
+    const int nslices = (a.K + BK - 1) / BK;
+    const Dma dma;
+    PartFrag<BI, BJ> f0, f1;
+    // Prologue: fill every stage (stages past the last slice read zeros),
+    // wait for slice 0, read its first half. Every slice below issues exactly
+    // G loads per wave, whether or not its target slice exists, so the count
+    // of loads issued after any given one is the same on every path.
+#pragma unroll
+    for (int j = 0; j < STAGES; ++j)
+        dma.issue(a, t, m0, n0, j * BK, rows_valid, cols_valid, Ast[j], Bst[j]);
+    ring_barrier<(STAGES - 1) * G>();
+    read_part(f0, Ast[0], Bst[0], 0);
+
+    // Slice s lives in stage (Ac, Bc), slice s + 1 in (An, Bn); on entry f0
+    // holds (or is loading) part 0 of slice s; parts alternate between f0
+    // and f1 (P is even, so the last part is in f1). The barrier comes after
+    // the reads of the last part and before its MFMAs; at the barrier the
+    // loads of slices s + 2 .. s + STAGES - 1 may still be in flight.
+    // Scheduling fences pin the order: each half's fragment reads issue
+    // before the other half's MFMAs, and no MFMA moves across a barrier or
+    // into a neighbouring half (the scheduler would otherwise hoist the
+    // barrier, with its wait on the reads just issued, above the MFMAs, or
+    // pull MFMAs up next to the reads they depend on).
+    auto slice = [&](int s, float* Ac, float* Bc, const float* An, const float* Bn) {
+#pragma unroll
+        for (int v = 0; v + 1 < P; ++v) {
+            if (v & 1)
+                read_part(f0, Ac, Bc, v + 1);
+            else
+                read_part(f1, Ac, Bc, v + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (v & 1)
+                mma_part(f1);
+            else
+                mma_part(f0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ring_barrier<(STAGES - 2) * G>();
+        read_part(f0, An, Bn, 0);   // past the last slice: read and unused
+        dma.issue(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_part(f1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Whole rounds of STAGES slices, free of conditionals, then the rest.
+    int s0 = 0;
+    for (; s0 + STAGES <= nslices; s0 += STAGES) {
+#pragma unroll
+        for (int j = 0; j < STAGES; ++j)
+            slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+    }
+#pragma unroll
+    for (int j = 0; j < STAGES - 1; ++j)
+        if (s0 + j < nslices)
+            slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+    // The zero-filling loads issued for slices past the end must land before
+    // the workgroup's LDS can be handed to another workgroup.
+    ring_barrier<0>();
 
 #pragma unroll
     for (int bi = 0; bi < BI; ++bi)
@@ -416,6 +585,63 @@ Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
 // workgroup per compute unit).
 Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
                        Tile64x128::kernel<true>(), Tile64x128::NT};
+
+// mfma_256x256: the pipelined kernel with a 256x256 block tile, 16 waves of
+// 64x64 (four per SIMD, all of one workgroup), one workgroup per compute
+// unit (2 x 32 KiB LDS stages). With every wave of a compute unit in one
+// workgroup there is no staggered finish between workgroups sharing a SIMD,
+// and the A and B panels are read from L2 half as often as with 128x128
+// tiles. The 4-byte-fill instance spills a few registers at this occupancy
+// (correct, slower); shapes that need it are rarely large.
+#ifndef SGEMM_M256_BM
+#define SGEMM_M256_BM 256
+#endif
+#ifndef SGEMM_M256_BN
+#define SGEMM_M256_BN 256
+#endif
+#ifndef SGEMM_M256_WM
+#define SGEMM_M256_WM 64
+#endif
+#ifndef SGEMM_M256_WN
+#define SGEMM_M256_WN 64
+#endif
+#ifndef SGEMM_M256_WPE
+#define SGEMM_M256_WPE 4
+#endif
+#ifndef SGEMM_M256_STAGES
+#define SGEMM_M256_STAGES 2
+#endif
+constexpr int M256_BM = SGEMM_M256_BM, M256_BN = SGEMM_M256_BN, M256_WM = SGEMM_M256_WM,
+              M256_WN = SGEMM_M256_WN, M256_BK = 16;
+constexpr int M256_NT = (M256_BM / M256_WM) * (M256_BN / M256_WN) * 64;
+
+template <bool VEC>
+static const void* kernel_mfma256() {
+    return (const void*)k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC>;
+}
+
+static int check_mfma256(const Args& a) {
+    if (!extents_ok(a, M256_BM, M256_BN, M256_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, M256_BM) * cdiv(a.N, M256_BN);
+    return tiles <= max_workgroups(M256_NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, M256_BM), tn = (int)cdiv(a.N, M256_BN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(M256_NT);
+    if (vec_ok(a))
+        hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true>),
+                           grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false>),
+                           grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2

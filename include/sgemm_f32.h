@@ -114,7 +114,12 @@ enum sgemm_f32_variant_id {
        v_mfma_f32_32x32x2_f32): twice the tiles of mfma_128x128 for medium
        shapes */
     SGEMM_F32_MFMA_64x128 = 12,
-    SGEMM_F32_NUM_VARIANTS = 13
+    /* FP32 matrix-core kernel, 256x256 block tile of 16 waves (one
+       workgroup per compute unit), software-pipelined: the LDS reads of one
+       half slice overlap the MFMAs of the other, and the barrier sits
+       between the halves; for large shapes */
+    SGEMM_F32_MFMA_256 = 13,
+    SGEMM_F32_NUM_VARIANTS = 14
 };
 
 /* C = alpha*A*B + beta*C, kernel chosen automatically (see sgemm_f32_plan). */

@@ -112,6 +112,9 @@ SMALL = [
     (200, 136, 64, 1.0, 0.0, "uniform", (0, 0, 0), (1, 1, 0)),
     (200, 136, 64, 1.0, 0.25, "integer", (0, 0, 0), (1, 3, 2)),
     (513, 385, 250, 1.0, 0.0, "normal", (0, 0, 0), (0, 0, 0)),
+    # one K slice only, and exactly two (the pipelined kernel's LDS ring)
+    (260, 270, 16, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
+    (257, 300, 32, 1.0, 0.5, "uniform", (0, 4, 0), (0, 0, 0)),
 ]
 
 
@@ -209,7 +212,8 @@ def test_workloads(dev, name, integer):
         assert rep.ok, f"{w.name}: {rep}"
 
 
-@pytest.mark.parametrize("variant", ["valu_main", "mfma_64x64", "mfma_128x128", "vec4_transa"])
+@pytest.mark.parametrize("variant", ["valu_main", "mfma_64x64", "mfma_128x128", "vec4_transa",
+                                     "mfma_256x256"])
 def test_main_kernels_at_2048(dev, variant):
     w = WORKLOADS["S2048"]
     A, B, C0 = make_inputs(w)
@@ -218,6 +222,23 @@ def test_main_kernels_at_2048(dev, variant):
     assert rc == 0
     for rep in check_sampled(C, A, B, C0, w.M, w.N, w.K, w.alpha, w.beta, False, seed=5):
         assert rep.ok, f"{variant}: {rep}"
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
+@pytest.mark.parametrize("variant", ["mfma_256x256", "mfma_128x128"])
+def test_large_tiles_on_odd_shape(dev, variant, integer):
+    # 1000 x 1531 x 777: ragged in every dimension and not 16-byte aligned,
+    # so the 4-byte fill runs; every output checked.
+    w = WORKLOADS["R_odd"]
+    if integer:
+        w = w.integer_variant()
+    A, B, C0 = make_inputs(w)
+    v = sg.sgemm_f32_variant_by_name(variant)
+    rc, C = run(v, w.M, w.N, w.K, w.alpha, w.beta, A, B, C0, dev, tag=w.name)
+    assert rc == 0
+    rep = check_full(C, A, B, C0, w.M, w.N, w.K, w.alpha, w.beta, integer)
+    print(f"[gpu] {variant} {w.name}: {rep}", flush=True)
+    assert rep.ok, f"{variant}: {rep}"
 
 
 @pytest.mark.parametrize("kind", [0, 1, 2])
