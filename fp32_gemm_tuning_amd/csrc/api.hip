@@ -14,7 +14,7 @@ namespace sgemm {
 static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
     &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
-    &kMfma256,
+    &kMfma256, &kMfmaKgroup, &kMfmaKgroup96,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
@@ -44,34 +44,34 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------------------
 // Variant choice. Following the pages' tile selection ("Optimizing Matrix
 // Multiply on CUDA, Part 2", "Selecting Among Three Kernels"; "Part 1",
-// "Small and Odd Sizes"), the host estimates the time of the busiest compute
-// unit for each candidate and takes the smallest. With T tiles dealt out to
-// C compute units (MI355X places workgroups breadth-first, so the busiest
-// unit holds n = ceil(T / C) of them, all resident at once), that unit does
-// n * BM * BN * (K + K0) multiply-add units -- K0 standing for the per-tile
-// first fill and epilogue -- at a rate that depends on n: one workgroup per
-// unit leaves the matrix cores waiting on fills and barriers, four keep them
-// busy. The rates are measured fractions of peak on MI355X (interleaved
-// timing of the candidates on the square and odd workloads). mfma_256x256
-// holds one workgroup per unit, so for it n counts rounds, not residents;
-// its 16 waves keep the matrix cores busy from the first round.
+// "Small and Odd Sizes"), the host predicts each candidate's time and takes
+// the smallest. With T tiles dealt out to C compute units (MI355X places
+// workgroups breadth-first), the busiest unit holds n = ceil(T / C) tiles;
+// the prediction is a fixed cost (launch, first fill, epilogue) plus that
+// unit's n * 2*BM*BN*K FLOP at a fraction of its peak that depends on n
+// (few tiles per unit leave the matrix cores waiting on fills and barriers).
+// Both were fitted per kernel to interleaved timings of every candidate on
+// 24 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X; the
+// fitted model picks the fastest kernel or one within 6% on all of them.
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
     int bm, bn;
-    double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 workgroups per CU
+    double overhead_us;
+    double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 tiles per CU
 };
 
-// Listed in order of preference when estimates tie.
+// Listed in order of preference when predictions tie.
 static const Candidate kCandidates[] = {
-    {SGEMM_F32_MFMA_128, 128, 128, {0.80, 0.85, 0.91, 0.91}},
-    {SGEMM_F32_MFMA_256, 256, 256, {0.925, 0.93, 0.93, 0.93}},
-    {SGEMM_F32_MFMA_64x128, 64, 128, {0.70, 0.82, 0.85, 0.88}},
-    {SGEMM_F32_MFMA_64, 64, 64, {0.60, 0.70, 0.72, 0.83}},
+    {SGEMM_F32_MFMA_128, 128, 128, 10.5, {0.808, 0.868, 0.892, 0.912}},
+    {SGEMM_F32_MFMA_256, 256, 256, 25.5, {0.965, 0.928, 0.928, 0.928}},
+    {SGEMM_F32_MFMA_64x128, 64, 128, 5.5, {0.679, 0.733, 0.807, 0.850}},
+    {SGEMM_F32_MFMA_64, 64, 64, 11.0, {0.624, 0.620, 0.712, 0.795}},
+    {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 7.5, {0.745, 0.753, 0.776, 0.802}},
+    {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 7.5, {0.692, 0.712, 0.751, 0.766}},
 };
-// Per-tile cost that does not shrink with K (first fill, epilogue), in units
-// of K.
-static const double kTileOverheadK = 256.0;
+// Peak FP32 FLOP/s of one compute unit: 4 SIMDs x 64 FLOP/clk x 2.4 GHz.
+static const double kPeakPerCu = 4.0 * 64.0 * 2.4e9;
 // At or below this many rows the skinny kernel (HBM-bound regime) is used.
 static const int64_t kSkinnyMaxM = 32;
 // Below this many multiply-adds launch latency dominates and the fine-tiled
@@ -87,14 +87,15 @@ static int choose(int64_t M, int64_t N, int64_t K, int num_cus) {
     if (M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
     if ((double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
     int best = -1;
-    double best_cost = 0.0;
+    double best_us = 0.0;
     for (const Candidate& c : kCandidates) {
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
         const int64_t n = cdiv(tiles, num_cus);
-        const double cost = (double)n * c.bm * c.bn * ((double)K + kTileOverheadK) / eff_at(c, n);
-        if (best < 0 || cost < best_cost) {
+        const double us = c.overhead_us +
+                          1e6 * (double)n * 2.0 * c.bm * c.bn * (double)K / (kPeakPerCu * eff_at(c, n));
+        if (best < 0 || us < best_us) {
             best = c.variant;
-            best_cost = cost;
+            best_us = us;
         }
     }
     return best;

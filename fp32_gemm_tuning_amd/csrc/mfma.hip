@@ -126,9 +126,14 @@ struct TileFillDma {
     static constexpr int CPR = BK / 4;
     static constexpr int W = NT / 64;
     static constexpr int EPI = VEC ? 256 : 64;          // floats per wave instruction
-    static constexpr int A_INSTR = BM * BK / EPI / W;   // per wave per slice
-    static constexpr int B_INSTR = BK * BN / EPI / W;
-    static_assert(A_INSTR * EPI * W == BM * BK && B_INSTR * EPI * W == BK * BN, "tile/wave mismatch");
+    // Wave instructions per slice (each writes EPI floats); wave w issues
+    // pieces w, w + W, w + 2W, ... so the counts differ by at most one
+    // between waves when W does not divide them.
+    static constexpr int A_TOTAL = BM * BK / EPI, B_TOTAL = BK * BN / EPI;
+    static_assert(A_TOTAL * EPI == BM * BK && B_TOTAL * EPI == BK * BN, "tile/instruction mismatch");
+    static constexpr int A_INSTR = (A_TOTAL + W - 1) / W;   // per wave per slice, at most
+    static constexpr int B_INSTR = (B_TOTAL + W - 1) / W;
+    static constexpr bool EVEN = A_TOTAL % W == 0 && B_TOTAL % W == 0;
 
     // A slice starting at or past K is legal: its resources are empty and
     // every lane's load reads as zero (the pipelined kernel issues loads for
@@ -152,7 +157,8 @@ struct TileFillDma {
         const int w = t >> 6, lane = t & 63;
 #pragma unroll
         for (int p = 0; p < A_INSTR; ++p) {
-            const int piece = w * A_INSTR + p;
+            const int piece = w + W * p;
+            if (!EVEN && piece >= A_TOTAL) break;
             float* dst = As + piece * EPI;
             if (VEC) {
                 const int slot = piece * 64 + lane;       // 16-byte chunk index in As
@@ -169,7 +175,8 @@ struct TileFillDma {
         }
 #pragma unroll
         for (int p = 0; p < B_INSTR; ++p) {
-            const int piece = w * B_INSTR + p;
+            const int piece = w + W * p;
+            if (!EVEN && piece >= B_TOTAL) break;
             float* dst = Bs + piece * EPI;
             if (VEC) {
                 const int slot = piece * 64 + lane;
@@ -380,6 +387,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int BI = WM / 32, BJ = WN / 32;
     using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
     constexpr int BNP = Dma::BNP;
+    static_assert(Dma::EVEN, "the ring barrier counts the same loads on every wave");
     constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert((STAGES - 1) * G < 64, "outstanding loads exceed vmcnt");
@@ -526,6 +534,167 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
             }
 }
 
+// ===========================================================================
+// mfma_64x128_kg4: a 64x128 tile computed by 16 waves in four K-groups of
+// four (each wave 32x64, as in mfma_64x128). Group g multiplies the slices
+// g, g+4, g+8, ... from its own two LDS stages, so a compute unit holds 16
+// waves of one tile instead of 4, and a shape with fewer tiles than compute
+// units (the odd 1000x1531x777 has 192) still keeps four waves on every
+// SIMD of the units it uses. The pages split K across blocks with a
+// workspace ("Optimizing Matrix Multiply on CUDA, Part 2", "Selecting Among
+// Three Kernels"); here the split stays inside the workgroup: the four
+// partial tiles are summed through LDS in the fixed order g = 0, 1, 2, 3, so
+// the result does not depend on timing. One workgroup per compute unit
+// (96 KB of LDS).
+// ===========================================================================
+template <int BM, int BN, int WM, int WN, bool VEC>
+__global__ __launch_bounds__(4 * (BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN), (BM / WM) * (BN / WN))))
+void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    constexpr int BK = 16, KG = 4;
+    constexpr int GT = (BM / WM) * (BN / WN) * 64;  // threads per K-group
+    constexpr int WAVES_N = BN / WN;
+    constexpr int BI = WM / 32, BJ = WN / 32;
+    constexpr int PER_LANE = BI * BJ * 16;  // accumulators per lane
+    using Dma = TileFillDma<BM, BN, BK, GT, VEC>;
+    constexpr int BNP = Dma::BNP;
+    // Stage objects, one per stage (so that the fill of one stage is never
+    // taken for a write to the stage being read), each holding all groups.
+    __shared__ __attribute__((aligned(16))) float As0[KG * BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs0[KG * BK * BNP];
+    __shared__ __attribute__((aligned(16))) float As1[KG * BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs1[KG * BK * BNP];
+    // After the K loop the partial tiles are summed through the B stages.
+    static_assert(KG == 4 && KG * BK * BNP >= PER_LANE * GT, "a partial tile must fit a B stage");
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+    const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63;
+    const int g = __builtin_amdgcn_readfirstlane(t / GT), tl = t % GT, wl = tl >> 6;
+    const int wm = wl / WAVES_N, wn = wl % WAVES_N;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[BI][BJ];
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Fragment offsets as in k_mfma_tile (lanes 0-31 take k = s, lanes 32-63
+    // k = 8 + s at MFMA step s), within this group's part of a stage.
+    int aoff[BI][2], boff[BJ];
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi) {
+        const int row = wm * WM + bi * 32 + c;
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+            aoff[bi][v] = g * BM * BK + row * BK + (((2 * h + v) ^ swz16(row)) << 2);
+    }
+#pragma unroll
+    for (int bj = 0; bj < BJ; ++bj) boff[bj] = g * BK * BNP + 8 * h * BNP + wn * WN + bj * 32 + c;
+
+    auto compute = [&](const float* Ac, const float* Bc) {
+        float af[BI][8], bf[BJ][8];
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi) {
+            const f32x4 lo = *(const f32x4*)&Ac[aoff[bi][0]];
+            const f32x4 hi = *(const f32x4*)&Ac[aoff[bi][1]];
+            af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
+            af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+        }
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+    };
+
+    // Step i: group g multiplies slice i*KG + g from the current stage while
+    // its loads of slice (i+1)*KG + g fill the other one; one workgroup
+    // barrier per step (it also waits for each wave's loads).
+    const int nslices = (a.K + BK - 1) / BK;
+    const int nsteps = (nslices + KG - 1) / KG;
+    const Dma dma;
+    auto step = [&](int i, float* Acur, float* Bcur, float* Anext, float* Bnext) {
+        const int s = i * KG + g;
+        if (s + KG < nslices)
+            dma.issue(a, tl, m0, n0, (s + KG) * BK, rows_valid, cols_valid, Anext + g * BM * BK,
+                      Bnext + g * BK * BNP);
+        if (s < nslices) compute(Acur, Bcur);
+        __syncthreads();
+    };
+    if (g < nslices)
+        dma.issue(a, tl, m0, n0, g * BK, rows_valid, cols_valid, As0 + g * BM * BK,
+                  Bs0 + g * BK * BNP);
+    __syncthreads();
+    for (int i = 0; i < nsteps; i += 2) {
+        step(i, As0, Bs0, As1, Bs1);
+        if (i + 1 < nsteps) step(i + 1, As1, Bs1, As0, Bs0);
+    }
+
+    // Fixed-order reduction of the four partial tiles (the last step's
+    // barrier has retired every read of the stages).
+    // Two-level tree in a fixed order, (p0 + p2) + (p1 + p3), through the B
+    // stages: each wave holds at most one partial tile besides its own. The
+    // accumulators of a lane travel as 16-byte vectors, vector q of thread tl
+    // at buf[(q*GT + tl)*4], so a wave's accesses are consecutive.
+    constexpr int Q = PER_LANE / 4;
+    auto put = [&](float* buf) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
+            *(f32x4*)&buf[(q * GT + tl) * 4] = f32x4{acc[bi][bj][r0], acc[bi][bj][r0 + 1],
+                                                    acc[bi][bj][r0 + 2], acc[bi][bj][r0 + 3]};
+        }
+    };
+    auto add = [&](const float* buf) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
+            const f32x4 v = *(const f32x4*)&buf[(q * GT + tl) * 4];
+            acc[bi][bj][r0] += v.x;
+            acc[bi][bj][r0 + 1] += v.y;
+            acc[bi][bj][r0 + 2] += v.z;
+            acc[bi][bj][r0 + 3] += v.w;
+        }
+    };
+    if (g == 2) put(Bs0);
+    if (g == 3) put(Bs1);
+    __syncthreads();
+    if (g == 0) add(Bs0);
+    if (g == 1) add(Bs1);
+    __syncthreads();
+    if (g == 1) put(Bs0);
+    __syncthreads();
+    if (g != 0) return;
+    add(Bs0);
+
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int j = wn * WN + bj * 32 + c;
+                if (i < rows_valid && j < cols_valid)
+                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+            }
+}
+
 // Host-side limits shared by the tiled MFMA kernels: per-slice buffer extents
 // must stay below 2^31 bytes.
 static bool extents_ok(const Args& a, int BM, int BN, int BK) {
@@ -642,6 +811,36 @@ static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
 }
 
 Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT};
+
+template <int BM, int BN, int WM, int WN>
+struct KgroupInstance {
+    static constexpr int NT = 4 * (BM / WM) * (BN / WN) * 64;
+    static int check(const Args& a) {
+        if (!extents_ok(a, BM, BN, 16)) return SGEMM_F32_ERR_TOO_LARGE;
+        const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
+        return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+    }
+    static hipError_t launch(const Args& a, hipStream_t s) {
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
+        if (vec_ok(a))
+            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, true>), grid, block, 0, s, a, tm, tn,
+                               xcd_remap_enabled());
+        else
+            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, false>), grid, block, 0, s, a, tm, tn,
+                               xcd_remap_enabled());
+        return hipGetLastError();
+    }
+    static const void* kernel() { return (const void*)k_mfma_kgroup<BM, BN, WM, WN, true>; }
+};
+
+// 64x128 tile, 4 groups of 4 waves of 32x64 (16 waves, 96 KB LDS).
+using Kg128 = KgroupInstance<64, 128, 32, 64>;
+Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::kernel(), Kg128::NT};
+// 64x96 tile, 4 groups of 3 waves of 64x32 (12 waves, 80 KB LDS): the odd
+// 1000x1531 output is exactly 256 such tiles.
+using Kg96 = KgroupInstance<64, 96, 64, 32>;
+Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2

@@ -119,7 +119,13 @@ enum sgemm_f32_variant_id {
        half slice overlap the MFMAs of the other, and the barrier sits
        between the halves; for large shapes */
     SGEMM_F32_MFMA_256 = 13,
-    SGEMM_F32_NUM_VARIANTS = 14
+    /* FP32 matrix-core kernel, 64x128 block tile of 16 waves in four K-groups
+       (group g takes slices g, g+4, ...), partial tiles summed through LDS in
+       a fixed order; for shapes with fewer tiles than compute units */
+    SGEMM_F32_MFMA_64x128_KG4 = 14,
+    /* the same with a 64x96 tile of 12 waves (4 groups of 3 waves of 64x32) */
+    SGEMM_F32_MFMA_64x96_KG4 = 15,
+    SGEMM_F32_NUM_VARIANTS = 16
 };
 
 /* C = alpha*A*B + beta*C, kernel chosen automatically (see sgemm_f32_plan). */

@@ -102,11 +102,11 @@ def _plan(M, N, K, lda=None, ldb=None, ldc=None, cus=256, off=0):
 def test_plan_picks_matrix_core_kernels_for_the_workloads():
     w = WORKLOADS
     assert _plan(4096, 4096, 4096) == "mfma_256x256"
-    assert _plan(w["S2048"].M, w["S2048"].N, w["S2048"].K) == "mfma_64x128"
+    assert _plan(w["S2048"].M, w["S2048"].N, w["S2048"].K) == "mfma_128x128"
     assert _plan(w["S8192"].M, w["S8192"].N, w["S8192"].K) == "mfma_256x256"
     assert _plan(w["S4092"].M, w["S4092"].N, w["S4092"].K) == "mfma_256x256"
-    # 96 tiles of 128x128 on 256 compute units: the 64x128 tile wins
-    assert _plan(w["R_odd"].M, w["R_odd"].N, w["R_odd"].K) == "mfma_64x128"
+    # 1000 x 1531 is exactly 256 tiles of 64x96: one 12-wave K-split tile per CU
+    assert _plan(w["R_odd"].M, w["R_odd"].N, w["R_odd"].K) == "mfma_64x96_kg4"
     assert _plan(w["R_skinny"].M, w["R_skinny"].N, w["R_skinny"].K) == "mfma_skinny"
     assert _plan(256, 256, 256) == "mfma_direct"
 
@@ -115,13 +115,14 @@ def test_plan_busiest_cu_rule():
     # 4096^2: one 256^2 tile per CU (16 waves of one workgroup) beats four
     # 128^2 tiles, eight 64x128 or sixteen 64^2 tiles.
     assert _plan(4096, 4096, 4096, cus=256) == "mfma_256x256"
-    # 2048^2: 64 tiles of 256^2 would leave 192 CUs idle; two 64x128 tiles per
-    # CU beat one 128^2 tile each.
-    assert _plan(2048, 2048, 2048, cus=256) == "mfma_64x128"
+    # 2048^2: 64 tiles of 256^2 would leave 192 CUs idle; one 128^2 tile each.
+    assert _plan(2048, 2048, 2048, cus=256) == "mfma_128x128"
     # 4096 x 2048: 128 tiles of 256^2 (half the CUs) lose to two 128^2 per CU.
     assert _plan(4096, 2048, 4096, cus=256) == "mfma_128x128"
-    # 1024x1536: 96 tiles of 128^2 keep 160 CUs idle; 192 of 64x128 do not.
-    assert _plan(1024, 1536, 768, cus=256) == "mfma_64x128"
+    # 1024x1536: 96 tiles of 128^2 keep 160 CUs idle; 256 tiles of 64x96 do not.
+    assert _plan(1024, 1536, 768, cus=256) == "mfma_64x96_kg4"
+    # 1000^3: 256 tiles of 64^2 (with 16 of them ragged) on 256 CUs.
+    assert _plan(1000, 1000, 1000, cus=256) == "mfma_64x64"
     # 8192^2: four rounds of 256^2 tiles.
     assert _plan(8192, 8192, 8192, cus=256) == "mfma_256x256"
     # a single CU: the largest tile always wins.
