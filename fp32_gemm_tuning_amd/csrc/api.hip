@@ -14,7 +14,7 @@ namespace sgemm {
 static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
     &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
-    &kMfma256, &kMfmaKgroup, &kMfmaKgroup96,
+    &kMfma256, &kMfmaKgroup, &kMfmaKgroup96, &kMfmaKgroup128,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
@@ -51,8 +51,9 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // unit's n * 2*BM*BN*K FLOP at a fraction of its peak that depends on n
 // (few tiles per unit leave the matrix cores waiting on fills and barriers).
 // Both were fitted per kernel to interleaved timings of every candidate on
-// 24 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X; the
-// fitted model picks the fastest kernel or one within 6% on all of them.
+// 26 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X; the
+// fitted model picks the fastest kernel on 23 of them and one within 9% on
+// the rest.
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
@@ -63,12 +64,13 @@ struct Candidate {
 
 // Listed in order of preference when predictions tie.
 static const Candidate kCandidates[] = {
-    {SGEMM_F32_MFMA_128, 128, 128, 10.5, {0.808, 0.868, 0.892, 0.912}},
-    {SGEMM_F32_MFMA_256, 256, 256, 25.5, {0.965, 0.928, 0.928, 0.928}},
-    {SGEMM_F32_MFMA_64x128, 64, 128, 5.5, {0.679, 0.733, 0.807, 0.850}},
-    {SGEMM_F32_MFMA_64, 64, 64, 11.0, {0.624, 0.620, 0.712, 0.795}},
-    {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 7.5, {0.745, 0.753, 0.776, 0.802}},
-    {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 7.5, {0.692, 0.712, 0.751, 0.766}},
+    {SGEMM_F32_MFMA_128, 128, 128, 11.0, {0.820, 0.877, 0.900, 0.907}},
+    {SGEMM_F32_MFMA_256, 256, 256, 24.5, {0.961, 0.927, 0.925, 0.925}},
+    {SGEMM_F32_MFMA_64x128, 64, 128, 6.5, {0.694, 0.734, 0.805, 0.844}},
+    {SGEMM_F32_MFMA_64, 64, 64, 7.5, {0.515, 0.606, 0.692, 0.783}},
+    {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 9.5, {0.790, 0.761, 0.778, 0.805}},
+    {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.5, {0.752, 0.721, 0.762, 0.769}},
+    {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 16.0, {0.903, 0.870, 0.871, 0.875}},
 };
 // Peak FP32 FLOP/s of one compute unit: 4 SIMDs x 64 FLOP/clk x 2.4 GHz.
 static const double kPeakPerCu = 4.0 * 64.0 * 2.4e9;

@@ -33,7 +33,7 @@ extern Variant kNaive, kCoalesced, kLdsTiled, kReg1d, kReg2d, kVec4TransA;
 extern Variant kValuMain;
 // mfma.hip
 extern Variant kMfma128, kMfma64, kMfmaSkinny, kMfmaKsplit, kMfmaDirect, kMfma64x128,
-    kMfma256, kMfmaKgroup, kMfmaKgroup96;
+    kMfma256, kMfmaKgroup, kMfmaKgroup96, kMfmaKgroup128;
 
 // Common host checks.
 bool aligned16(const void* p);

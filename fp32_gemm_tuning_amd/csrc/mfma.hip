@@ -564,8 +564,7 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     __shared__ __attribute__((aligned(16))) float Bs0[KG * BK * BNP];
     __shared__ __attribute__((aligned(16))) float As1[KG * BM * BK];
     __shared__ __attribute__((aligned(16))) float Bs1[KG * BK * BNP];
-    // After the K loop the partial tiles are summed through the B stages.
-    static_assert(KG == 4 && KG * BK * BNP >= PER_LANE * GT, "a partial tile must fit a B stage");
+    static_assert(KG == 4, "four K-groups");
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
@@ -647,40 +646,60 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 
     // Fixed-order reduction of the four partial tiles (the last step's
     // barrier has retired every read of the stages).
-    // Two-level tree in a fixed order, (p0 + p2) + (p1 + p3), through the B
+    // Two-level tree in a fixed order, (p0 + p2) + (p1 + p3), through the
     // stages: each wave holds at most one partial tile besides its own. The
-    // accumulators of a lane travel as 16-byte vectors, vector q of thread tl
-    // at buf[(q*GT + tl)*4], so a wave's accesses are consecutive.
+    // accumulators of a lane travel as 16-byte vectors; vector q of thread tl
+    // goes to lo[(q*GT + tl)*4] for q < Q/2 and to hi[((q - Q/2)*GT + tl)*4]
+    // above, so a wave's accesses are consecutive. Slot 0 is stage 0 and slot
+    // 1 stage 1: each half of a slot is its B part when a whole partial tile
+    // fits in it, else the A part and the B part.
     constexpr int Q = PER_LANE / 4;
-    auto put = [&](float* buf) {
+    constexpr bool IN_B = KG * BK * BNP >= PER_LANE * GT;
+    static_assert(IN_B || (KG * BK * BNP >= PER_LANE / 2 * GT && KG * BM * BK >= PER_LANE / 2 * GT),
+                  "a partial tile must fit one LDS stage");
+    auto slot = [&](int j, float*& lo, float*& hi) {
+        float* A = j == 0 ? As0 : As1;
+        float* B = j == 0 ? Bs0 : Bs1;
+        lo = B + tl * 4;
+        hi = (IN_B ? B + Q / 2 * GT * 4 : A) + tl * 4;
+    };
+    auto put = [&](int j) {
+        float *lo, *hi;
+        slot(j, lo, hi);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
-            *(f32x4*)&buf[(q * GT + tl) * 4] = f32x4{acc[bi][bj][r0], acc[bi][bj][r0 + 1],
-                                                    acc[bi][bj][r0 + 2], acc[bi][bj][r0 + 3]};
+            *(f32x4*)(q < Q / 2 ? lo + q * GT * 4 : hi + (q - Q / 2) * GT * 4) =
+                f32x4{acc[bi][bj][r0], acc[bi][bj][r0 + 1], acc[bi][bj][r0 + 2], acc[bi][bj][r0 + 3]};
         }
     };
-    auto add = [&](const float* buf) {
+    auto add = [&](int j) {
+        float *lo, *hi;
+        slot(j, lo, hi);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
-            const f32x4 v = *(const f32x4*)&buf[(q * GT + tl) * 4];
+            const f32x4 v = *(const f32x4*)(q < Q / 2 ? lo + q * GT * 4 : hi + (q - Q / 2) * GT * 4);
             acc[bi][bj][r0] += v.x;
             acc[bi][bj][r0 + 1] += v.y;
             acc[bi][bj][r0 + 2] += v.z;
             acc[bi][bj][r0 + 3] += v.w;
+            // After each 32x32 block: the block's sums must exist before
+            // later loads issue, or the compiler loads the whole partial
+            // tile first and spills registers.
+            if (q % 4 == 3) asm volatile("" : "+v"(acc[bi][bj])::"memory");
         }
     };
-    if (g == 2) put(Bs0);
-    if (g == 3) put(Bs1);
+    if (g == 2) put(0);
+    if (g == 3) put(1);
     __syncthreads();
-    if (g == 0) add(Bs0);
-    if (g == 1) add(Bs1);
+    if (g == 0) add(0);
+    if (g == 1) add(1);
     __syncthreads();
-    if (g == 1) put(Bs0);
+    if (g == 1) put(0);
     __syncthreads();
     if (g != 0) return;
-    add(Bs0);
+    add(0);
 
 #pragma unroll
     for (int bi = 0; bi < BI; ++bi)
@@ -839,8 +858,20 @@ using Kg128 = KgroupInstance<64, 128, 32, 64>;
 Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::kernel(), Kg128::NT};
 // 64x96 tile, 4 groups of 3 waves of 64x32 (12 waves, 80 KB LDS): the odd
 // 1000x1531 output is exactly 256 such tiles.
-using Kg96 = KgroupInstance<64, 96, 64, 32>;
+#ifndef SGEMM_KG96_BM
+#define SGEMM_KG96_BM 64
+#define SGEMM_KG96_BN 96
+#define SGEMM_KG96_WM 64
+#define SGEMM_KG96_WN 32
+#endif
+using Kg96 = KgroupInstance<SGEMM_KG96_BM, SGEMM_KG96_BN, SGEMM_KG96_WM, SGEMM_KG96_WN>;
 Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT};
+// 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
+// tile per compute unit for medium shapes such as 2048^3 (256 tiles), where
+// mfma_128x128 would leave one wave per SIMD.
+using Kg128x128 = KgroupInstance<128, 128, 64, 64>;
+Variant kMfmaKgroup128 = {"mfma_128x128_kg4", Kg128x128::check, Kg128x128::launch,
+                          Kg128x128::kernel(), Kg128x128::NT};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2

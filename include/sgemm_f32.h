@@ -125,7 +125,9 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_MFMA_64x128_KG4 = 14,
     /* the same with a 64x96 tile of 12 waves (4 groups of 3 waves of 64x32) */
     SGEMM_F32_MFMA_64x96_KG4 = 15,
-    SGEMM_F32_NUM_VARIANTS = 16
+    /* the same with a 128x128 tile of 16 waves (4 groups of 4 waves of 64x64) */
+    SGEMM_F32_MFMA_128x128_KG4 = 16,
+    SGEMM_F32_NUM_VARIANTS = 17
 };
 
 /* C = alpha*A*B + beta*C, kernel chosen automatically (see sgemm_f32_plan). */
