@@ -117,20 +117,27 @@ struct TileFill {
 // The same fill with gfx950's buffer-to-LDS loads: no prefetch registers and
 // no LDS store instructions; a wave instruction writes 64 x 16 bytes (VEC) or
 // 64 x 4 bytes contiguously, so each lane computes which global element
-// belongs at its destination slot (inverting the A swizzle). B rows are not
-// padded: its fragment reads are 4-byte reads, which the LDS serves one
-// half-wave at a time, each half reading 32 consecutive floats of one row.
-template <int BM, int BN, int BK, int NT, bool VEC>
+// belongs at its destination slot. B rows are not padded: its fragment reads
+// are 4-byte reads, which the LDS serves one half-wave at a time, each half
+// reading 32 consecutive floats of one row. A rows are either swizzled
+// (PADA = false: the lane inverts the XOR swizzle) or padded by one 16-byte
+// chunk (PADA = true: row pitch BK + 4 floats; the pad slots load zeros).
+// With 16 consecutive rows read at one chunk the padded pitch spreads them
+// over 16 distinct 4-bank groups of the 64-bank LDS, and a fragment's chunk
+// offset becomes a constant that folds into the read instruction.
+template <int BM, int BN, int BK, int NT, bool VEC, bool PADA = false>
 struct TileFillDma {
     static constexpr int BNP = BN;
-    static constexpr int CPR = BK / 4;
+    static constexpr int CPR = BK / 4;                  // 16-byte chunks of A data per row
+    static constexpr int APITCH = BK + (PADA ? 4 : 0);  // floats per A row in LDS
     static constexpr int W = NT / 64;
     static constexpr int EPI = VEC ? 256 : 64;          // floats per wave instruction
     // Wave instructions per slice (each writes EPI floats); wave w issues
     // pieces w, w + W, w + 2W, ... so the counts differ by at most one
     // between waves when W does not divide them.
-    static constexpr int A_TOTAL = BM * BK / EPI, B_TOTAL = BK * BN / EPI;
-    static_assert(A_TOTAL * EPI == BM * BK && B_TOTAL * EPI == BK * BN, "tile/instruction mismatch");
+    static constexpr int A_TOTAL = BM * APITCH / EPI, B_TOTAL = BK * BN / EPI;
+    static_assert(A_TOTAL * EPI == BM * APITCH && B_TOTAL * EPI == BK * BN,
+                  "tile/instruction mismatch");
     static constexpr int A_INSTR = (A_TOTAL + W - 1) / W;   // per wave per slice, at most
     static constexpr int B_INSTR = (B_TOTAL + W - 1) / W;
     static constexpr bool EVEN = A_TOTAL % W == 0 && B_TOTAL % W == 0;
@@ -160,11 +167,21 @@ struct TileFillDma {
             const int piece = w + W * p;
             if (!EVEN && piece >= A_TOTAL) break;
             float* dst = As + piece * EPI;
-            if (VEC) {
+            if (VEC && PADA) {
+                const int slot = piece * 64 + lane;       // 16-byte slot index in As
+                const int row = slot / (CPR + 1), q = slot % (CPR + 1);
+                const bool ok = q < CPR && row < rows_valid && 4 * q + 4 <= kk;
+                buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
+            } else if (VEC) {
                 const int slot = piece * 64 + lane;       // 16-byte chunk index in As
                 const int row = slot / CPR, q = (slot % CPR) ^ swz_chunk<BK>(row);
                 const bool ok = row < rows_valid && 4 * q + 4 <= kk;
                 buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
+            } else if (PADA) {
+                const int f = piece * 64 + lane;          // float index in As
+                const int row = f / APITCH, kq = f % APITCH;
+                const bool ok = kq < kk && row < rows_valid;   // kk <= BK: pads fail
+                buf_load_lds4(rA, dst, ok ? (uint32_t)((row * (int)a.lda + kq) * 4) : OOB);
             } else {
                 const int f = piece * 64 + lane;          // float index in As
                 const int row = f / BK, pc = (f % BK) >> 2;
@@ -376,7 +393,7 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool PADA>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
@@ -385,21 +402,23 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int BI = WM / 32, BJ = WN / 32;
-    using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
-    constexpr int BNP = Dma::BNP;
-    static_assert(Dma::EVEN, "the ring barrier counts the same loads on every wave");
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC, PADA>;
+    constexpr int BNP = Dma::BNP, APITCH = Dma::APITCH;
+    // Deeper rings count outstanding loads, which must then be the same on
+    // every wave; with two stages the barrier waits for all of them.
+    static_assert(Dma::EVEN || STAGES == 2, "the ring barrier counts the same loads on every wave");
     constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert((STAGES - 1) * G < 64, "outstanding loads exceed vmcnt");
     // One LDS object per stage, so that the compiler can tell the stage being
     // filled from the stages being read (unused stages are dropped).
-    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
+    __shared__ __attribute__((aligned(16))) float As0[BM * APITCH];
     __shared__ __attribute__((aligned(16))) float Bs0[BK * BNP];
-    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
+    __shared__ __attribute__((aligned(16))) float As1[BM * APITCH];
     __shared__ __attribute__((aligned(16))) float Bs1[BK * BNP];
-    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? BM * BK : 4];
+    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? BM * APITCH : 4];
     __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? BK * BNP : 4];
-    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? BM * BK : 4];
+    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? BM * APITCH : 4];
     __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? BK * BNP : 4];
     float* const Ast[4] = {As0, As1, As2, As3};
     float* const Bst[4] = {Bs0, Bs1, Bs2, Bs3};
@@ -436,8 +455,8 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 #pragma unroll
     for (int bi = 0; bi < BI; ++bi) {
         const int row = wm * WM + bi * 32 + c;
-        arow[bi] = row * BK;
-        achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
+        arow[bi] = row * APITCH;
+        achunk[bi] = PADA ? P * h : ((P * h) ^ swz_chunk<BK>(row));
     }
 #pragma unroll
     for (int bj = 0; bj < BJ; ++bj) boff[bj] = (BK / 2) * h * BNP + wn * WN + bj * 32 + c;
@@ -445,15 +464,15 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi)
-            f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
+            f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((PADA ? achunk[bi] + v : achunk[bi] ^ v) << 2)];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[boff[bj] + (4 * v + k) * BNP];
     };
-    auto mma_part = [&](const PartFrag<BI, BJ>& f) {
+    auto mma_part = [&](const PartFrag<BI, BJ>& f, int k_begin = 0, int k_end = 4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = k_begin; k < k_end; ++k)
 #pragma unroll
             for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
@@ -501,9 +520,15 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
         }
         ring_barrier<(STAGES - 2) * G>();
         read_part(f0, An, Bn, 0);   // past the last slice: read and unused
+        // The matrix cores restart on the last part's first two k-steps
+        // before the wave spends issue slots on the loads (about 1% faster
+        // than issuing the loads first).
+        __builtin_amdgcn_sched_barrier(0);
+        mma_part(f1, 0, 2);
+        __builtin_amdgcn_sched_barrier(0);
         dma.issue(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
         __builtin_amdgcn_sched_barrier(0);
-        mma_part(f1);
+        mma_part(f1, 2, 4);
         __builtin_amdgcn_sched_barrier(0);
     };
     // Whole rounds of STAGES slices, free of conditionals, then the rest.
@@ -799,14 +824,20 @@ Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
 #ifndef SGEMM_M256_STAGES
 #define SGEMM_M256_STAGES 2
 #endif
+#ifndef SGEMM_M256_BK
+#define SGEMM_M256_BK 16
+#endif
+#ifndef SGEMM_M256_PADA
+#define SGEMM_M256_PADA false
+#endif
 constexpr int M256_BM = SGEMM_M256_BM, M256_BN = SGEMM_M256_BN, M256_WM = SGEMM_M256_WM,
-              M256_WN = SGEMM_M256_WN, M256_BK = 16;
+              M256_WN = SGEMM_M256_WN, M256_BK = SGEMM_M256_BK;
 constexpr int M256_NT = (M256_BM / M256_WM) * (M256_BN / M256_WN) * 64;
 
 template <bool VEC>
 static const void* kernel_mfma256() {
     return (const void*)k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC>;
+                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC, SGEMM_M256_PADA>;
 }
 
 static int check_mfma256(const Args& a) {
@@ -820,11 +851,11 @@ static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)tm * tn)), block(M256_NT);
     if (vec_ok(a))
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, SGEMM_M256_PADA>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     else
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false, SGEMM_M256_PADA>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     return hipGetLastError();
 }
