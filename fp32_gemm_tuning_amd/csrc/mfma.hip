@@ -145,6 +145,10 @@ struct TileFillDma {
     // A slice starting at or past K is legal: its resources are empty and
     // every lane's load reads as zero (the pipelined kernel issues loads for
     // slices past the end so that every path issues the same number).
+    // FULL: the tile lies wholly inside A, B and C and K is a multiple of BK,
+    // so no lane needs a range mask; a slice past K still reads zeros
+    // through empty resources.
+    template <bool FULL = false>
     __device__ __forceinline__ void issue(const Args& a, int t, int m0, int n0, int k0,
                                           int rows_valid, int cols_valid, float* As,
                                           float* Bs) const {
@@ -157,7 +161,8 @@ struct TileFillDma {
         const int kr = a.K - k0;
         const int kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < BK ? kr : BK));
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-            a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+            a.A + (int64_t)m0 * a.lda + k0,
+            (FULL && kk == 0) ? 0u : (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(
             a.B + (int64_t)k0 * a.ldb + n0,
             kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4) : 0u);
@@ -170,12 +175,12 @@ struct TileFillDma {
             if (VEC && PADA) {
                 const int slot = piece * 64 + lane;       // 16-byte slot index in As
                 const int row = slot / (CPR + 1), q = slot % (CPR + 1);
-                const bool ok = q < CPR && row < rows_valid && 4 * q + 4 <= kk;
+                const bool ok = q < CPR && (FULL || (row < rows_valid && 4 * q + 4 <= kk));
                 buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
             } else if (VEC) {
                 const int slot = piece * 64 + lane;       // 16-byte chunk index in As
                 const int row = slot / CPR, q = (slot % CPR) ^ swz_chunk<BK>(row);
-                const bool ok = row < rows_valid && 4 * q + 4 <= kk;
+                const bool ok = FULL || (row < rows_valid && 4 * q + 4 <= kk);
                 buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
             } else if (PADA) {
                 const int f = piece * 64 + lane;          // float index in As
@@ -198,7 +203,7 @@ struct TileFillDma {
             if (VEC) {
                 const int slot = piece * 64 + lane;
                 const int krow = slot / (BN / 4), nq = slot % (BN / 4);
-                const bool ok = krow < kk && 4 * nq + 4 <= cols_valid;
+                const bool ok = FULL || (krow < kk && 4 * nq + 4 <= cols_valid);
                 buf_load_lds16(rB, dst, ok ? (uint32_t)((krow * (int)a.ldb + 4 * nq) * 4) : OOB);
             } else {
                 const int f = piece * 64 + lane;
@@ -393,7 +398,8 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool PADA>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool PADA,
+          bool FULL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
@@ -490,7 +496,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     // of loads issued after any given one is the same on every path.
 #pragma unroll
     for (int j = 0; j < STAGES; ++j)
-        dma.issue(a, t, m0, n0, j * BK, rows_valid, cols_valid, Ast[j], Bst[j]);
+        dma.template issue<FULL>(a, t, m0, n0, j * BK, rows_valid, cols_valid, Ast[j], Bst[j]);
     ring_barrier<(STAGES - 1) * G>();
     read_part(f0, Ast[0], Bst[0], 0);
 
@@ -526,7 +532,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
         __builtin_amdgcn_sched_barrier(0);
         mma_part(f1, 0, 2);
         __builtin_amdgcn_sched_barrier(0);
-        dma.issue(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
+        dma.template issue<FULL>(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
         __builtin_amdgcn_sched_barrier(0);
         mma_part(f1, 2, 4);
         __builtin_amdgcn_sched_barrier(0);
@@ -837,7 +843,7 @@ constexpr int M256_NT = (M256_BM / M256_WM) * (M256_BN / M256_WN) * 64;
 template <bool VEC>
 static const void* kernel_mfma256() {
     return (const void*)k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC, SGEMM_M256_PADA>;
+                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC, SGEMM_M256_PADA, false>;
 }
 
 static int check_mfma256(const Args& a) {
@@ -849,13 +855,18 @@ static int check_mfma256(const Args& a) {
 static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
     const int tm = (int)cdiv(a.M, M256_BM), tn = (int)cdiv(a.N, M256_BN);
     const dim3 grid((unsigned)((int64_t)tm * tn)), block(M256_NT);
-    if (vec_ok(a))
+    const bool full = a.M % M256_BM == 0 && a.N % M256_BN == 0 && a.K % M256_BK == 0;
+    if (vec_ok(a) && full)
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, SGEMM_M256_PADA>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, SGEMM_M256_PADA, true>),
+                           grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else if (vec_ok(a))
+        hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, SGEMM_M256_PADA, false>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     else
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false, SGEMM_M256_PADA>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false, SGEMM_M256_PADA, false>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     return hipGetLastError();
 }
