@@ -415,7 +415,12 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     static_assert(Dma::EVEN || STAGES == 2, "the ring barrier counts the same loads on every wave");
     constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
-    static_assert((STAGES - 1) * G < 64, "outstanding loads exceed vmcnt");
+    static_assert((STAGES - 2) * G < 64, "outstanding loads exceed vmcnt");
+    // The prologue leaves the later stages' loads in flight only when every
+    // wave issues the same G loads per slice (G is the largest per-wave
+    // count; a wave that issues fewer must wait for all of its own) and the
+    // count fits the 6-bit field.
+    constexpr int PROLOGUE_VMCNT = (Dma::EVEN && (STAGES - 1) * G < 64) ? (STAGES - 1) * G : 0;
     // One LDS object per stage, so that the compiler can tell the stage being
     // filled from the stages being read (unused stages are dropped).
     __shared__ __attribute__((aligned(16))) float As0[BM * APITCH];
@@ -497,7 +502,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 #pragma unroll
     for (int j = 0; j < STAGES; ++j)
         dma.template issue<FULL>(a, t, m0, n0, j * BK, rows_valid, cols_valid, Ast[j], Bst[j]);
-    ring_barrier<(STAGES - 1) * G>();
+    ring_barrier<PROLOGUE_VMCNT>();
     read_part(f0, Ast[0], Bst[0], 0);
 
     // Slice s lives in stage (Ac, Bc), slice s + 1 in (An, Bn); on entry f0
