@@ -206,6 +206,130 @@ def sweep(args, dev) -> int:
     return 0
 
 
+def smi_snapshot() -> dict:
+    """Current graphics clock (MHz), and socket power (W) where reported, from
+    rocm-smi (read-only); empty when the tool is unavailable."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                             capture_output=True, text=True, timeout=20).stdout
+        card = next(iter(json.loads(out[out.index("{"):]).values()))
+    except Exception:
+        return {}
+    res = {}
+    for k, v in card.items():
+        kl = k.lower()
+        try:
+            if kl.startswith("sclk") and "speed" in kl:
+                res["sclk_mhz"] = float(str(v).strip("() ").lower().replace("mhz", ""))
+            elif "power" in kl and "(w)" in kl:
+                res["power_w"] = float(v)
+        except ValueError:
+            pass
+    return res
+
+
+def copy_bandwidth_gbs(dev, mib: int = 1024, reps: int = 5) -> float:
+    """Best device-to-device copy rate, counting bytes read plus bytes written."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, 2.0 * n * 4 / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    return best
+
+
+# Workloads timed back to back over one event pair (launch overhead exposed).
+B2B_CALLS = {"S256": 200, "R_odd": 200, "R_skinny": 200}
+
+
+def regimes(args, dev) -> int:
+    """Per workload, with the automatic dispatch and inputs resident: per-launch
+    event times, back-to-back throughput, the shape's roofline from a measured
+    copy bandwidth, clock and power around the timed sets, and the oracle's
+    all-core and single-core rates on the small shapes. R_skinny also runs
+    cold: its calls alternate between two copies of B (537 MB, more than the
+    256 MB last-level cache)."""
+    import numpy as np
+    import torch
+
+    import fp32_gemm_tuning_amd as sg
+    import oracle
+    from datagen import WORKLOADS, make_inputs
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    bw = copy_bandwidth_gbs(dev)
+    print(json.dumps({"regimes": True, "copy_bandwidth_gbs": round(bw, 1)}), flush=True)
+    oracle.build(force=False)
+    for wname in args.workloads.split(","):
+        w = WORKLOADS[wname]
+        A, B, C0 = make_inputs(w)
+        dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C0))
+        cold = wname == "R_skinny"
+        dB2 = dB.clone() if cold else None
+        _, vid = sg.sgemm_f32_plan(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC, w.N, cus)
+        flip = [0]
+
+        def call(bsel=None):
+            b = dB if bsel is None else bsel
+            return sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, b, w.N, w.beta, dC, w.N, sp)
+
+        def call_cold():
+            flip[0] ^= 1
+            return call(dB2 if flip[0] else dB)
+
+        ai = w.flops / w.bytes_min
+        roof = min(FP32_PEAK_TFLOPS, ai * bw / 1e3)
+        rec = {"regimes": True, "workload": wname, "kernel": sg.sgemm_f32_variant_name(vid),
+               "ai_flop_per_byte": round(ai, 2), "roofline_tflops": round(roof, 2),
+               "roofline_bound": "fp32" if roof >= FP32_PEAK_TFLOPS else "hbm(measured copy)"}
+        for tag, fn in (("warm", call), ("cold", call_cold)) if cold else (("warm", call),):
+            smi0 = smi_snapshot()
+            durs, _ = time_calls(fn, args.steps, args.warmup, stream)
+            n_b2b = B2B_CALLS.get(wname, args.steps)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n_b2b):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            smi1 = smi_snapshot()
+            b2b = a.elapsed_time(b) / n_b2b
+            tf = w.flops / (float(np.median(durs)) * 1e-3) / 1e12
+            rec[tag] = {"event_ms_mean": round(float(durs.mean()), 4),
+                        "event_ms_median": round(float(np.median(durs)), 4),
+                        "event_ms_min": round(float(durs.min()), 4),
+                        "b2b_calls": n_b2b, "b2b_ms_per_call": round(b2b, 4),
+                        "tflops_median": round(tf, 2),
+                        "tflops_b2b": round(w.flops / (b2b * 1e-3) / 1e12, 2),
+                        "pct_of_roofline": round(100 * tf / roof, 1),
+                        "pct_fp32_peak": round(100 * tf / FP32_PEAK_TFLOPS, 1),
+                        "smi_before": smi0, "smi_after": smi1}
+        if wname in ("S256", "R_odd"):
+            res = {}
+            nthreads = oracle.max_threads()
+            for th in (nthreads, 1):
+                oracle.set_threads(th)
+                t0 = time.perf_counter()
+                oracle.sgemm_ref(A, B, C0, w.alpha, w.beta)
+                res[f"oracle_gflops_{th}_threads"] = round(w.flops / (time.perf_counter() - t0) / 1e9, 2)
+            oracle.set_threads(nthreads)
+            rec["cpu_oracle"] = res
+        print(json.dumps(rec), flush=True)
+        del dA, dB, dC, dB2
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +345,10 @@ def main() -> int:
     ap.add_argument("--context", action="store_true",
                     help="in a sweep, also time torch's FP32 matmul (vendor library, "
                          "TF32 off) as context")
+    ap.add_argument("--regimes", action="store_true",
+                    help="per workload on --workloads: event and back-to-back timing, "
+                         "roofline from a measured copy bandwidth, clock/power, oracle "
+                         "rates (one JSON line each)")
     ap.add_argument("--peak", action="store_true",
                     help="only run the peak-rate probes and print them")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -254,6 +382,8 @@ def main() -> int:
         del src, dst
     if args.sweep:
         return sweep(args, dev)
+    if args.regimes:
+        return regimes(args, dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     if args.peak:
         print(json.dumps({"measured_peak_tflops": measured_peaks(dev, torch.cuda.current_stream(dev),
