@@ -144,7 +144,8 @@ def sweep(args, dev) -> int:
     from datagen import WORKLOADS, make_inputs
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    names = list(sg.VARIANTS) if args.variants == "all" else args.variants.split(",")
+    names = (list(sg.VARIANTS) if args.variants == "all" else
+             [] if args.variants == "none" else args.variants.split(","))
     for wname in args.workloads.split(","):
         w = WORKLOADS[wname]
         A, B, C0 = make_inputs(w)
@@ -341,7 +342,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time every variant on --workloads (one JSON line each)")
     ap.add_argument("--workloads", default="S256,R_odd,R_skinny,S2048,S4092,S4096,S8192")
-    ap.add_argument("--variants", default="all")
+    ap.add_argument("--variants", default="all",
+                    help="comma-separated variant names, 'all', or 'none' (automatic choice only)")
     ap.add_argument("--context", action="store_true",
                     help="in a sweep, also time torch's FP32 matmul (vendor library, "
                          "TF32 off) as context")
