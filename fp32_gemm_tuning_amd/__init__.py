@@ -13,6 +13,7 @@ or raw device addresses as ints; they return the C status code):
     sgemm_f32_plan(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus) -> (code, variant)
     sgemm_f32_num_variants(), sgemm_f32_variant_name(v), sgemm_f32_variant_by_name(s),
     sgemm_f32_strerror(code), sgemm_f32_kernel_info(v) -> dict
+    sgemm_f32_set_model(entries) -> code, sgemm_f32_get_model() -> list of dicts
 
 Tensor helper:
     gemm(A, B, C, alpha=1.0, beta=0.0, variant=None, stream=None)
@@ -43,6 +44,15 @@ class SgemmError(RuntimeError):
     def __init__(self, code: int, where: str = "sgemm_f32"):
         self.code = int(code)
         super().__init__(f"{where} returned {code}: {sgemm_f32_strerror(code)}")
+
+
+MODEL_MAX = 16
+
+
+class ModelEntry(ctypes.Structure):
+    """sgemm_f32_model_entry: one candidate of the dispatch model."""
+    _fields_ = [("variant", ctypes.c_int), ("overhead_us", ctypes.c_double),
+                ("eff", ctypes.c_double * 4)]
 
 
 def _load() -> ctypes.CDLL:
@@ -83,6 +93,10 @@ def _load() -> ctypes.CDLL:
     lib.sgemm_f32_kernel_info.restype = c_int
     lib.sgemm_f32_peak_probe.argtypes = [c_int, c_int, c_int, vp, vp, ctypes.POINTER(ctypes.c_double)]
     lib.sgemm_f32_peak_probe.restype = c_int
+    lib.sgemm_f32_set_model.argtypes = [ctypes.POINTER(ModelEntry), c_int]
+    lib.sgemm_f32_set_model.restype = c_int
+    lib.sgemm_f32_get_model.argtypes = [ctypes.POINTER(ModelEntry), c_int]
+    lib.sgemm_f32_get_model.restype = c_int
     return lib
 
 
@@ -164,6 +178,30 @@ def sgemm_f32_peak_probe(kind: int, workgroups: int, iters: int, out, stream=Non
     rc = _lib.sgemm_f32_peak_probe(int(kind), int(workgroups), int(iters), _ptr(out),
                                    _stream(stream, out), ctypes.byref(fl))
     return int(rc), float(fl.value)
+
+
+def sgemm_f32_set_model(entries) -> int:
+    """Replace the dispatch model. `entries`: sequence of dicts with keys
+    variant (id or name), overhead_us, eff (4 floats); empty or None restores
+    the built-in model. Returns the C status code."""
+    entries = list(entries or [])
+    arr = (ModelEntry * max(1, len(entries)))()
+    for i, e in enumerate(entries):
+        v = e["variant"]
+        arr[i].variant = sgemm_f32_variant_by_name(v) if isinstance(v, str) else int(v)
+        arr[i].overhead_us = float(e["overhead_us"])
+        for b in range(4):
+            arr[i].eff[b] = float(e["eff"][b])
+    return int(_lib.sgemm_f32_set_model(arr, len(entries)))
+
+
+def sgemm_f32_get_model() -> list:
+    """The active dispatch model as a list of dicts (variant given by name)."""
+    arr = (ModelEntry * MODEL_MAX)()
+    n = int(_lib.sgemm_f32_get_model(arr, MODEL_MAX))
+    return [{"variant": sgemm_f32_variant_name(arr[i].variant),
+             "overhead_us": float(arr[i].overhead_us), "eff": [float(x) for x in arr[i].eff]}
+            for i in range(min(n, MODEL_MAX))]
 
 
 def _variant_id(variant) -> Optional[int]:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <new>
 #include <cstdlib>
 #include <cstring>
 
@@ -62,16 +63,44 @@ struct Candidate {
     double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 tiles per CU
 };
 
-// Listed in order of preference when predictions tie.
-static const Candidate kCandidates[] = {
-    {SGEMM_F32_MFMA_128, 128, 128, 11.0, {0.820, 0.877, 0.900, 0.907}},
-    {SGEMM_F32_MFMA_256, 256, 256, 24.5, {0.961, 0.927, 0.925, 0.925}},
-    {SGEMM_F32_MFMA_64x128, 64, 128, 6.5, {0.694, 0.734, 0.805, 0.844}},
-    {SGEMM_F32_MFMA_64, 64, 64, 7.5, {0.515, 0.606, 0.692, 0.783}},
-    {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 9.5, {0.790, 0.761, 0.778, 0.805}},
-    {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.5, {0.752, 0.721, 0.762, 0.769}},
-    {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 16.0, {0.903, 0.870, 0.871, 0.875}},
+// The tile kernels the model can choose among, with their block tiles.
+struct TileKernel {
+    int variant, bm, bn;
 };
+static const TileKernel kTileKernels[] = {
+    {SGEMM_F32_MFMA_128, 128, 128},        {SGEMM_F32_MFMA_256, 256, 256},
+    {SGEMM_F32_MFMA_64x128, 64, 128},      {SGEMM_F32_MFMA_64, 64, 64},
+    {SGEMM_F32_MFMA_64x128_KG4, 64, 128},  {SGEMM_F32_MFMA_64x96_KG4, 64, 96},
+    {SGEMM_F32_MFMA_128x128_KG4, 128, 128},
+};
+static const TileKernel* tile_kernel(int variant) {
+    for (const TileKernel& k : kTileKernels)
+        if (k.variant == variant) return &k;
+    return nullptr;
+}
+
+static constexpr int kMaxModel = SGEMM_F32_MODEL_MAX;
+struct Model {
+    int n;
+    Candidate c[kMaxModel];
+};
+
+// Built-in model, listed in order of preference when predictions tie.
+static const Model kDefaultModel = {7,
+                                    {
+                                        {SGEMM_F32_MFMA_128, 128, 128, 11.0, {0.820, 0.877, 0.900, 0.907}},
+                                        {SGEMM_F32_MFMA_256, 256, 256, 24.5, {0.961, 0.927, 0.925, 0.925}},
+                                        {SGEMM_F32_MFMA_64x128, 64, 128, 6.5, {0.694, 0.734, 0.805, 0.844}},
+                                        {SGEMM_F32_MFMA_64, 64, 64, 7.5, {0.515, 0.606, 0.692, 0.783}},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 9.5, {0.790, 0.761, 0.778, 0.805}},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.5, {0.752, 0.721, 0.762, 0.769}},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 16.0, {0.903, 0.870, 0.871, 0.875}},
+                                    }};
+// The active model. A replacement is published by swapping this pointer;
+// superseded models are never freed, so a concurrent reader never sees a
+// model change under it (each replacement keeps about 1 KB).
+static std::atomic<const Model*> g_model{&kDefaultModel};
+
 // Peak FP32 FLOP/s of one compute unit: 4 SIMDs x 64 FLOP/clk x 2.4 GHz.
 static const double kPeakPerCu = 4.0 * 64.0 * 2.4e9;
 // At or below this many rows the skinny kernel (HBM-bound regime) is used.
@@ -88,9 +117,11 @@ static int choose(int64_t M, int64_t N, int64_t K, int num_cus) {
     if (num_cus < 1) num_cus = 1;
     if (M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
     if ((double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
+    const Model* m = g_model.load(std::memory_order_acquire);
     int best = -1;
     double best_us = 0.0;
-    for (const Candidate& c : kCandidates) {
+    for (int i = 0; i < m->n; ++i) {
+        const Candidate& c = m->c[i];
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
         const int64_t n = cdiv(tiles, num_cus);
         const double us = c.overhead_us +
@@ -282,3 +313,41 @@ SGEMM_F32_API int sgemm_f32_kernel_info(int variant, int* threads, int* lds_byte
 }
 
 }  // extern "C"
+
+extern "C" SGEMM_F32_API int sgemm_f32_set_model(const sgemm_f32_model_entry* entries, int n) {
+    if (n < 0 || n > kMaxModel) return -2;
+    if (n == 0) {
+        g_model.store(&kDefaultModel, std::memory_order_release);
+        return 0;
+    }
+    if (entries == nullptr) return -1;
+    Model* m = new (std::nothrow) Model();
+    if (m == nullptr) return -4;
+    m->n = n;
+    for (int i = 0; i < n; ++i) {
+        const sgemm_f32_model_entry& e = entries[i];
+        const TileKernel* k = tile_kernel(e.variant);
+        bool ok = k != nullptr && e.overhead_us >= 0.0 && e.overhead_us <= 1e6;
+        for (int b = 0; b < 4; ++b) ok = ok && e.eff[b] > 0.0 && e.eff[b] <= 1.5;
+        for (int p = 0; p < i; ++p) ok = ok && entries[p].variant != e.variant;
+        if (!ok) {
+            delete m;
+            return -3;
+        }
+        m->c[i] = Candidate{e.variant, k->bm, k->bn, e.overhead_us, {e.eff[0], e.eff[1], e.eff[2], e.eff[3]}};
+    }
+    g_model.store(m, std::memory_order_release);
+    return 0;
+}
+
+extern "C" SGEMM_F32_API int sgemm_f32_get_model(sgemm_f32_model_entry* out, int cap) {
+    if (cap < 0 || (out == nullptr && cap > 0)) return -1;
+    const Model* m = g_model.load(std::memory_order_acquire);
+    for (int i = 0; i < m->n && i < cap; ++i) {
+        const Candidate& c = m->c[i];
+        out[i].variant = c.variant;
+        out[i].overhead_us = c.overhead_us;
+        for (int b = 0; b < 4; ++b) out[i].eff[b] = c.eff[b];
+    }
+    return m->n;
+}

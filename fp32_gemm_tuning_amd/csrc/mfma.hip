@@ -583,11 +583,12 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 // the result does not depend on timing. One workgroup per compute unit
 // (96 KB of LDS).
 // ===========================================================================
-template <int BM, int BN, int WM, int WN, bool VEC>
+template <int BM, int BN, int WM, int WN, int BK, bool VEC>
 __global__ __launch_bounds__(4 * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN), (BM / WM) * (BN / WN))))
 void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
-    constexpr int BK = 16, KG = 4;
+    constexpr int KG = 4;
+    constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
     constexpr int GT = (BM / WM) * (BN / WN) * 64;  // threads per K-group
     constexpr int WAVES_N = BN / WN;
     constexpr int BI = WM / 32, BJ = WN / 32;
@@ -621,40 +622,49 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Fragment offsets as in k_mfma_tile (lanes 0-31 take k = s, lanes 32-63
-    // k = 8 + s at MFMA step s), within this group's part of a stage.
-    int aoff[BI][2], boff[BJ];
+    // Fragment offsets as in k_mfma_tile (in sub-step u, lanes 0-31 take
+    // k = 16u + s and lanes 32-63 k = 16u + 8 + s at MFMA step s), within
+    // this group's part of a stage.
+    int aoff[STEPS][BI][2], boff[STEPS][BJ];
 #pragma unroll
-    for (int bi = 0; bi < BI; ++bi) {
-        const int row = wm * WM + bi * 32 + c;
-#pragma unroll
-        for (int v = 0; v < 2; ++v)
-            aoff[bi][v] = g * BM * BK + row * BK + (((2 * h + v) ^ swz16(row)) << 2);
-    }
-#pragma unroll
-    for (int bj = 0; bj < BJ; ++bj) boff[bj] = g * BK * BNP + 8 * h * BNP + wn * WN + bj * 32 + c;
-
-    auto compute = [&](const float* Ac, const float* Bc) {
-        float af[BI][8], bf[BJ][8];
+    for (int u = 0; u < STEPS; ++u) {
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi) {
-            const f32x4 lo = *(const f32x4*)&Ac[aoff[bi][0]];
-            const f32x4 hi = *(const f32x4*)&Ac[aoff[bi][1]];
-            af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
-            af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+            const int row = wm * WM + bi * 32 + c;
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+                aoff[u][bi][v] = g * BM * BK + row * BK +
+                                 (((4 * u + 2 * h + v) ^ swz_chunk<BK>(row)) << 2);
         }
 #pragma unroll
         for (int bj = 0; bj < BJ; ++bj)
+            boff[u][bj] = g * BK * BNP + (16 * u + 8 * h) * BNP + wn * WN + bj * 32 + c;
+    }
+
+    auto compute = [&](const float* Ac, const float* Bc) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+        for (int u = 0; u < STEPS; ++u) {
+            float af[BI][8], bf[BJ][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
+            for (int bi = 0; bi < BI; ++bi) {
+                const f32x4 lo = *(const f32x4*)&Ac[aoff[u][bi][0]];
+                const f32x4 hi = *(const f32x4*)&Ac[aoff[u][bi][1]];
+                af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
+                af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+            }
 #pragma unroll
-            for (int bi = 0; bi < BI; ++bi)
+            for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-                for (int bj = 0; bj < BJ; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
-                                                                       acc[bi][bj], 0, 0, 0);
+                for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[u][bj] + k * BNP];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                           acc[bi][bj], 0, 0, 0);
+        }
     };
 
     // Step i: group g multiplies slice i*KG + g from the current stage while
@@ -878,11 +888,11 @@ static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
 
 Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT};
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK = 16>
 struct KgroupInstance {
     static constexpr int NT = 4 * (BM / WM) * (BN / WN) * 64;
     static int check(const Args& a) {
-        if (!extents_ok(a, BM, BN, 16)) return SGEMM_F32_ERR_TOO_LARGE;
+        if (!extents_ok(a, BM, BN, BK)) return SGEMM_F32_ERR_TOO_LARGE;
         const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
         return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
     }
@@ -890,14 +900,14 @@ struct KgroupInstance {
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
         if (vec_ok(a))
-            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, true>), grid, block, 0, s, a, tm, tn,
+            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, true>), grid, block, 0, s, a, tm, tn,
                                xcd_remap_enabled());
         else
-            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, false>), grid, block, 0, s, a, tm, tn,
+            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, false>), grid, block, 0, s, a, tm, tn,
                                xcd_remap_enabled());
         return hipGetLastError();
     }
-    static const void* kernel() { return (const void*)k_mfma_kgroup<BM, BN, WM, WN, true>; }
+    static const void* kernel() { return (const void*)k_mfma_kgroup<BM, BN, WM, WN, BK, true>; }
 };
 
 // 64x128 tile, 4 groups of 4 waves of 32x64 (16 waves, 96 KB LDS).
@@ -905,13 +915,10 @@ using Kg128 = KgroupInstance<64, 128, 32, 64>;
 Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::kernel(), Kg128::NT};
 // 64x96 tile, 4 groups of 3 waves of 64x32 (12 waves, 80 KB LDS): the odd
 // 1000x1531 output is exactly 256 such tiles.
-#ifndef SGEMM_KG96_BM
-#define SGEMM_KG96_BM 64
-#define SGEMM_KG96_BN 96
-#define SGEMM_KG96_WM 64
-#define SGEMM_KG96_WN 32
+#ifndef SGEMM_KG96_BK
+#define SGEMM_KG96_BK 16
 #endif
-using Kg96 = KgroupInstance<SGEMM_KG96_BM, SGEMM_KG96_BN, SGEMM_KG96_WM, SGEMM_KG96_WN>;
+using Kg96 = KgroupInstance<64, 96, 64, 32, SGEMM_KG96_BK>;
 Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT};
 // 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
 // tile per compute unit for medium shapes such as 2048^3 (256 tiles), where

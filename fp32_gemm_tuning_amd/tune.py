@@ -1,0 +1,247 @@
+"""Fit sgemm_f32's dispatch model to the device at hand.
+
+The library chooses among its tiled matrix-core kernels with a model of each
+kernel's time (include/sgemm_f32.h, sgemm_f32_model_entry): a fixed cost plus
+the busiest compute unit's work at a fraction of its peak that depends on how
+many tiles that unit holds. This follows the pages' kernel selection by the
+busiest SM's work ("Optimizing Matrix Multiply on CUDA, Part 2", "Selecting
+Among Three Kernels") and their remark that tile choices do not carry over
+between GPUs ("GEMM from scratch", Module 08): the constants are measured.
+
+    measure()  interleaved HIP-event timing of every tiled kernel on a set of
+               shapes (the order of kernels rotates between rounds)
+    fit()      per kernel, the fixed cost on a grid and, for each tiles-per-CU
+               bucket, the median fraction of peak; the fixed cost that best
+               predicts that kernel's times (mean |log(predicted/measured)|) wins
+    install()  hand a model to the library (sgemm_f32_set_model)
+    save(), load()  a model as JSON
+
+Command line (on the GPU):
+    python -m fp32_gemm_tuning_amd.tune --out model.json [--quick]
+    python -m fp32_gemm_tuning_amd.tune --load model.json   (installs and prints plans)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import sys
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import fp32_gemm_tuning_amd as sg
+
+# Block tile of every kernel the model can choose (the library checks the
+# same list when a model is installed), in the built-in model's order, which
+# is also the order of preference when predictions tie.
+TILE: Dict[str, Tuple[int, int]] = {
+    "mfma_128x128": (128, 128),
+    "mfma_256x256": (256, 256),
+    "mfma_64x128": (64, 128),
+    "mfma_64x64": (64, 64),
+    "mfma_64x128_kg4": (64, 128),
+    "mfma_64x96_kg4": (64, 96),
+    "mfma_128x128_kg4": (128, 128),
+}
+PEAK_PER_CU = 4 * 64 * 2.4e9   # FP32 matrix FLOP/s of one MI355X compute unit
+
+# Shapes the built-in model was fitted on: square, flat, tall, odd, short-K.
+DEFAULT_SHAPES: List[Tuple[int, int, int]] = [
+    (512, 512, 512), (768, 768, 768), (1024, 1024, 1024), (1280, 1280, 1280),
+    (1536, 1536, 1536), (2048, 2048, 2048), (2560, 2560, 2560), (3072, 3072, 3072),
+    (3584, 3584, 3584), (4096, 4096, 4096), (5000, 5000, 5000), (6144, 6144, 6144),
+    (8192, 8192, 8192), (1000, 1531, 777), (1024, 1536, 768), (1000, 1531, 1500),
+    (2000, 1531, 777), (8192, 1024, 8192), (4096, 2048, 4096), (1024, 8192, 1024),
+    (3000, 3000, 500), (500, 3000, 3000), (4000, 4000, 256), (2048, 2048, 8192),
+    (1024, 1024, 4096), (2048, 4096, 2048),
+]
+QUICK_SHAPES: List[Tuple[int, int, int]] = [
+    (1024, 1024, 1024), (1000, 1531, 777), (2048, 2048, 2048), (3072, 3072, 3072),
+    (4096, 4096, 4096), (8192, 1024, 8192),
+]
+
+
+def bucket(n: int) -> int:
+    """Tiles-per-CU bucket of a model entry: n = 1, 2, 3-4, >= 5."""
+    return 0 if n <= 1 else 1 if n == 2 else 2 if n <= 4 else 3
+
+
+def tiles_per_cu(variant: str, M: int, N: int, num_cus: int) -> int:
+    bm, bn = TILE[variant]
+    return -(-(-(-M // bm) * -(-N // bn)) // max(1, num_cus))
+
+
+def predict_us(entry: dict, M: int, N: int, K: int, num_cus: int,
+               peak_per_cu: float = PEAK_PER_CU) -> float:
+    """The library's prediction for one model entry (sgemm_f32_model_entry)."""
+    bm, bn = TILE[entry["variant"]]
+    n = tiles_per_cu(entry["variant"], M, N, num_cus)
+    return entry["overhead_us"] + 1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * entry["eff"][bucket(n)])
+
+
+def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int) -> str:
+    """The entry with the smallest prediction (earlier entries win ties)."""
+    best, best_us = None, 0.0
+    for e in model:
+        us = predict_us(e, M, N, K, num_cus)
+        if best is None or us < best_us:
+            best, best_us = e["variant"], us
+    return best
+
+
+def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[str]] = None,
+            rounds: int = 3, calls: int = 4, device=None, log=None) -> List[dict]:
+    """Median HIP-event time of each (kernel, shape), kernels interleaved.
+    Returns samples {variant, M, N, K, ms}; kernels that reject a shape are
+    left out."""
+    import torch
+    dev = torch.device("cuda:0") if device is None else device
+    stream = torch.cuda.current_stream(dev)
+    variants = list(TILE) if variants is None else list(variants)
+    ids = {v: sg.sgemm_f32_variant_by_name(v) for v in variants}
+    out = []
+    for (M, N, K) in shapes:
+        g = torch.Generator(device=dev).manual_seed(M * 7 + N * 13 + K)
+        A = torch.rand(M, K, device=dev, generator=g) * 2 - 1
+        B = torch.rand(K, N, device=dev, generator=g) * 2 - 1
+        C = torch.empty(M, N, device=dev)
+        times = {v: [] for v in variants}
+        ok = {}
+        for v in variants:    # first call of each kernel: warm-up and support check
+            ok[v] = sg.sgemm_f32_variant(ids[v], M, N, K, 1.0, A, K, B, N, 0.0, C, N,
+                                         stream.cuda_stream) == 0
+        torch.cuda.synchronize()
+        live = [v for v in variants if ok[v]]
+        for r in range(rounds):
+            order = live[r % max(1, len(live)):] + live[:r % max(1, len(live))]
+            for v in order:
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(calls)]
+                for a, b in ev:
+                    a.record(stream)
+                    sg.sgemm_f32_variant(ids[v], M, N, K, 1.0, A, K, B, N, 0.0, C, N,
+                                         stream.cuda_stream)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                times[v] += [a.elapsed_time(b) for a, b in ev]
+        for v in live:
+            ts = sorted(times[v])
+            ms = ts[len(ts) // 2]
+            out.append({"variant": v, "M": M, "N": N, "K": K, "ms": ms})
+            if log:
+                log(f"{M}x{N}x{K} {v}: {ms:.4f} ms, {2.0 * M * N * K / ms / 1e9:.1f} TFLOP/s")
+        del A, B, C
+    return out
+
+
+def fit(samples: Sequence[dict], num_cus: int, peak_per_cu: float = PEAK_PER_CU,
+        t0_grid_us: Optional[Sequence[float]] = None) -> List[dict]:
+    """Per kernel: fixed cost (from the grid) and per-bucket fractions of peak
+    (medians, at most 1), choosing the fixed cost whose predictions best match
+    the measured times. Buckets without samples borrow the nearest filled one."""
+    grid = [0.5 * i for i in range(81)] if t0_grid_us is None else list(t0_grid_us)
+    by_v: Dict[str, List[Tuple[int, float, float]]] = {}
+    for s in samples:
+        bm, bn = TILE[s["variant"]]
+        n = tiles_per_cu(s["variant"], s["M"], s["N"], num_cus)
+        work_us = 1e6 * n * 2.0 * bm * bn * s["K"] / peak_per_cu   # at 100% of peak
+        by_v.setdefault(s["variant"], []).append((n, work_us, s["ms"] * 1e3))
+    model = []
+    for v in TILE:
+        ds = by_v.get(v)
+        if not ds:
+            continue
+        best = None
+        for t0 in grid:
+            per_b: Dict[int, List[float]] = {}
+            for n, w, t in ds:
+                # A fraction of peak above 1 is not physical: such a fixed
+                # cost is too large, and the capped rate shows it in the error.
+                e = w / (t - t0) if t > t0 else 1.0
+                per_b.setdefault(bucket(n), []).append(min(1.0, max(1e-3, e)))
+            eff = {b: sorted(x)[len(x) // 2] for b, x in per_b.items()}
+            full = []
+            for b in range(4):
+                if b in eff:
+                    full.append(eff[b])
+                else:
+                    near = min(eff, key=lambda k: (abs(k - b), -k))
+                    full.append(eff[near])
+            err = sum(abs(math.log((t0 + w / full[bucket(n)]) / t)) for n, w, t in ds) / len(ds)
+            if best is None or err < best[0]:
+                best = (err, t0, full)
+        model.append({"variant": v, "overhead_us": round(best[1], 3),
+                      "eff": [round(x, 4) for x in best[2]], "fit_error": round(best[0], 4)})
+    return model
+
+
+def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[dict]:
+    """Per shape: the kernel the model picks, the fastest measured one, and
+    the time lost (fraction)."""
+    by_shape: Dict[Tuple[int, int, int], Dict[str, float]] = {}
+    for s in samples:
+        by_shape.setdefault((s["M"], s["N"], s["K"]), {})[s["variant"]] = s["ms"]
+    res = []
+    for (M, N, K), d in by_shape.items():
+        sub = [e for e in model if e["variant"] in d]
+        pick = choose(sub, M, N, K, num_cus)
+        fastest = min(d, key=d.get)
+        res.append({"shape": [M, N, K], "picked": pick, "fastest": fastest,
+                    "loss": round(d[pick] / d[fastest] - 1.0, 4)})
+    return res
+
+
+def install(model: Sequence[dict]) -> int:
+    """Hand the model to the library; returns its status code."""
+    return sg.sgemm_f32_set_model([{k: e[k] for k in ("variant", "overhead_us", "eff")}
+                                   for e in model])
+
+
+def save(model: Sequence[dict], path: str, meta: Optional[dict] = None) -> None:
+    with open(path, "w") as f:
+        json.dump({"model": list(model), **(meta or {})}, f, indent=1)
+
+
+def load(path: str) -> List[dict]:
+    with open(path) as f:
+        return json.load(f)["model"]
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--out", help="write the fitted model here (JSON)")
+    ap.add_argument("--load", help="install a saved model and print the plans of the shapes")
+    ap.add_argument("--quick", action="store_true", help="6 shapes instead of 26")
+    ap.add_argument("--rounds", type=int, default=3)
+    ap.add_argument("--calls", type=int, default=4)
+    args = ap.parse_args(argv)
+    import torch
+    if not torch.cuda.is_available():
+        print("tune needs a GPU", file=sys.stderr)
+        return 1
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    shapes = QUICK_SHAPES if args.quick else DEFAULT_SHAPES
+    if args.load:
+        model = load(args.load)
+        rc = install(model)
+        print(json.dumps({"installed": args.load, "rc": rc}))
+        for (M, N, K) in shapes:
+            _, v = sg.sgemm_f32_plan(M, N, K, 1.0, 0x1000, K, 0x1000, N, 0.0, 0x1000, N, cus)
+            print(json.dumps({"shape": [M, N, K], "plan": sg.sgemm_f32_variant_name(v)}))
+        return 0 if rc == 0 else 1
+    samples = measure(shapes, rounds=args.rounds, calls=args.calls,
+                      log=lambda m: print(m, file=sys.stderr, flush=True))
+    model = fit(samples, cus)
+    report = check(model, samples, cus)
+    for e in model:
+        print(json.dumps(e))
+    worst = max(r["loss"] for r in report)
+    picked_fastest = sum(r["loss"] == 0.0 for r in report)
+    print(json.dumps({"shapes": len(report), "picked_fastest": picked_fastest,
+                      "worst_loss": worst}))
+    if args.out:
+        save(model, args.out, {"num_cus": cus, "samples": samples, "check": report})
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -150,6 +150,40 @@ SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, c
                                  int64_t lda, const float *B, int64_t ldb, float beta,
                                  const float *C, int64_t ldc, int num_cus, int *variant);
 
+/* The dispatch model sgemm_f32 uses to choose among the tiled matrix-core
+ * kernels (sgemm_f32_plan reports the choice). It follows the pages' kernel
+ * selection by the busiest SM's work ("Optimizing Matrix Multiply on CUDA,
+ * Part 2", "Selecting Among Three Kernels"), with measured constants: for a
+ * candidate with block tile BM x BN on a device with C compute units, the
+ * predicted time in microseconds is
+ *     overhead_us + 1e6 * n * 2*BM*BN*K / (614.4e9 * eff[b]),
+ * n = ceil(ceil(M/BM) * ceil(N/BN) / C), b = 0, 1, 2, 3 for n = 1, 2, 3-4, >= 5
+ * (614.4e9 FLOP/s is one compute unit's FP32 matrix peak). The smallest
+ * prediction wins; ties go to the earlier entry. M <= 32 and tiny products
+ * bypass the model (mfma_skinny, mfma_direct). */
+#define SGEMM_F32_MODEL_MAX 16
+typedef struct {
+    int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,
+                           MFMA_64x128_KG4, MFMA_64x96_KG4 or MFMA_128x128_KG4 */
+    double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
+    double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */
+} sgemm_f32_model_entry;
+
+/* Replace the process-wide dispatch model by entries[0..n). n = 0 restores the
+ * built-in model (entries may then be NULL). The library copies the entries.
+ * Returns 0; -1 if entries is NULL with n > 0; -2 if n is outside
+ * [0, SGEMM_F32_MODEL_MAX]; -3 if an entry names a variant that is not a tiled
+ * kernel, repeats one, or holds a value out of range (the model is then left
+ * unchanged); -4 if host memory runs out. Safe to call while other threads
+ * launch: each call sees either the old or the new model; each replacement
+ * keeps about 1 KB of host memory until the process ends.
+ * fp32_gemm_tuning_amd.tune fits a model to the current device. */
+SGEMM_F32_API int sgemm_f32_set_model(const sgemm_f32_model_entry *entries, int n);
+
+/* Copy the active model into out[0..cap). Returns the number of entries in the
+ * model (which may exceed cap), or -1 if cap < 0 or out is NULL with cap > 0. */
+SGEMM_F32_API int sgemm_f32_get_model(sgemm_f32_model_entry *out, int cap);
+
 /* Number of variants (SGEMM_F32_NUM_VARIANTS). */
 SGEMM_F32_API int sgemm_f32_num_variants(void);
 
