@@ -117,101 +117,104 @@ struct TileFill {
 // The same fill with gfx950's buffer-to-LDS loads: no prefetch registers and
 // no LDS store instructions; a wave instruction writes 64 x 16 bytes (VEC) or
 // 64 x 4 bytes contiguously, so each lane computes which global element
-// belongs at its destination slot. B rows are not padded: its fragment reads
-// are 4-byte reads, which the LDS serves one half-wave at a time, each half
-// reading 32 consecutive floats of one row. A rows are either swizzled
-// (PADA = false: the lane inverts the XOR swizzle) or padded by one 16-byte
-// chunk (PADA = true: row pitch BK + 4 floats; the pad slots load zeros).
-// With 16 consecutive rows read at one chunk the padded pitch spreads them
-// over 16 distinct 4-bank groups of the 64-bank LDS, and a fragment's chunk
-// offset becomes a constant that folds into the read instruction.
-template <int BM, int BN, int BK, int NT, bool VEC, bool PADA = false>
-struct TileFillDma {
-    static constexpr int BNP = BN;
-    static constexpr int CPR = BK / 4;                  // 16-byte chunks of A data per row
-    static constexpr int APITCH = BK + (PADA ? 4 : 0);  // floats per A row in LDS
+// belongs at its destination slot.
+//
+// One operand's part of a K slice is ROWS rows (along M for A, along N for
+// B) by BK values of k. Its LDS layout follows its memory layout, so that
+// every load moves whole 16-byte (or 4-byte) pieces:
+//  - k-contiguous operands (A as stored, or a transposed B) keep [row][k]: BK
+//    floats per row, 16-byte chunk q of row r at chunk q ^ swz_chunk<BK>(r)
+//    (the lane inverts the swizzle); fragments are read 16 bytes at a time;
+//  - row-contiguous operands (B as stored, or a transposed A) keep [k][row]:
+//    ROWS floats per k, unpadded; fragments are read 4 bytes at a time, which
+//    the LDS serves one half-wave at a time, each half reading 32
+//    consecutive floats of one row.
+// Element (row, k) of the slice starting at k0 is X[(r0 + row)*ld + k0 + k]
+// in memory when the operand is k-contiguous, else X[(k0 + k)*ld + r0 + row].
+// Wave w issues pieces w, w + W, w + 2W, ... of the TOTAL per slice, so the
+// per-wave counts differ by at most one when W does not divide TOTAL.
+template <int ROWS, int BK, int NT, bool VEC, bool KCONTIG>
+struct OperandFill {
     static constexpr int W = NT / 64;
-    static constexpr int EPI = VEC ? 256 : 64;          // floats per wave instruction
-    // Wave instructions per slice (each writes EPI floats); wave w issues
-    // pieces w, w + W, w + 2W, ... so the counts differ by at most one
-    // between waves when W does not divide them.
-    static constexpr int A_TOTAL = BM * APITCH / EPI, B_TOTAL = BK * BN / EPI;
-    static_assert(A_TOTAL * EPI == BM * APITCH && B_TOTAL * EPI == BK * BN,
-                  "tile/instruction mismatch");
-    static constexpr int A_INSTR = (A_TOTAL + W - 1) / W;   // per wave per slice, at most
-    static constexpr int B_INSTR = (B_TOTAL + W - 1) / W;
-    static constexpr bool EVEN = A_TOTAL % W == 0 && B_TOTAL % W == 0;
+    static constexpr int EPI = VEC ? 256 : 64;   // floats per wave instruction
+    static constexpr int TOTAL = ROWS * BK / EPI;
+    static_assert(TOTAL * EPI == ROWS * BK, "tile/instruction mismatch");
+    static constexpr int INSTR = (TOTAL + W - 1) / W;   // per wave per slice, at most
+    static constexpr bool EVEN = TOTAL % W == 0;
+    static constexpr int CPR = BK / 4;                  // 16-byte chunks per k-contiguous row
 
-    // A slice starting at or past K is legal: its resources are empty and
-    // every lane's load reads as zero (the pipelined kernel issues loads for
-    // slices past the end so that every path issues the same number).
-    // FULL: the tile lies wholly inside A, B and C and K is a multiple of BK,
-    // so no lane needs a range mask; a slice past K still reads zeros
-    // through empty resources.
+    // A slice starting at or past K is legal: its resource is empty and every
+    // lane's load reads as zero (the pipelined kernel issues loads for slices
+    // past the end so that every path issues the same number). FULL: the
+    // tile lies wholly inside the matrix and K is a multiple of BK, so no lane
+    // needs a range mask (16-byte loads only).
+    template <bool FULL>
+    __device__ __forceinline__ void issue(const float* X, int64_t ld, int r0, int k0, int K,
+                                          int rows_valid, int t, float* dst_base) const {
+        // kk = valid k in the slice (0 past the end): then no lane is in
+        // range, and the extents stay below 2^31 bytes, so the out-of-range
+        // offset always reads zero. The base address may point past the
+        // matrix; nothing is read through it. (The clamp compiles to a vector
+        // instruction; readfirstlane keeps the resource in scalar registers.)
+        const int kr = K - k0;
+        const int kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < BK ? kr : BK));
+        __amdgpu_buffer_rsrc_t r;
+        if (KCONTIG)
+            r = make_rsrc(X + (int64_t)r0 * ld + k0,
+                          (FULL && kk == 0) ? 0u : (uint32_t)(((int64_t)(rows_valid - 1) * ld + kk) * 4));
+        else
+            r = make_rsrc(X + (int64_t)k0 * ld + r0,
+                          kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * ld + rows_valid) * 4) : 0u);
+        const int ldi = (int)ld;
+        const int w = t >> 6, lane = t & 63;
+#pragma unroll
+        for (int p = 0; p < INSTR; ++p) {
+            const int piece = w + W * p;
+            if (!EVEN && piece >= TOTAL) break;
+            const float* dst = dst_base + piece * EPI;
+            if (KCONTIG && VEC) {
+                const int slot = piece * 64 + lane;       // 16-byte chunk index in the tile
+                const int row = slot / CPR, q = (slot % CPR) ^ swz_chunk<BK>(row);
+                const bool ok = FULL || (row < rows_valid && 4 * q + 4 <= kk);
+                buf_load_lds16(r, dst, ok ? (uint32_t)((row * ldi + 4 * q) * 4) : OOB);
+            } else if (KCONTIG) {
+                const int f = piece * 64 + lane;          // float index in the tile
+                const int row = f / BK, pc = (f % BK) >> 2;
+                const int kq = ((pc ^ swz_chunk<BK>(row)) << 2) | (f & 3);
+                const bool ok = row < rows_valid && kq < kk;
+                buf_load_lds4(r, dst, ok ? (uint32_t)((row * ldi + kq) * 4) : OOB);
+            } else if (VEC) {
+                const int slot = piece * 64 + lane;
+                const int krow = slot / (ROWS / 4), nq = slot % (ROWS / 4);
+                const bool ok = FULL || (krow < kk && 4 * nq + 4 <= rows_valid);
+                buf_load_lds16(r, dst, ok ? (uint32_t)((krow * ldi + 4 * nq) * 4) : OOB);
+            } else {
+                const int f = piece * 64 + lane;
+                const int krow = f / ROWS, n = f % ROWS;
+                const bool ok = krow < kk && n < rows_valid;
+                buf_load_lds4(r, dst, ok ? (uint32_t)((krow * ldi + n) * 4) : OOB);
+            }
+        }
+    }
+};
+
+// Both operands of a slice. TA / TB: the operand is stored transposed (A as
+// K x M, B as N x K, row-major), which makes A row-contiguous and B
+// k-contiguous.
+template <int BM, int BN, int BK, int NT, bool VEC, bool TA = false, bool TB = false>
+struct TileFillDma {
+    using FA = OperandFill<BM, BK, NT, VEC, !TA>;
+    using FB = OperandFill<BN, BK, NT, VEC, TB>;
+    static constexpr int BNP = BN;
+    static constexpr int A_INSTR = FA::INSTR, B_INSTR = FB::INSTR;
+    static constexpr bool EVEN = FA::EVEN && FB::EVEN;
+
     template <bool FULL = false>
     __device__ __forceinline__ void issue(const Args& a, int t, int m0, int n0, int k0,
                                           int rows_valid, int cols_valid, float* As,
                                           float* Bs) const {
-        // kk = number of valid k in the slice (0 past the end): no lane is
-        // then in range, and both extents stay below 2^31 bytes, so the
-        // out-of-range offset always reads zero. The base addresses may point
-        // past the matrices; nothing is read through them.
-        // (The clamp compiles to a vector instruction; readfirstlane keeps the
-        // resources in scalar registers.)
-        const int kr = a.K - k0;
-        const int kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < BK ? kr : BK));
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-            a.A + (int64_t)m0 * a.lda + k0,
-            (FULL && kk == 0) ? 0u : (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
-            a.B + (int64_t)k0 * a.ldb + n0,
-            kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4) : 0u);
-        const int w = t >> 6, lane = t & 63;
-#pragma unroll
-        for (int p = 0; p < A_INSTR; ++p) {
-            const int piece = w + W * p;
-            if (!EVEN && piece >= A_TOTAL) break;
-            float* dst = As + piece * EPI;
-            if (VEC && PADA) {
-                const int slot = piece * 64 + lane;       // 16-byte slot index in As
-                const int row = slot / (CPR + 1), q = slot % (CPR + 1);
-                const bool ok = q < CPR && (FULL || (row < rows_valid && 4 * q + 4 <= kk));
-                buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
-            } else if (VEC) {
-                const int slot = piece * 64 + lane;       // 16-byte chunk index in As
-                const int row = slot / CPR, q = (slot % CPR) ^ swz_chunk<BK>(row);
-                const bool ok = FULL || (row < rows_valid && 4 * q + 4 <= kk);
-                buf_load_lds16(rA, dst, ok ? (uint32_t)((row * (int)a.lda + 4 * q) * 4) : OOB);
-            } else if (PADA) {
-                const int f = piece * 64 + lane;          // float index in As
-                const int row = f / APITCH, kq = f % APITCH;
-                const bool ok = kq < kk && row < rows_valid;   // kk <= BK: pads fail
-                buf_load_lds4(rA, dst, ok ? (uint32_t)((row * (int)a.lda + kq) * 4) : OOB);
-            } else {
-                const int f = piece * 64 + lane;          // float index in As
-                const int row = f / BK, pc = (f % BK) >> 2;
-                const int kq = ((pc ^ swz_chunk<BK>(row)) << 2) | (f & 3);
-                const bool ok = row < rows_valid && kq < kk;
-                buf_load_lds4(rA, dst, ok ? (uint32_t)((row * (int)a.lda + kq) * 4) : OOB);
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < B_INSTR; ++p) {
-            const int piece = w + W * p;
-            if (!EVEN && piece >= B_TOTAL) break;
-            float* dst = Bs + piece * EPI;
-            if (VEC) {
-                const int slot = piece * 64 + lane;
-                const int krow = slot / (BN / 4), nq = slot % (BN / 4);
-                const bool ok = FULL || (krow < kk && 4 * nq + 4 <= cols_valid);
-                buf_load_lds16(rB, dst, ok ? (uint32_t)((krow * (int)a.ldb + 4 * nq) * 4) : OOB);
-            } else {
-                const int f = piece * 64 + lane;
-                const int krow = f / BN, n = f % BN;
-                const bool ok = krow < kk && n < cols_valid;
-                buf_load_lds4(rB, dst, ok ? (uint32_t)((krow * (int)a.ldb + n) * 4) : OOB);
-            }
-        }
+        FA().template issue<FULL>(a.A, a.lda, m0, k0, a.K, rows_valid, t, As);
+        FB().template issue<FULL>(a.B, a.ldb, n0, k0, a.K, cols_valid, t, Bs);
     }
 };
 
@@ -398,8 +401,7 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool PADA,
-          bool FULL>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
@@ -408,8 +410,8 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int BI = WM / 32, BJ = WN / 32;
-    using Dma = TileFillDma<BM, BN, BK, NT, VEC, PADA>;
-    constexpr int BNP = Dma::BNP, APITCH = Dma::APITCH;
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
+    constexpr int BNP = Dma::BNP, APITCH = BK;
     // Deeper rings count outstanding loads, which must then be the same on
     // every wave; with two stages the barrier waits for all of them.
     static_assert(Dma::EVEN || STAGES == 2, "the ring barrier counts the same loads on every wave");
@@ -467,7 +469,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     for (int bi = 0; bi < BI; ++bi) {
         const int row = wm * WM + bi * 32 + c;
         arow[bi] = row * APITCH;
-        achunk[bi] = PADA ? P * h : ((P * h) ^ swz_chunk<BK>(row));
+        achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
     }
 #pragma unroll
     for (int bj = 0; bj < BJ; ++bj) boff[bj] = (BK / 2) * h * BNP + wn * WN + bj * 32 + c;
@@ -475,7 +477,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi)
-            f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((PADA ? achunk[bi] + v : achunk[bi] ^ v) << 2)];
+            f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -848,9 +850,6 @@ Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
 #ifndef SGEMM_M256_BK
 #define SGEMM_M256_BK 16
 #endif
-#ifndef SGEMM_M256_PADA
-#define SGEMM_M256_PADA false
-#endif
 constexpr int M256_BM = SGEMM_M256_BM, M256_BN = SGEMM_M256_BN, M256_WM = SGEMM_M256_WM,
               M256_WN = SGEMM_M256_WN, M256_BK = SGEMM_M256_BK;
 constexpr int M256_NT = (M256_BM / M256_WM) * (M256_BN / M256_WN) * 64;
@@ -858,7 +857,7 @@ constexpr int M256_NT = (M256_BM / M256_WM) * (M256_BN / M256_WN) * 64;
 template <bool VEC>
 static const void* kernel_mfma256() {
     return (const void*)k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC, SGEMM_M256_PADA, false>;
+                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC, false>;
 }
 
 static int check_mfma256(const Args& a) {
@@ -873,15 +872,15 @@ static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
     const bool full = a.M % M256_BM == 0 && a.N % M256_BN == 0 && a.K % M256_BK == 0;
     if (vec_ok(a) && full)
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, SGEMM_M256_PADA, true>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, true>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     else if (vec_ok(a))
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, SGEMM_M256_PADA, false>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     else
         hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false, SGEMM_M256_PADA, false>),
+                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false, false>),
                            grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
     return hipGetLastError();
 }
