@@ -11,13 +11,22 @@ or raw device addresses as ints; they return the C status code):
     sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None)
     sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None)
     sgemm_f32_plan(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus) -> (code, variant)
+    sgemm_f32_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None)
+    sgemm_f32_variant_ex(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb,
+                         beta, C, ldc, stream=None)
+    sgemm_f32_plan_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      num_cus) -> (code, variant)
+    sgemm_f32_variant_trans_ok(variant)
     sgemm_f32_num_variants(), sgemm_f32_variant_name(v), sgemm_f32_variant_by_name(s),
     sgemm_f32_strerror(code), sgemm_f32_kernel_info(v) -> dict
     sgemm_f32_set_model(entries) -> code, sgemm_f32_get_model() -> list of dicts
 
 Tensor helper:
     gemm(A, B, C, alpha=1.0, beta=0.0, variant=None, stream=None)
-        C <- alpha*A@B + beta*C for row-major float32 CUDA tensors; raises SgemmError.
+        C <- alpha*A@B + beta*C for float32 CUDA tensors; raises SgemmError. A and B
+        may be transposed views (A.t() of a row-major K x M tensor, say) and C a
+        column-major one: the call then passes the matching layout and
+        transposition flags (no copy).
 """
 from __future__ import annotations
 
@@ -33,6 +42,9 @@ ERR_VARIANT = -100
 ERR_UNSUPPORTED = -101
 ERR_TOO_LARGE = -102
 ERR_DEVICE = -103
+
+ROW_MAJOR, COL_MAJOR = 0, 1
+NO_TRANS, TRANS = 0, 1
 
 VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", "valu_main",
             "mfma_128x128", "mfma_64x64", "mfma_skinny", "mfma_64x64_k4", "mfma_direct",
@@ -80,6 +92,14 @@ def _load() -> ctypes.CDLL:
     lib.sgemm_f32_variant.restype = c_int
     lib.sgemm_f32_plan.argtypes = gemm_args + [c_int, ctypes.POINTER(c_int)]
     lib.sgemm_f32_plan.restype = c_int
+    lib.sgemm_f32_ex.argtypes = [c_int, c_int, c_int] + gemm_args + [vp]
+    lib.sgemm_f32_ex.restype = c_int
+    lib.sgemm_f32_variant_ex.argtypes = [c_int, c_int, c_int, c_int] + gemm_args + [vp]
+    lib.sgemm_f32_variant_ex.restype = c_int
+    lib.sgemm_f32_plan_ex.argtypes = [c_int, c_int, c_int] + gemm_args + [c_int, ctypes.POINTER(c_int)]
+    lib.sgemm_f32_plan_ex.restype = c_int
+    lib.sgemm_f32_variant_trans_ok.argtypes = [c_int]
+    lib.sgemm_f32_variant_trans_ok.restype = c_int
     lib.sgemm_f32_num_variants.argtypes = []
     lib.sgemm_f32_num_variants.restype = c_int
     lib.sgemm_f32_variant_name.argtypes = [c_int]
@@ -144,6 +164,34 @@ def sgemm_f32_plan(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus) -> Tup
                              int(ldb), float(beta), _ptr(C), int(ldc), int(num_cus),
                              ctypes.byref(v))
     return int(rc), int(v.value)
+
+
+def sgemm_f32_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                 stream=None) -> int:
+    return int(_lib.sgemm_f32_ex(int(layout), int(transa), int(transb), int(M), int(N), int(K),
+                                 float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb), float(beta),
+                                 _ptr(C), int(ldc), _stream(stream, C, A, B)))
+
+
+def sgemm_f32_variant_ex(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                         ldc, stream=None) -> int:
+    return int(_lib.sgemm_f32_variant_ex(int(variant), int(layout), int(transa), int(transb),
+                                         int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
+                                         _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+                                         _stream(stream, C, A, B)))
+
+
+def sgemm_f32_plan_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      num_cus) -> Tuple[int, int]:
+    v = ctypes.c_int(-2)
+    rc = _lib.sgemm_f32_plan_ex(int(layout), int(transa), int(transb), int(M), int(N), int(K),
+                                float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb), float(beta),
+                                _ptr(C), int(ldc), int(num_cus), ctypes.byref(v))
+    return int(rc), int(v.value)
+
+
+def sgemm_f32_variant_trans_ok(variant: int) -> int:
+    return int(_lib.sgemm_f32_variant_trans_ok(int(variant)))
 
 
 def sgemm_f32_num_variants() -> int:
@@ -215,31 +263,73 @@ def _variant_id(variant) -> Optional[int]:
     return int(variant)
 
 
-def _ld(t, rows: int, cols: int, name: str) -> int:
+def _check_f32(t, rows: int, cols: int, name: str) -> None:
     if str(t.dtype) != "torch.float32":
         raise TypeError(f"{name} must be float32, got {t.dtype}")
     if t.dim() != 2 or tuple(t.shape) != (rows, cols):
         raise ValueError(f"{name} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
-    if cols > 1 and t.stride(1) != 1:
+
+
+def _storage(t, name: str):
+    """(order, ld) of a 2-D tensor: "row" if its column stride is 1 (element
+    (r, c) at r*ld + c), "col" if its row stride is 1 (at c*ld + r). A
+    dimension of extent 1 has no meaningful stride and matches either."""
+    rows, cols = int(t.shape[0]), int(t.shape[1])
+    sr, sc = int(t.stride(0)), int(t.stride(1))
+    if cols <= 1 or sc == 1:
+        ld = sr if rows > 1 else cols
+        if ld >= max(1, cols):
+            return "row", max(1, ld)
+    if rows <= 1 or sr == 1:
+        ld = sc if cols > 1 else rows
+        if ld >= max(1, rows):
+            return "col", max(1, ld)
+    raise ValueError(f"{name} must be row- or column-major with a unit stride, "
+                     f"got strides {tuple(t.stride())}")
+
+
+def _ld(t, rows: int, cols: int, name: str) -> int:
+    _check_f32(t, rows, cols, name)
+    order, ld = _storage(t, name)
+    if order != "row":
         raise ValueError(f"{name} must be row-major with unit column stride")
-    return max(int(t.stride(0)) if rows > 1 else cols, cols, 1)
+    return ld
 
 
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=None, stream=None):
-    """C <- alpha * A @ B + beta * C on row-major float32 CUDA tensors (in place)."""
+    """C <- alpha * A @ B + beta * C on float32 CUDA tensors (in place).
+
+    C's storage order (row- or column-major) sets the layout; A and B each
+    either share it or are stored the other way, which is passed as a
+    transposition (no copy). A contiguous tensor counts as row-major."""
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[1])
-    lda = _ld(A, M, K, "A")
-    ldb = _ld(B, K, N, "B")
-    ldc = _ld(C, M, N, "C")
+    _check_f32(A, M, K, "A")
+    _check_f32(B, K, N, "B")
+    _check_f32(C, M, N, "C")
     for t, n in ((A, "A"), (B, "B"), (C, "C")):
         if not t.is_cuda:
             raise ValueError(f"{n} must be a GPU tensor")
+    oc, ldc = _storage(C, "C")
+    oa, lda = _storage(A, "A")
+    ob, ldb = _storage(B, "B")
+    layout = ROW_MAJOR if oc == "row" else COL_MAJOR
+    ta = NO_TRANS if oa == oc else TRANS
+    tb = NO_TRANS if ob == oc else TRANS
     v = _variant_id(variant)
-    if v is None:
-        rc = sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+    if layout == ROW_MAJOR and ta == NO_TRANS and tb == NO_TRANS:
+        if v is None:
+            rc = sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+        else:
+            rc = sgemm_f32_variant(v, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+        where = "sgemm_f32"
     else:
-        rc = sgemm_f32_variant(v, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+        if v is None:
+            rc = sgemm_f32_ex(layout, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+        else:
+            rc = sgemm_f32_variant_ex(v, layout, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                      ldc, stream)
+        where = "sgemm_f32_ex"
     if rc != 0:
-        raise SgemmError(rc)
+        raise SgemmError(rc, where)
     return C

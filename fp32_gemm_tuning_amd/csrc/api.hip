@@ -21,22 +21,35 @@ static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
 static int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
-// Argument checks in signature order; returns -i for the first bad argument i
-// (M = 1). A and B must be valid only when they are read (M, N, K > 0 and
-// alpha != 0); C only when it is written (M, N > 0).
-static int validate(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
-                    const float* B, int64_t ldb, const float* C, int64_t ldc) {
+// Argument checks in signature order; returns the code of the first bad
+// argument: -13 layout, -14 transa, -15 transb, then -1 M, -2 N, -3 K, -5 A,
+// -6 lda, -7 B, -8 ldb, -10 C, -11 ldc (the positions of these arguments in
+// sgemm_f32, counting M as 1). A and B must be valid only when they are read
+// (M, N, K > 0 and alpha != 0); C only when it is written (M, N > 0). A
+// leading dimension must cover the contiguous extent of its matrix as stored:
+// for row-major storage the column count of the stored matrix (A stored
+// M x K, or K x M when transposed), for column-major storage its row count.
+static int validate(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                    float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                    const float* C, int64_t ldc) {
+    if (layout != SGEMM_F32_ROW_MAJOR && layout != SGEMM_F32_COL_MAJOR) return -13;
+    if (transa != SGEMM_F32_NO_TRANS && transa != SGEMM_F32_TRANS) return -14;
+    if (transb != SGEMM_F32_NO_TRANS && transb != SGEMM_F32_TRANS) return -15;
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
+    const bool col = layout == SGEMM_F32_COL_MAJOR;
+    const int64_t a_contig = col ? (transa ? K : M) : (transa ? M : K);
+    const int64_t b_contig = col ? (transb ? N : K) : (transb ? K : N);
+    const int64_t c_contig = col ? M : N;
     const bool reads_ab = M > 0 && N > 0 && K > 0 && alpha != 0.0f;
     const bool writes_c = M > 0 && N > 0;
     if (reads_ab && (A == nullptr || misaligned4(A))) return -5;
-    if (lda < max1(K)) return -6;
+    if (lda < max1(a_contig)) return -6;
     if (reads_ab && (B == nullptr || misaligned4(B))) return -7;
-    if (ldb < max1(N)) return -8;
+    if (ldb < max1(b_contig)) return -8;
     if (writes_c && (C == nullptr || misaligned4(C))) return -10;
-    if (ldc < max1(N)) return -11;
+    if (ldc < max1(c_contig)) return -11;
     return 0;
 }
 
@@ -113,22 +126,28 @@ static double eff_at(const Candidate& c, int64_t n) {
     return n <= 1 ? c.eff[0] : n == 2 ? c.eff[1] : n <= 4 ? c.eff[2] : c.eff[3];
 }
 
-static int choose(int64_t M, int64_t N, int64_t K, int num_cus) {
+// `trans`: an operand is stored transposed (after the column-major swap);
+// only the kernels that read transposed operands are then candidates, and
+// the first of the built-in ones if the model holds none of them.
+static int choose(int64_t M, int64_t N, int64_t K, int num_cus, bool trans) {
     if (num_cus < 1) num_cus = 1;
-    if (M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
-    if ((double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
+    if (!trans && M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
+    if (!trans && (double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
     const Model* m = g_model.load(std::memory_order_acquire);
-    int best = -1;
+    int best = trans ? SGEMM_F32_MFMA_128 : -1;
     double best_us = 0.0;
+    bool found = false;
     for (int i = 0; i < m->n; ++i) {
         const Candidate& c = m->c[i];
+        if (trans && !kTable[c.variant]->trans_ok) continue;
         const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
         const int64_t n = cdiv(tiles, num_cus);
         const double us = c.overhead_us +
                           1e6 * (double)n * 2.0 * c.bm * c.bn * (double)K / (kPeakPerCu * eff_at(c, n));
-        if (best < 0 || us < best_us) {
+        if (!found || us < best_us) {
             best = c.variant;
             best_us = us;
+            found = true;
         }
     }
     return best;
@@ -169,33 +188,55 @@ int xcd_remap_enabled() {
     return cur;
 }
 
-static Args make_args(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
-                      const float* B, int64_t ldb, float beta, float* C, int64_t ldc) {
+// The row-major problem the kernels solve. A column-major call is the same
+// product transposed: C^T = op(B)^T op(A)^T, where the column-major storage of
+// each matrix is the row-major storage of its transpose. So the operands and
+// M, N swap places, and so do the transposition flags. ("100 Days of GPU",
+// Day 44, "Five paths, one table": the column-major library call with
+// swapped operands yields the row-major product in place; this is the same
+// identity used the other way round.)
+static Args make_args(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                      float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                      float beta, float* C, int64_t ldc) {
+    const bool col = layout == SGEMM_F32_COL_MAJOR;
     Args a;
-    a.A = A;
-    a.B = B;
+    a.A = col ? B : A;
+    a.B = col ? A : B;
     a.C = C;
-    a.lda = lda;
-    a.ldb = ldb;
+    a.lda = col ? ldb : lda;
+    a.ldb = col ? lda : ldb;
     a.ldc = ldc;
-    a.M = (int32_t)M;
-    a.N = (int32_t)N;
+    a.M = (int32_t)(col ? N : M);
+    a.N = (int32_t)(col ? M : N);
     a.K = (int32_t)K;
     a.alpha = alpha;
     a.beta = beta;
+    a.ta = col ? transb : transa;
+    a.tb = col ? transa : transb;
     return a;
 }
 
-static int run(int forced, int64_t M, int64_t N, int64_t K, float alpha, const float* A,
-               int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
-               void* stream) {
+// The variant the automatic choice launches for a (valid, non-quick-return)
+// row-major problem. Shapes beyond a kernel's 32-bit buffer offsets fall back
+// to the plain-pointer register-tiled rung, which reads untransposed
+// operands only; a transposed call keeps its choice and fails its check.
+static int plan_args(const Args& a, int num_cus) {
+    const bool trans = a.ta || a.tb;
+    int v = choose(a.M, a.N, a.K, num_cus, trans);
+    if (!trans && kTable[v]->check(a) != 0) v = SGEMM_F32_REG_2D;
+    return v;
+}
+
+static int run(int forced, int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+               float alpha, const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+               float* C, int64_t ldc, void* stream) {
     if (forced >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
-    int rc = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    int rc = validate(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc) return rc;
     if (M == 0 || N == 0) return 0;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const Args a = make_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     if (K == 0 || alpha == 0.0f) {
         const hipError_t e = launch_scale(a, s);
         return e == hipSuccess ? 0 : (int)e;
@@ -205,16 +246,31 @@ static int run(int forced, int64_t M, int64_t N, int64_t K, float alpha, const f
         int cus = 0;
         rc = device_cus(&cus);
         if (rc) return rc;
-        v = choose(M, N, K, cus);
-        // Shapes beyond a kernel's 32-bit buffer offsets fall back to the
-        // plain-pointer register-tiled rung.
-        if (kTable[v]->check(a) != 0) v = SGEMM_F32_REG_2D;
+        v = plan_args(a, cus);
     }
     const Variant& var = *kTable[v];
+    if ((a.ta || a.tb) && !var.trans_ok) return SGEMM_F32_ERR_UNSUPPORTED;
     rc = var.check(a);
     if (rc) return rc;
     const hipError_t e = var.launch(a, s);
     return e == hipSuccess ? 0 : (int)e;
+}
+
+static int plan(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb, float beta, const float* C,
+                int64_t ldc, int num_cus, int* variant) {
+    int rc = validate(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc) return rc;
+    if (variant == nullptr) return -12;
+    if (M == 0 || N == 0 || K == 0 || alpha == 0.0f) {
+        *variant = -1;
+        return 0;
+    }
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
+    const Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta,
+                             const_cast<float*>(C), ldc);
+    *variant = plan_args(a, num_cus);
+    return 0;
 }
 
 }  // namespace sgemm
@@ -226,33 +282,51 @@ extern "C" {
 SGEMM_F32_API int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
                             int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                             int64_t ldc, void* stream) {
-    return run(-1, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run(-1, SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS, SGEMM_F32_NO_TRANS, M, N, K, alpha, A,
+               lda, B, ldb, beta, C, ldc, stream);
 }
 
 SGEMM_F32_API int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, float alpha,
                                     const float* A, int64_t lda, const float* B, int64_t ldb,
                                     float beta, float* C, int64_t ldc, void* stream) {
     if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
-    return run(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run(variant, SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS, SGEMM_F32_NO_TRANS, M, N, K, alpha,
+               A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
                                  int64_t lda, const float* B, int64_t ldb, float beta,
                                  const float* C, int64_t ldc, int num_cus, int* variant) {
-    (void)beta;
-    int rc = validate(M, N, K, alpha, A, lda, B, ldb, C, ldc);
-    if (rc) return rc;
-    if (variant == nullptr) return -12;
-    if (M == 0 || N == 0 || K == 0 || alpha == 0.0f) {
-        *variant = -1;
-        return 0;
-    }
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
-    const Args a = make_args(M, N, K, alpha, A, lda, B, ldb, beta, const_cast<float*>(C), ldc);
-    int v = choose(M, N, K, num_cus);
-    if (kTable[v]->check(a) != 0) v = SGEMM_F32_REG_2D;
-    *variant = v;
-    return 0;
+    return plan(SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS, SGEMM_F32_NO_TRANS, M, N, K, alpha, A, lda,
+                B, ldb, beta, C, ldc, num_cus, variant);
+}
+
+SGEMM_F32_API int sgemm_f32_ex(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float* A, int64_t lda, const float* B,
+                               int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    return run(-1, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+SGEMM_F32_API int sgemm_f32_variant_ex(int variant, int layout, int transa, int transb, int64_t M,
+                                       int64_t N, int64_t K, float alpha, const float* A,
+                                       int64_t lda, const float* B, int64_t ldb, float beta,
+                                       float* C, int64_t ldc, void* stream) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    return run(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+               stream);
+}
+
+SGEMM_F32_API int sgemm_f32_plan_ex(int layout, int transa, int transb, int64_t M, int64_t N,
+                                    int64_t K, float alpha, const float* A, int64_t lda,
+                                    const float* B, int64_t ldb, float beta, const float* C,
+                                    int64_t ldc, int num_cus, int* variant) {
+    return plan(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus,
+                variant);
+}
+
+SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    return kTable[variant]->trans_ok ? 1 : 0;
 }
 
 SGEMM_F32_API int sgemm_f32_num_variants(void) { return SGEMM_F32_NUM_VARIANTS; }
@@ -276,14 +350,20 @@ SGEMM_F32_API const char* sgemm_f32_strerror(int code) {
         case -2: return "argument 2 (N) is negative";
         case -3: return "argument 3 (K) is negative";
         case -5: return "argument 5 (A) is NULL or not 4-byte aligned";
-        case -6: return "argument 6 (lda) is smaller than max(1, K)";
+        case -6: return "argument 6 (lda) is smaller than the contiguous extent of A as stored "
+                        "(max(1, K) for row-major, untransposed A)";
         case -7: return "argument 7 (B) is NULL or not 4-byte aligned";
-        case -8: return "argument 8 (ldb) is smaller than max(1, N)";
+        case -8: return "argument 8 (ldb) is smaller than the contiguous extent of B as stored "
+                        "(max(1, N) for row-major, untransposed B)";
         case -10: return "argument 10 (C) is NULL or not 4-byte aligned";
-        case -11: return "argument 11 (ldc) is smaller than max(1, N)";
+        case -11: return "argument 11 (ldc) is smaller than the contiguous extent of C "
+                         "(max(1, N) row-major, max(1, M) column-major)";
         case -12: return "output pointer is NULL";
+        case -13: return "layout is neither SGEMM_F32_ROW_MAJOR nor SGEMM_F32_COL_MAJOR";
+        case -14: return "transa is neither SGEMM_F32_NO_TRANS nor SGEMM_F32_TRANS";
+        case -15: return "transb is neither SGEMM_F32_NO_TRANS nor SGEMM_F32_TRANS";
         case SGEMM_F32_ERR_VARIANT: return "variant id out of range";
-        case SGEMM_F32_ERR_UNSUPPORTED: return "variant cannot run this shape or alignment";
+        case SGEMM_F32_ERR_UNSUPPORTED: return "variant cannot run this shape, alignment or transposition";
         case SGEMM_F32_ERR_TOO_LARGE: return "a size exceeds what the kernel can index";
         case SGEMM_F32_ERR_DEVICE: return "no usable HIP device";
         default: break;

@@ -9,7 +9,8 @@
 namespace sgemm {
 
 // One GEMM problem, passed by value as the kernel argument block.
-// Row-major: A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j].
+// Row-major: A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j]
+// (untransposed operands).
 struct Args {
     const float* A;
     const float* B;
@@ -17,6 +18,10 @@ struct Args {
     int64_t lda, ldb, ldc;
     int32_t M, N, K;
     float alpha, beta;
+    // Transposed operands (only kernels whose variant sets trans_ok read
+    // these): ta -> A is stored K x M, A(i,k) = A[k*lda + i]; tb -> B is
+    // stored N x K, B(k,j) = B[j*ldb + k].
+    int32_t ta, tb;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -19,6 +19,7 @@ struct Variant {
     launch_fn launch;
     const void* kernel;  // main kernel, for hipFuncGetAttributes / occupancy
     int threads;         // workgroup size of the main kernel
+    bool trans_ok;       // accepts transposed operands (Args::ta, Args::tb)
 };
 
 // C = beta*C (K == 0 or alpha == 0), C read only when beta != 0.

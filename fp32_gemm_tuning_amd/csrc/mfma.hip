@@ -27,6 +27,8 @@
 // get an out-of-range offset and read as zero, so partial tiles need no
 // branches in the K loop; only the final stores are guarded.
 #include "kernels.hpp"
+
+#include <type_traits>
 #include "sgemm_f32.h"
 
 namespace sgemm {
@@ -218,6 +220,76 @@ struct TileFillDma {
     }
 };
 
+// One wave's share of a BK-deep slice held in LDS, multiplied in 16-deep
+// sub-steps with v_mfma_f32_32x32x2_f32: in sub-step u, lanes 0-31 (h = 0)
+// take k = 16u + s and lanes 32-63 take k = 16u + 8 + s at MFMA step
+// s = 0..7, so each lane needs 8 consecutive k of its row (of A) and of its
+// column (of B). A k-contiguous stage ([row][k] with the XOR chunk swizzle:
+// A, or B stored transposed) yields them in two 16-byte reads at chunks
+// 4u + 2h and 4u + 2h + 1; a row-contiguous one ([k][row]: B, or A stored
+// transposed) in 8 4-byte reads down rows 16u + 8h .. 16u + 8h + 7. The
+// offsets are in floats from the stage base plus abase / bbase.
+template <int BM, int BN, int WM, int WN, int BK, bool TA, bool TB>
+struct SubstepMma {
+    static constexpr int STEPS = BK / 16, BI = WM / 32, BJ = WN / 32;
+    int aoff[STEPS][BI][2], boff[STEPS][BJ][2];
+
+    __device__ __forceinline__ SubstepMma(int wm, int wn, int h, int c, int abase, int bbase) {
+#pragma unroll
+        for (int u = 0; u < STEPS; ++u) {
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi) {
+                const int row = wm * WM + bi * 32 + c;
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+                    aoff[u][bi][v] = TA ? abase + (16 * u + 8 * h) * BM + row
+                                        : abase + row * BK + (((4 * u + 2 * h + v) ^ swz_chunk<BK>(row)) << 2);
+            }
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj) {
+                const int col = wn * WN + bj * 32 + c;
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+                    boff[u][bj][v] = TB ? bbase + col * BK + (((4 * u + 2 * h + v) ^ swz_chunk<BK>(col)) << 2)
+                                        : bbase + (16 * u + 8 * h) * BN + col;
+            }
+        }
+    }
+
+    template <bool KCONTIG, int PITCH>
+    static __device__ __forceinline__ void frag8(const float* X, const int (&off)[2], float (&f)[8]) {
+        if (KCONTIG) {
+            const f32x4 lo = *(const f32x4*)&X[off[0]];
+            const f32x4 hi = *(const f32x4*)&X[off[1]];
+            f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+            f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = X[off[0] + k * PITCH];
+        }
+    }
+
+    __device__ __forceinline__ void operator()(const float* Ac, const float* Bc,
+                                               f32x16 (&acc)[BI][BJ]) const {
+#pragma unroll
+        for (int u = 0; u < STEPS; ++u) {
+            float af[BI][8], bf[BJ][8];
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi) frag8<!TA, BM>(Ac, aoff[u][bi], af[bi]);
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj) frag8<TB, BN>(Bc, boff[u][bj], bf[bj]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                           acc[bi][bj], 0, 0, 0);
+        }
+    }
+};
+
 // ===========================================================================
 // Tiled FP32 MFMA kernel, generic over the block tile BM x BN and the wave
 // tile WM x WN (each wave owns WM/32 x WN/32 blocks of 32x32 accumulated
@@ -253,14 +325,15 @@ struct TileFillDma {
 constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
 constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
 
-template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC>
+template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC, bool TA = false,
+          bool TB = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int BI = WM / 32, BJ = WN / 32;
-    using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC, TA, TB>;
     constexpr int BNP = Dma::BNP;
     constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
     // One LDS object per stage, so that the compiler can tell the stage being
@@ -287,48 +360,8 @@ void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // LDS read offsets of this lane's fragments (floats). In sub-step u the
-    // wave covers k = 16u .. 16u+15 of the slice: lanes 0-31 (h = 0) take
-    // k = 16u + s and lanes 32-63 take 16u + 8 + s at MFMA step s = 0..7.
-    int aoff[STEPS][BI][2], boff[STEPS][BJ];
-#pragma unroll
-    for (int u = 0; u < STEPS; ++u) {
-#pragma unroll
-        for (int bi = 0; bi < BI; ++bi) {
-            const int row = wm * WM + bi * 32 + c;
-#pragma unroll
-            for (int v = 0; v < 2; ++v)
-                aoff[u][bi][v] = row * BK + (((4 * u + 2 * h + v) ^ swz_chunk<BK>(row)) << 2);
-        }
-#pragma unroll
-        for (int bj = 0; bj < BJ; ++bj) boff[u][bj] = (16 * u + 8 * h) * BNP + wn * WN + bj * 32 + c;
-    }
-
-    auto compute = [&](const float* Ac, const float* Bc) {
-#pragma unroll
-        for (int u = 0; u < STEPS; ++u) {
-            float af[BI][8], bf[BJ][8];
-#pragma unroll
-            for (int bi = 0; bi < BI; ++bi) {
-                const f32x4 lo = *(const f32x4*)&Ac[aoff[u][bi][0]];
-                const f32x4 hi = *(const f32x4*)&Ac[aoff[u][bi][1]];
-                af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
-                af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
-            }
-#pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[u][bj] + k * BNP];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-#pragma unroll
-                for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < BJ; ++bj)
-                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
-                                                                           acc[bi][bj], 0, 0, 0);
-        }
-    };
+    const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, 0, 0);
+    auto compute = [&](const float* Ac, const float* Bc) { mma(Ac, Bc, acc); };
 
     // One pipelined step: start filling slice s+1 into the other stage with
     // buffer-to-LDS loads, multiply slice s from this stage, barrier (which
@@ -401,7 +434,8 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
+          bool TA = false, bool TB = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
@@ -410,7 +444,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int BI = WM / 32, BJ = WN / 32;
-    using Dma = TileFillDma<BM, BN, BK, NT, VEC>;
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC, TA, TB>;
     constexpr int BNP = Dma::BNP, APITCH = BK;
     // Deeper rings count outstanding loads, which must then be the same on
     // every wave; with two stages the barrier waits for all of them.
@@ -460,28 +494,48 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 
     // Lanes 0-31 take k = s and lanes 32-63 take k = BK/2 + s at MFMA step s
     // of the slice; part v covers steps 4v .. 4v+3, i.e. 16-byte chunk
-    // P*h + v of the lane's A row and B rows BK/2*h + 4v .. BK/2*h + 4v + 3.
-    // A fragment address of part v: arow + ((achunk ^ v) << 2), computed per
-    // read (one XOR and one shift-or, hidden under the MFMAs) rather than
-    // held in P registers per row block.
-    int arow[BI], achunk[BI], boff[BJ];
+    // P*h + v of a k-contiguous row ([row][k], swizzled: A, or B stored
+    // transposed) and rows BK/2*h + 4v .. BK/2*h + 4v + 3 of a row-contiguous
+    // stage ([k][row]: B, or A stored transposed). A chunk address of part v
+    // is xrow + ((xchunk ^ v) << 2), computed per read (one XOR and one
+    // shift-or, hidden under the MFMAs) rather than held in P registers per
+    // block.
+    int arow[BI], achunk[BI], brow[BJ], bchunk[BJ];
 #pragma unroll
     for (int bi = 0; bi < BI; ++bi) {
         const int row = wm * WM + bi * 32 + c;
-        arow[bi] = row * APITCH;
+        arow[bi] = TA ? (BK / 2) * h * BM + row : row * APITCH;
         achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
     }
 #pragma unroll
-    for (int bj = 0; bj < BJ; ++bj) boff[bj] = (BK / 2) * h * BNP + wn * WN + bj * 32 + c;
+    for (int bj = 0; bj < BJ; ++bj) {
+        const int col = wn * WN + bj * 32 + c;
+        brow[bj] = TB ? col * BK : (BK / 2) * h * BNP + col;
+        bchunk[bj] = (P * h) ^ swz_chunk<BK>(col);
+    }
 
     auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
 #pragma unroll
-        for (int bi = 0; bi < BI; ++bi)
-            f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
+        for (int bi = 0; bi < BI; ++bi) {
+            if constexpr (TA) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+                for (int k = 0; k < 4; ++k) f.a[bi][k] = Ac[arow[bi] + (4 * v + k) * BM];
+            } else {
+                f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
+            }
+        }
+        if constexpr (TB) {
 #pragma unroll
-            for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[boff[bj] + (4 * v + k) * BNP];
+            for (int bj = 0; bj < BJ; ++bj) {
+                const f32x4 q = *(const f32x4*)&Bc[brow[bj] + ((bchunk[bj] ^ v) << 2)];
+                f.b[bj][0] = q.x; f.b[bj][1] = q.y; f.b[bj][2] = q.z; f.b[bj][3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[brow[bj] + (4 * v + k) * BNP];
+        }
     };
     auto mma_part = [&](const PartFrag<BI, BJ>& f, int k_begin = 0, int k_end = 4) {
 #pragma unroll
@@ -585,7 +639,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 // the result does not depend on timing. One workgroup per compute unit
 // (96 KB of LDS).
 // ===========================================================================
-template <int BM, int BN, int WM, int WN, int BK, bool VEC>
+template <int BM, int BN, int WM, int WN, int BK, bool VEC, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(4 * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN), (BM / WM) * (BN / WN))))
 void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
@@ -595,7 +649,7 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int WAVES_N = BN / WN;
     constexpr int BI = WM / 32, BJ = WN / 32;
     constexpr int PER_LANE = BI * BJ * 16;  // accumulators per lane
-    using Dma = TileFillDma<BM, BN, BK, GT, VEC>;
+    using Dma = TileFillDma<BM, BN, BK, GT, VEC, TA, TB>;
     constexpr int BNP = Dma::BNP;
     // Stage objects, one per stage (so that the fill of one stage is never
     // taken for a write to the stage being read), each holding all groups.
@@ -624,50 +678,10 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Fragment offsets as in k_mfma_tile (in sub-step u, lanes 0-31 take
-    // k = 16u + s and lanes 32-63 k = 16u + 8 + s at MFMA step s), within
-    // this group's part of a stage.
-    int aoff[STEPS][BI][2], boff[STEPS][BJ];
-#pragma unroll
-    for (int u = 0; u < STEPS; ++u) {
-#pragma unroll
-        for (int bi = 0; bi < BI; ++bi) {
-            const int row = wm * WM + bi * 32 + c;
-#pragma unroll
-            for (int v = 0; v < 2; ++v)
-                aoff[u][bi][v] = g * BM * BK + row * BK +
-                                 (((4 * u + 2 * h + v) ^ swz_chunk<BK>(row)) << 2);
-        }
-#pragma unroll
-        for (int bj = 0; bj < BJ; ++bj)
-            boff[u][bj] = g * BK * BNP + (16 * u + 8 * h) * BNP + wn * WN + bj * 32 + c;
-    }
-
-    auto compute = [&](const float* Ac, const float* Bc) {
-#pragma unroll
-        for (int u = 0; u < STEPS; ++u) {
-            float af[BI][8], bf[BJ][8];
-#pragma unroll
-            for (int bi = 0; bi < BI; ++bi) {
-                const f32x4 lo = *(const f32x4*)&Ac[aoff[u][bi][0]];
-                const f32x4 hi = *(const f32x4*)&Ac[aoff[u][bi][1]];
-                af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
-                af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
-            }
-#pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[u][bj] + k * BNP];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-#pragma unroll
-                for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-                    for (int bj = 0; bj < BJ; ++bj)
-                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
-                                                                           acc[bi][bj], 0, 0, 0);
-        }
-    };
+    // This group's part of a stage starts at g * BM * BK (A) and
+    // g * BK * BNP (B).
+    const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, g * BM * BK, g * BK * BNP);
+    auto compute = [&](const float* Ac, const float* Bc) { mma(Ac, Bc, acc); };
 
     // Step i: group g multiplies slice i*KG + g from the current stage while
     // its loads of slice (i+1)*KG + g fill the other one; one workgroup
@@ -763,16 +777,32 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 }
 
 // Host-side limits shared by the tiled MFMA kernels: per-slice buffer extents
-// must stay below 2^31 bytes.
+// must stay below 2^31 bytes. A slice of A spans BM rows of BK (BK rows of
+// BM when A is stored transposed); one of B spans BK rows of BN (BN rows of
+// BK when transposed).
 static bool extents_ok(const Args& a, int BM, int BN, int BK) {
-    const int64_t ea = ((int64_t)(BM - 1) * a.lda + BK) * 4;
-    const int64_t eb = ((int64_t)(BK - 1) * a.ldb + BN) * 4;
+    const int64_t ea = a.ta ? ((int64_t)(BK - 1) * a.lda + BM) * 4 : ((int64_t)(BM - 1) * a.lda + BK) * 4;
+    const int64_t eb = a.tb ? ((int64_t)(BN - 1) * a.ldb + BK) * 4 : ((int64_t)(BK - 1) * a.ldb + BN) * 4;
     return ea < (int64_t)OOB && eb < (int64_t)OOB;
 }
 
+// 16-byte fills need the contiguous extent of each operand (K of A, N of B;
+// M of a transposed A, K of a transposed B), both leading dimensions and
+// both base addresses in whole 16-byte chunks.
 static bool vec_ok(const Args& a) {
-    return !((a.K & 3) || (a.N & 3) || (a.lda & 3) || (a.ldb & 3) || !aligned16(a.A) ||
+    const int ca = a.ta ? a.M : a.K, cb = a.tb ? a.K : a.N;
+    return !((ca & 3) || (cb & 3) || (a.lda & 3) || (a.ldb & 3) || !aligned16(a.A) ||
              !aligned16(a.B));
+}
+
+// Calls f(std::integral_constant<bool, ta>, std::integral_constant<bool, tb>)
+// with the call's transposition flags as compile-time constants.
+template <class F>
+static hipError_t with_trans(const Args& a, F&& f) {
+    using T = std::true_type;
+    using N = std::false_type;
+    if (a.ta) return a.tb ? f(T{}, T{}) : f(T{}, N{});
+    return a.tb ? f(N{}, T{}) : f(N{}, N{});
 }
 
 // Launch helpers for instances of k_mfma_tile. The 4-byte-fill instance keeps
@@ -794,13 +824,18 @@ struct TileInstance {
     static hipError_t launch(const Args& a, hipStream_t s) {
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
-        if (vec_ok(a))
-            hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU, true>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-        else
-            hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, 3, false>), grid, block, 0, s,
-                               a, tm, tn, xcd_remap_enabled());
-        return hipGetLastError();
+        const bool vec = vec_ok(a);
+        return with_trans(a, [&](auto ta, auto tb) {
+            constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+            if (vec)
+                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU, true,
+                                                TA, TB>),
+                                   grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+            else
+                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, 3, false, TA, TB>), grid,
+                                   block, 0, s, a, tm, tn, xcd_remap_enabled());
+            return hipGetLastError();
+        });
     }
 };
 
@@ -815,12 +850,12 @@ static hipError_t launch_mfma64x128(const Args& a, hipStream_t s) {
 }
 
 Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
-                    Tile128::kernel<true>(), Tile128::NT};
+                    Tile128::kernel<true>(), Tile128::NT, true};
 // 64x128 tile, 4 waves of 32x64: twice the tiles of mfma_128x128 for
 // medium shapes (e.g. 2048^3, where 256 tiles of 128x128 leave one
 // workgroup per compute unit).
 Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
-                       Tile64x128::kernel<true>(), Tile64x128::NT};
+                       Tile64x128::kernel<true>(), Tile64x128::NT, true};
 
 // mfma_256x256: the pipelined kernel with a 256x256 block tile, 16 waves of
 // 64x64 (four per SIMD, all of one workgroup), one workgroup per compute
@@ -870,22 +905,27 @@ static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
     const int tm = (int)cdiv(a.M, M256_BM), tn = (int)cdiv(a.N, M256_BN);
     const dim3 grid((unsigned)((int64_t)tm * tn)), block(M256_NT);
     const bool full = a.M % M256_BM == 0 && a.N % M256_BN == 0 && a.K % M256_BK == 0;
-    if (vec_ok(a) && full)
-        hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, true>),
-                           grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    else if (vec_ok(a))
-        hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false>),
-                           grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    else
-        hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                        SGEMM_M256_STAGES, SGEMM_M256_WPE, false, false>),
-                           grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    return hipGetLastError();
+    const bool vec = vec_ok(a);
+    return with_trans(a, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (vec && full)
+            hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                            SGEMM_M256_STAGES, SGEMM_M256_WPE, true, true, TA, TB>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+        else if (vec)
+            hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                            SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false, TA, TB>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+        else
+            hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                            SGEMM_M256_STAGES, SGEMM_M256_WPE, false, false, TA, TB>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+        return hipGetLastError();
+    });
 }
 
-Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT};
+Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT,
+                    true};
 
 template <int BM, int BN, int WM, int WN, int BK = 16>
 struct KgroupInstance {
@@ -898,33 +938,39 @@ struct KgroupInstance {
     static hipError_t launch(const Args& a, hipStream_t s) {
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
-        if (vec_ok(a))
-            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, true>), grid, block, 0, s, a, tm, tn,
-                               xcd_remap_enabled());
-        else
-            hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, false>), grid, block, 0, s, a, tm, tn,
-                               xcd_remap_enabled());
-        return hipGetLastError();
+        const bool vec = vec_ok(a);
+        return with_trans(a, [&](auto ta, auto tb) {
+            constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+            if (vec)
+                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, true, TA, TB>), grid, block, 0, s,
+                                   a, tm, tn, xcd_remap_enabled());
+            else
+                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, false, TA, TB>), grid, block, 0,
+                                   s, a, tm, tn, xcd_remap_enabled());
+            return hipGetLastError();
+        });
     }
     static const void* kernel() { return (const void*)k_mfma_kgroup<BM, BN, WM, WN, BK, true>; }
 };
 
 // 64x128 tile, 4 groups of 4 waves of 32x64 (16 waves, 96 KB LDS).
 using Kg128 = KgroupInstance<64, 128, 32, 64>;
-Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::kernel(), Kg128::NT};
+Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::kernel(), Kg128::NT,
+                       true};
 // 64x96 tile, 4 groups of 3 waves of 64x32 (12 waves, 80 KB LDS): the odd
 // 1000x1531 output is exactly 256 such tiles.
 #ifndef SGEMM_KG96_BK
 #define SGEMM_KG96_BK 16
 #endif
 using Kg96 = KgroupInstance<64, 96, 64, 32, SGEMM_KG96_BK>;
-Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT};
+Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT,
+                         true};
 // 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
 // tile per compute unit for medium shapes such as 2048^3 (256 tiles), where
 // mfma_128x128 would leave one wave per SIMD.
 using Kg128x128 = KgroupInstance<128, 128, 64, 64>;
 Variant kMfmaKgroup128 = {"mfma_128x128_kg4", Kg128x128::check, Kg128x128::launch,
-                          Kg128x128::kernel(), Kg128x128::NT};
+                          Kg128x128::kernel(), Kg128x128::NT, true};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2

@@ -37,7 +37,10 @@
  *                           6 lda too small, 7 B null or misaligned, 8 ldb too
  *                           small, 10 C null or misaligned, 11 ldc too small.
  *                           (A, B, C are only required when they are read or
- *                           written.) sgemm_f32_variant uses the same numbers.
+ *                           written.) sgemm_f32_variant uses the same numbers,
+ *                           and so do the _ex entry points for these arguments
+ *                           (named by meaning, not position), plus
+ *                           -13 layout, -14 transa, -15 transb.
  *    SGEMM_F32_ERR_VARIANT      variant id out of range
  *    SGEMM_F32_ERR_UNSUPPORTED  the forced variant cannot run this shape or
  *                               alignment (e.g. a 16-byte-load rung with a
@@ -130,6 +133,17 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_NUM_VARIANTS = 17
 };
 
+/* Storage order and operand transposition of the _ex entry points (the
+ * BLAS sgemm surface). */
+enum sgemm_f32_layout {
+    SGEMM_F32_ROW_MAJOR = 0, /* element (r, c) at base[r * ld + c] */
+    SGEMM_F32_COL_MAJOR = 1  /* element (r, c) at base[c * ld + r] */
+};
+enum sgemm_f32_trans {
+    SGEMM_F32_NO_TRANS = 0, /* op(X) = X */
+    SGEMM_F32_TRANS = 1     /* op(X) = X^T */
+};
+
 /* C = alpha*A*B + beta*C, kernel chosen automatically (see sgemm_f32_plan). */
 SGEMM_F32_API int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A,
                             int64_t lda, const float *B, int64_t ldb, float beta, float *C,
@@ -150,6 +164,53 @@ SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, c
                                  int64_t lda, const float *B, int64_t ldb, float beta,
                                  const float *C, int64_t ldc, int num_cus, int *variant);
 
+/* C = alpha * op(A) * op(B) + beta * C with op(A) M x K, op(B) K x N and C
+ * M x N, all three stored in `layout` order (SGEMM_F32_ROW_MAJOR or
+ * SGEMM_F32_COL_MAJOR); transa / transb are SGEMM_F32_NO_TRANS or
+ * SGEMM_F32_TRANS. The stored matrices are A: M x K (K x M if transa),
+ * B: K x N (N x K if transb), C: M x N, and each leading dimension must be at
+ * least max(1, the stored matrix's column count) for row-major storage, its
+ * row count for column-major storage (CBLAS conventions). Everything else --
+ * ownership, alignment, quick returns, beta == 0, asynchrony, return codes --
+ * is as for sgemm_f32; sgemm_f32_ex(SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS,
+ * SGEMM_F32_NO_TRANS, ...) is sgemm_f32.
+ *
+ * A column-major call is the row-major product of the transposes,
+ * C^T = op(B)^T op(A)^T, with the operands and M, N swapped: column-major
+ * storage of a matrix is row-major storage of its transpose. This is the
+ * operand swap the pages use to get a row-major product out of a
+ * column-major library ("100 Days of GPU", Day 44, "Five paths, one table",
+ * the library call the page scores against), here applied in the other
+ * direction. So a column-major call with both operands
+ * untransposed runs the same kernels as a row-major one, at the same speed.
+ * After the swap an operand may be stored transposed (A as K x M or B as
+ * N x K, row-major); the matrix-core tile kernels read such operands
+ * directly (the buffer-to-LDS fill stores them in the LDS layout the
+ * fragment reads need; see sgemm_f32_variant_trans_ok), and the automatic
+ * choice then takes one of them. */
+SGEMM_F32_API int sgemm_f32_ex(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float *A, int64_t lda, const float *B,
+                               int64_t ldb, float beta, float *C, int64_t ldc, void *stream);
+
+/* sgemm_f32_ex with the kernel forced to `variant`. A variant that cannot
+ * read a transposed operand (sgemm_f32_variant_trans_ok == 0) returns
+ * SGEMM_F32_ERR_UNSUPPORTED when one remains after the column-major swap. */
+SGEMM_F32_API int sgemm_f32_variant_ex(int variant, int layout, int transa, int transb, int64_t M,
+                                       int64_t N, int64_t K, float alpha, const float *A,
+                                       int64_t lda, const float *B, int64_t ldb, float beta,
+                                       float *C, int64_t ldc, void *stream);
+
+/* The variant sgemm_f32_ex would launch, as sgemm_f32_plan (host-only). */
+SGEMM_F32_API int sgemm_f32_plan_ex(int layout, int transa, int transb, int64_t M, int64_t N,
+                                    int64_t K, float alpha, const float *A, int64_t lda,
+                                    const float *B, int64_t ldb, float beta, const float *C,
+                                    int64_t ldc, int num_cus, int *variant);
+
+/* 1 if `variant` reads transposed operands (mfma_128x128, mfma_256x256,
+ * mfma_64x128 and the three K-group kernels), 0 if not, or
+ * SGEMM_F32_ERR_VARIANT. */
+SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
+
 /* The dispatch model sgemm_f32 uses to choose among the tiled matrix-core
  * kernels (sgemm_f32_plan reports the choice). It follows the pages' kernel
  * selection by the busiest SM's work ("Optimizing Matrix Multiply on CUDA,
@@ -160,7 +221,10 @@ SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, c
  * n = ceil(ceil(M/BM) * ceil(N/BN) / C), b = 0, 1, 2, 3 for n = 1, 2, 3-4, >= 5
  * (614.4e9 FLOP/s is one compute unit's FP32 matrix peak). The smallest
  * prediction wins; ties go to the earlier entry. M <= 32 and tiny products
- * bypass the model (mfma_skinny, mfma_direct). */
+ * bypass the model (mfma_skinny, mfma_direct). A call with a transposed
+ * operand (after the column-major swap) uses the model for every shape,
+ * restricted to the entries that read transposed operands (mfma_128x128 if
+ * there are none). */
 #define SGEMM_F32_MODEL_MAX 16
 typedef struct {
     int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,
