@@ -17,6 +17,7 @@ Extra objects on that line:
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload S4096]
                   [--variant auto|mfma_128x128|...] [--no-cpu-baseline]
+  python bench.py --sweep [--workloads ...] [--variants all|none|a,b] [--context] [--layouts]
 """
 from __future__ import annotations
 
@@ -203,8 +204,44 @@ def sweep(args, dev) -> int:
                                                      FP32_PEAK_TFLOPS, 2),
                               "hbm_gbs_min_bytes": round(w.bytes_min / (kms * 1e-3) / 1e9, 1)}),
                   flush=True)
+        if args.layouts:
+            layout_sweep(w, dA, dB, dC, args, stream)
         del dA, dB, dC
     return 0
+
+
+def layout_sweep(w, dA, dB, dC, args, stream) -> None:
+    """The automatic choice through sgemm_f32_ex for every storage order and
+    transposition, on buffers of the workload's sizes (each stored operand
+    has the same element count in every orientation; leading dimensions are
+    the smallest allowed)."""
+    import itertools
+
+    import fp32_gemm_tuning_amd as sg
+    sp = stream.cuda_stream
+    M, N, K = w.M, w.N, w.K
+    for layout, ta, tb in itertools.product((sg.ROW_MAJOR, sg.COL_MAJOR), (0, 1), (0, 1)):
+        col = layout == sg.COL_MAJOR
+        lda = (K if ta else M) if col else (M if ta else K)
+        ldb = (N if tb else K) if col else (K if tb else N)
+        ldc = M if col else N
+        a = (layout, ta, tb, M, N, K, w.alpha, dA, lda, dB, ldb, w.beta, dC, ldc)
+        _, vid = sg.sgemm_f32_plan_ex(*a, torch_cus(dA))
+        durs, _ = time_calls(lambda: sg.sgemm_f32_ex(*a, sp), args.steps, args.warmup, stream)
+        kms = float(durs.mean())
+        print(json.dumps({"sweep": True, "workload": w.name,
+                          "layout": ("col" if col else "row") + "-" + "NT"[ta] + "NT"[tb],
+                          "variant": "auto:" + sg.sgemm_f32_variant_name(vid),
+                          "kernel_ms_mean": round(kms, 4),
+                          "kernel_ms_min": round(float(durs.min()), 4),
+                          "gflops": round(w.flops / (kms * 1e-3) / 1e9, 1),
+                          "pct_fp32_peak": round(100 * w.flops / (kms * 1e-3) / 1e12 /
+                                                 FP32_PEAK_TFLOPS, 2)}), flush=True)
+
+
+def torch_cus(t) -> int:
+    import torch
+    return torch.cuda.get_device_properties(t.device).multi_processor_count
 
 
 def smi_snapshot() -> dict:
@@ -347,6 +384,9 @@ def main() -> int:
     ap.add_argument("--context", action="store_true",
                     help="in a sweep, also time torch's FP32 matmul (vendor library, "
                          "TF32 off) as context")
+    ap.add_argument("--layouts", action="store_true",
+                    help="in a sweep, also time the automatic choice through sgemm_f32_ex "
+                         "for row- and column-major storage and every transposition")
     ap.add_argument("--regimes", action="store_true",
                     help="per workload on --workloads: event and back-to-back timing, "
                          "roofline from a measured copy bandwidth, clock/power, oracle "
