@@ -172,20 +172,33 @@ def sweep(args, dev) -> int:
                               "hbm_gbs_min_bytes": round(w.bytes_min / (kms * 1e-3) / 1e9, 1)}),
                   flush=True)
             del C1
-        for vname in ["auto"] + names:
+        # Workspace for the stream-K kernels (and for the automatic choice
+        # with one, "auto_ws").
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        _, wsb = sg.sgemm_f32_ws_size(-1, sg.ROW_MAJOR, 0, 0, w.M, w.N, w.K, cus)
+        ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=dev)
+        for vname in ["auto", "auto_ws"] + names:
             if vname in SLOW_RUNGS and wname not in SLOW_OK:
                 continue
             if vname == "auto":
                 call = lambda: sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta,
                                             dC, w.N, sp)
-                cus = torch.cuda.get_device_properties(dev).multi_processor_count
                 _, vid = sg.sgemm_f32_plan(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta,
                                            dC, w.N, cus)
                 label = "auto:" + sg.sgemm_f32_variant_name(vid)
+            elif vname == "auto_ws":
+                if wsb == 0:
+                    continue
+                call = lambda: sg.sgemm_f32_ws(sg.ROW_MAJOR, 0, 0, w.M, w.N, w.K, w.alpha, dA, w.K,
+                                               dB, w.N, w.beta, dC, w.N, ws, wsb, sp)
+                _, vid = sg.sgemm_f32_plan_ws(sg.ROW_MAJOR, 0, 0, w.M, w.N, w.K, w.alpha, dA, w.K,
+                                              dB, w.N, w.beta, dC, w.N, wsb, cus)
+                label = "auto_ws:" + sg.sgemm_f32_variant_name(vid)
             else:
                 vid = sg.sgemm_f32_variant_by_name(vname)
-                call = (lambda vid=vid: sg.sgemm_f32_variant(vid, w.M, w.N, w.K, w.alpha, dA,
-                                                             w.K, dB, w.N, w.beta, dC, w.N, sp))
+                call = (lambda vid=vid: sg.sgemm_f32_variant_ws(
+                    vid, sg.ROW_MAJOR, 0, 0, w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC,
+                    w.N, ws, wsb, sp))
                 label = vname
             slow = vname in SLOW_RUNGS
             rc = call()
@@ -206,7 +219,7 @@ def sweep(args, dev) -> int:
                   flush=True)
         if args.layouts:
             layout_sweep(w, dA, dB, dC, args, stream)
-        del dA, dB, dC
+        del dA, dB, dC, ws
     return 0
 
 

@@ -17,16 +17,24 @@ or raw device addresses as ints; they return the C status code):
     sgemm_f32_plan_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                       num_cus) -> (code, variant)
     sgemm_f32_variant_trans_ok(variant)
+    sgemm_f32_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                 workspace, workspace_bytes, stream=None)
+    sgemm_f32_variant_ws(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb,
+                         beta, C, ldc, workspace, workspace_bytes, stream=None)
+    sgemm_f32_plan_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      workspace_bytes, num_cus) -> (code, variant)
+    sgemm_f32_ws_size(variant, layout, transa, transb, M, N, K, num_cus) -> (code, bytes)
     sgemm_f32_num_variants(), sgemm_f32_variant_name(v), sgemm_f32_variant_by_name(s),
     sgemm_f32_strerror(code), sgemm_f32_kernel_info(v) -> dict
     sgemm_f32_set_model(entries) -> code, sgemm_f32_get_model() -> list of dicts
 
 Tensor helper:
-    gemm(A, B, C, alpha=1.0, beta=0.0, variant=None, stream=None)
+    gemm(A, B, C, alpha=1.0, beta=0.0, variant=None, stream=None, workspace=None)
         C <- alpha*A@B + beta*C for float32 CUDA tensors; raises SgemmError. A and B
         may be transposed views (A.t() of a row-major K x M tensor, say) and C a
         column-major one: the call then passes the matching layout and
-        transposition flags (no copy).
+        transposition flags (no copy). `workspace` (a CUDA tensor) enables the
+        stream-K kernels (sgemm_f32_ws).
 """
 from __future__ import annotations
 
@@ -42,6 +50,7 @@ ERR_VARIANT = -100
 ERR_UNSUPPORTED = -101
 ERR_TOO_LARGE = -102
 ERR_DEVICE = -103
+ERR_WORKSPACE = -104
 
 ROW_MAJOR, COL_MAJOR = 0, 1
 NO_TRANS, TRANS = 0, 1
@@ -49,7 +58,7 @@ NO_TRANS, TRANS = 0, 1
 VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", "valu_main",
             "mfma_128x128", "mfma_64x64", "mfma_skinny", "mfma_64x64_k4", "mfma_direct",
             "mfma_64x128", "mfma_256x256", "mfma_64x128_kg4",
-            "mfma_64x96_kg4", "mfma_128x128_kg4")
+            "mfma_64x96_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk")
 
 
 class SgemmError(RuntimeError):
@@ -98,6 +107,16 @@ def _load() -> ctypes.CDLL:
     lib.sgemm_f32_variant_ex.restype = c_int
     lib.sgemm_f32_plan_ex.argtypes = [c_int, c_int, c_int] + gemm_args + [c_int, ctypes.POINTER(c_int)]
     lib.sgemm_f32_plan_ex.restype = c_int
+    sz = ctypes.c_size_t
+    lib.sgemm_f32_ws.argtypes = [c_int, c_int, c_int] + gemm_args + [vp, sz, vp]
+    lib.sgemm_f32_ws.restype = c_int
+    lib.sgemm_f32_variant_ws.argtypes = [c_int, c_int, c_int, c_int] + gemm_args + [vp, sz, vp]
+    lib.sgemm_f32_variant_ws.restype = c_int
+    lib.sgemm_f32_plan_ws.argtypes = [c_int, c_int, c_int] + gemm_args + [sz, c_int, ctypes.POINTER(c_int)]
+    lib.sgemm_f32_plan_ws.restype = c_int
+    lib.sgemm_f32_ws_size.argtypes = [c_int, c_int, c_int, c_int, i64, i64, i64, c_int,
+                                      ctypes.POINTER(sz)]
+    lib.sgemm_f32_ws_size.restype = c_int
     lib.sgemm_f32_variant_trans_ok.argtypes = [c_int]
     lib.sgemm_f32_variant_trans_ok.restype = c_int
     lib.sgemm_f32_num_variants.argtypes = []
@@ -188,6 +207,40 @@ def sgemm_f32_plan_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, be
                                 float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb), float(beta),
                                 _ptr(C), int(ldc), int(num_cus), ctypes.byref(v))
     return int(rc), int(v.value)
+
+
+def sgemm_f32_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                 workspace_bytes, stream=None) -> int:
+    return int(_lib.sgemm_f32_ws(int(layout), int(transa), int(transb), int(M), int(N), int(K),
+                                 float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb), float(beta),
+                                 _ptr(C), int(ldc), _ptr(workspace), int(workspace_bytes),
+                                 _stream(stream, C, A, B)))
+
+
+def sgemm_f32_variant_ws(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                         ldc, workspace, workspace_bytes, stream=None) -> int:
+    return int(_lib.sgemm_f32_variant_ws(int(variant), int(layout), int(transa), int(transb),
+                                         int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
+                                         _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+                                         _ptr(workspace), int(workspace_bytes),
+                                         _stream(stream, C, A, B)))
+
+
+def sgemm_f32_plan_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      workspace_bytes, num_cus) -> Tuple[int, int]:
+    v = ctypes.c_int(-2)
+    rc = _lib.sgemm_f32_plan_ws(int(layout), int(transa), int(transb), int(M), int(N), int(K),
+                                float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb), float(beta),
+                                _ptr(C), int(ldc), int(workspace_bytes), int(num_cus),
+                                ctypes.byref(v))
+    return int(rc), int(v.value)
+
+
+def sgemm_f32_ws_size(variant, layout, transa, transb, M, N, K, num_cus) -> Tuple[int, int]:
+    b = ctypes.c_size_t(0)
+    rc = _lib.sgemm_f32_ws_size(int(variant), int(layout), int(transa), int(transb), int(M),
+                                int(N), int(K), int(num_cus), ctypes.byref(b))
+    return int(rc), int(b.value)
 
 
 def sgemm_f32_variant_trans_ok(variant: int) -> int:
@@ -296,12 +349,14 @@ def _ld(t, rows: int, cols: int, name: str) -> int:
     return ld
 
 
-def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=None, stream=None):
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=None, stream=None,
+         workspace=None):
     """C <- alpha * A @ B + beta * C on float32 CUDA tensors (in place).
 
     C's storage order (row- or column-major) sets the layout; A and B each
     either share it or are stored the other way, which is passed as a
-    transposition (no copy). A contiguous tensor counts as row-major."""
+    transposition (no copy). A contiguous tensor counts as row-major.
+    `workspace`: a CUDA tensor whose memory the stream-K kernels may use."""
     M, K = int(A.shape[0]), int(A.shape[1])
     N = int(B.shape[1])
     _check_f32(A, M, K, "A")
@@ -317,6 +372,17 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=None, stream=No
     ta = NO_TRANS if oa == oc else TRANS
     tb = NO_TRANS if ob == oc else TRANS
     v = _variant_id(variant)
+    if workspace is not None:
+        wb = int(workspace.numel() * workspace.element_size())
+        if v is None:
+            rc = sgemm_f32_ws(layout, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                              workspace, wb, stream)
+        else:
+            rc = sgemm_f32_variant_ws(v, layout, ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                      ldc, workspace, wb, stream)
+        if rc != 0:
+            raise SgemmError(rc, "sgemm_f32_ws")
+        return C
     if layout == ROW_MAJOR and ta == NO_TRANS and tb == NO_TRANS:
         if v is None:
             rc = sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <new>
 #include <cstdlib>
 #include <cstring>
@@ -15,10 +16,11 @@ namespace sgemm {
 static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
     &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
-    &kMfma256, &kMfmaKgroup, &kMfmaKgroup96, &kMfmaKgroup128,
+    &kMfma256, &kMfmaKgroup, &kMfmaKgroup96, &kMfmaKgroup128, &kMfma128Sk, &kMfma64x128Sk,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+static bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 static int64_t max1(int64_t v) { return v > 1 ? v : 1; }
 
 // Argument checks in signature order; returns the code of the first bad
@@ -65,9 +67,10 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // unit's n * 2*BM*BN*K FLOP at a fraction of its peak that depends on n
 // (few tiles per unit leave the matrix cores waiting on fills and barriers).
 // Both were fitted per kernel to interleaved timings of every candidate on
-// 26 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X; the
-// fitted model picks the fastest kernel on 23 of them and one within 9% on
-// the rest.
+// 26 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
+// (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
+// the fastest whole-tile kernel on 23 of them, with one the fastest of all
+// on 22, and in both cases one within 8% on the rest.
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
@@ -76,15 +79,17 @@ struct Candidate {
     double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 tiles per CU
 };
 
-// The tile kernels the model can choose among, with their block tiles.
+// The tile kernels the model can choose among, with their block tiles (and,
+// for the stream-K kernels, their K slice).
 struct TileKernel {
-    int variant, bm, bn;
+    int variant, bm, bn, bk;
 };
 static const TileKernel kTileKernels[] = {
-    {SGEMM_F32_MFMA_128, 128, 128},        {SGEMM_F32_MFMA_256, 256, 256},
-    {SGEMM_F32_MFMA_64x128, 64, 128},      {SGEMM_F32_MFMA_64, 64, 64},
-    {SGEMM_F32_MFMA_64x128_KG4, 64, 128},  {SGEMM_F32_MFMA_64x96_KG4, 64, 96},
-    {SGEMM_F32_MFMA_128x128_KG4, 128, 128},
+    {SGEMM_F32_MFMA_128, 128, 128, 0},        {SGEMM_F32_MFMA_256, 256, 256, 0},
+    {SGEMM_F32_MFMA_64x128, 64, 128, 0},      {SGEMM_F32_MFMA_64, 64, 64, 0},
+    {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 0},  {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 0},
+    {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 0}, {SGEMM_F32_MFMA_128_SK, 128, 128, 16},
+    {SGEMM_F32_MFMA_64x128_SK, 64, 128, 16},
 };
 static const TileKernel* tile_kernel(int variant) {
     for (const TileKernel& k : kTileKernels)
@@ -99,15 +104,17 @@ struct Model {
 };
 
 // Built-in model, listed in order of preference when predictions tie.
-static const Model kDefaultModel = {7,
+static const Model kDefaultModel = {9,
                                     {
-                                        {SGEMM_F32_MFMA_128, 128, 128, 11.0, {0.820, 0.877, 0.900, 0.907}},
-                                        {SGEMM_F32_MFMA_256, 256, 256, 24.5, {0.961, 0.927, 0.925, 0.925}},
-                                        {SGEMM_F32_MFMA_64x128, 64, 128, 6.5, {0.694, 0.734, 0.805, 0.844}},
-                                        {SGEMM_F32_MFMA_64, 64, 64, 7.5, {0.515, 0.606, 0.692, 0.783}},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 9.5, {0.790, 0.761, 0.778, 0.805}},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.5, {0.752, 0.721, 0.762, 0.769}},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 16.0, {0.903, 0.870, 0.871, 0.875}},
+                                        {SGEMM_F32_MFMA_128, 128, 128, 11.5, {0.822, 0.864, 0.901, 0.905}},
+                                        {SGEMM_F32_MFMA_256, 256, 256, 17.5, {0.971, 0.923, 0.936, 0.936}},
+                                        {SGEMM_F32_MFMA_64x128, 64, 128, 7.5, {0.712, 0.788, 0.820, 0.854}},
+                                        {SGEMM_F32_MFMA_64, 64, 64, 7.5, {0.525, 0.626, 0.713, 0.796}},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 10.0, {0.807, 0.782, 0.796, 0.808}},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.5, {0.754, 0.732, 0.777, 0.759}},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 14.0, {0.897, 0.860, 0.863, 0.866}},
+                                        {SGEMM_F32_MFMA_128_SK, 128, 128, 24.0, {0.756, 0.849, 0.864, 0.890}},
+                                        {SGEMM_F32_MFMA_64x128_SK, 64, 128, 14.5, {0.681, 0.737, 0.838, 0.854}},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a
@@ -122,28 +129,47 @@ static const int64_t kSkinnyMaxM = 32;
 // direct kernel is fastest (e.g. 256^3).
 static const double kTinyMacs = 64.0 * 1024 * 1024;
 
-static double eff_at(const Candidate& c, int64_t n) {
-    return n <= 1 ? c.eff[0] : n == 2 ? c.eff[1] : n <= 4 ? c.eff[2] : c.eff[3];
+static double eff_at(const Candidate& c, double n) {
+    return n <= 1.0 ? c.eff[0] : n <= 2.0 ? c.eff[1] : n <= 4.0 ? c.eff[2] : c.eff[3];
+}
+
+// Tiles' worth of work on the busiest compute unit for a candidate: whole
+// tiles dealt out breadth-first, or, for a stream-K kernel, the whole tiles
+// plus one run of slices (sk_split). 0 if a stream-K kernel would not split.
+static double busiest_tiles(const Candidate& c, int64_t M, int64_t N, int64_t K, int num_cus) {
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    const TileKernel* k = tile_kernel(c.variant);
+    if (k != nullptr && k->bk > 0) {
+        const SkSplit sp = sk_split(tiles, cdiv(K, k->bk), num_cus);
+        return sp.split() ? sp.busiest_tiles(num_cus) : 0.0;
+    }
+    return (double)cdiv(tiles, num_cus);
 }
 
 // `trans`: an operand is stored transposed (after the column-major swap);
-// only the kernels that read transposed operands are then candidates, and
-// the first of the built-in ones if the model holds none of them.
-static int choose(int64_t M, int64_t N, int64_t K, int num_cus, bool trans) {
+// only the kernels that read transposed operands are then candidates. The
+// stream-K kernels are candidates only when they split this shape and
+// `ws_bytes` covers the workspace they need. If no entry of the model
+// applies, mfma_128x128 (which takes any shape, transposed or not) runs.
+static int choose(const Args& a, int num_cus, size_t ws_bytes) {
     if (num_cus < 1) num_cus = 1;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const bool trans = a.ta || a.tb;
     if (!trans && M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
     if (!trans && (double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
     const Model* m = g_model.load(std::memory_order_acquire);
-    int best = trans ? SGEMM_F32_MFMA_128 : -1;
+    int best = SGEMM_F32_MFMA_128;
     double best_us = 0.0;
     bool found = false;
     for (int i = 0; i < m->n; ++i) {
         const Candidate& c = m->c[i];
-        if (trans && !kTable[c.variant]->trans_ok) continue;
-        const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-        const int64_t n = cdiv(tiles, num_cus);
+        const Variant& v = *kTable[c.variant];
+        if (trans && !v.trans_ok) continue;
+        if (v.ws_size != nullptr && (ws_bytes == 0 || v.ws_size(a, num_cus) > ws_bytes)) continue;
+        const double n = busiest_tiles(c, M, N, K, num_cus);
+        if (n <= 0.0) continue;
         const double us = c.overhead_us +
-                          1e6 * (double)n * 2.0 * c.bm * c.bn * (double)K / (kPeakPerCu * eff_at(c, n));
+                          1e6 * n * 2.0 * c.bm * c.bn * (double)K / (kPeakPerCu * eff_at(c, std::ceil(n)));
         if (!found || us < best_us) {
             best = c.variant;
             best_us = us;
@@ -220,18 +246,25 @@ static Args make_args(int layout, int transa, int transb, int64_t M, int64_t N, 
 // row-major problem. Shapes beyond a kernel's 32-bit buffer offsets fall back
 // to the plain-pointer register-tiled rung, which reads untransposed
 // operands only; a transposed call keeps its choice and fails its check.
-static int plan_args(const Args& a, int num_cus) {
+static int plan_args(const Args& a, int num_cus, size_t ws_bytes) {
     const bool trans = a.ta || a.tb;
-    int v = choose(a.M, a.N, a.K, num_cus, trans);
+    int v = choose(a, num_cus, ws_bytes);
     if (!trans && kTable[v]->check(a) != 0) v = SGEMM_F32_REG_2D;
     return v;
 }
 
+// A workspace of nonzero size must be a 16-byte aligned device pointer.
+static int validate_ws(const void* ws, size_t ws_bytes) {
+    return (ws_bytes > 0 && (ws == nullptr || misaligned16(ws))) ? -16 : 0;
+}
+
 static int run(int forced, int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
                float alpha, const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
-               float* C, int64_t ldc, void* stream) {
+               float* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
     if (forced >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
     int rc = validate(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc) return rc;
+    rc = validate_ws(ws, ws_bytes);
     if (rc) return rc;
     if (M == 0 || N == 0) return 0;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
@@ -241,24 +274,29 @@ static int run(int forced, int layout, int transa, int transb, int64_t M, int64_
         const hipError_t e = launch_scale(a, s);
         return e == hipSuccess ? 0 : (int)e;
     }
-    int v = forced;
-    if (v < 0) {
-        int cus = 0;
+    int v = forced, cus = 0;
+    if (v < 0 || kTable[v]->launch_ws != nullptr) {
         rc = device_cus(&cus);
         if (rc) return rc;
-        v = plan_args(a, cus);
     }
+    if (v < 0) v = plan_args(a, cus, ws_bytes);
     const Variant& var = *kTable[v];
     if ((a.ta || a.tb) && !var.trans_ok) return SGEMM_F32_ERR_UNSUPPORTED;
     rc = var.check(a);
     if (rc) return rc;
-    const hipError_t e = var.launch(a, s);
+    hipError_t e;
+    if (var.launch_ws != nullptr) {
+        if (var.ws_size(a, cus) > ws_bytes) return SGEMM_F32_ERR_WORKSPACE;
+        e = var.launch_ws(a, ws, ws_bytes, cus, s);
+    } else {
+        e = var.launch(a, s);
+    }
     return e == hipSuccess ? 0 : (int)e;
 }
 
 static int plan(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, const float* C,
-                int64_t ldc, int num_cus, int* variant) {
+                int64_t ldc, size_t ws_bytes, int num_cus, int* variant) {
     int rc = validate(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc) return rc;
     if (variant == nullptr) return -12;
@@ -269,7 +307,37 @@ static int plan(int layout, int transa, int transb, int64_t M, int64_t N, int64_
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
     const Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta,
                              const_cast<float*>(C), ldc);
-    *variant = plan_args(a, num_cus);
+    *variant = plan_args(a, num_cus, ws_bytes);
+    return 0;
+}
+
+// Workspace a stream-K variant (or, with variant == -1, the largest any of
+// them) needs for this problem on num_cus compute units.
+static int ws_size(int variant, int layout, int transa, int transb, int64_t M, int64_t N,
+                   int64_t K, int num_cus, size_t* bytes) {
+    if (variant < -1 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    if (layout != SGEMM_F32_ROW_MAJOR && layout != SGEMM_F32_COL_MAJOR) return -13;
+    if (transa != SGEMM_F32_NO_TRANS && transa != SGEMM_F32_TRANS) return -14;
+    if (transb != SGEMM_F32_NO_TRANS && transb != SGEMM_F32_TRANS) return -15;
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    if (bytes == nullptr) return -12;
+    *bytes = 0;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
+    if (num_cus < 1) num_cus = 1;
+    // Only the sizes and flags matter for the workspace.
+    const Args a = make_args(layout, transa, transb, M, N, K, 1.0f, nullptr, 1, nullptr, 1, 0.0f,
+                             nullptr, 1);
+    const bool trans = a.ta || a.tb;
+    for (int v = 0; v < SGEMM_F32_NUM_VARIANTS; ++v) {
+        const Variant& var = *kTable[v];
+        if (var.ws_size == nullptr || (variant >= 0 && v != variant)) continue;
+        if (variant < 0 && trans && !var.trans_ok) continue;
+        const size_t need = var.ws_size(a, num_cus);
+        if (need > *bytes) *bytes = need;
+    }
     return 0;
 }
 
@@ -283,7 +351,7 @@ SGEMM_F32_API int sgemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const 
                             int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                             int64_t ldc, void* stream) {
     return run(-1, SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS, SGEMM_F32_NO_TRANS, M, N, K, alpha, A,
-               lda, B, ldb, beta, C, ldc, stream);
+               lda, B, ldb, beta, C, ldc, nullptr, 0, stream);
 }
 
 SGEMM_F32_API int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K, float alpha,
@@ -291,20 +359,21 @@ SGEMM_F32_API int sgemm_f32_variant(int variant, int64_t M, int64_t N, int64_t K
                                     float beta, float* C, int64_t ldc, void* stream) {
     if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
     return run(variant, SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS, SGEMM_F32_NO_TRANS, M, N, K, alpha,
-               A, lda, B, ldb, beta, C, ldc, stream);
+               A, lda, B, ldb, beta, C, ldc, nullptr, 0, stream);
 }
 
 SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
                                  int64_t lda, const float* B, int64_t ldb, float beta,
                                  const float* C, int64_t ldc, int num_cus, int* variant) {
     return plan(SGEMM_F32_ROW_MAJOR, SGEMM_F32_NO_TRANS, SGEMM_F32_NO_TRANS, M, N, K, alpha, A, lda,
-                B, ldb, beta, C, ldc, num_cus, variant);
+                B, ldb, beta, C, ldc, 0, num_cus, variant);
 }
 
 SGEMM_F32_API int sgemm_f32_ex(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
                                float alpha, const float* A, int64_t lda, const float* B,
                                int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
-    return run(-1, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return run(-1, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0,
+               stream);
 }
 
 SGEMM_F32_API int sgemm_f32_variant_ex(int variant, int layout, int transa, int transb, int64_t M,
@@ -313,15 +382,47 @@ SGEMM_F32_API int sgemm_f32_variant_ex(int variant, int layout, int transa, int 
                                        float* C, int64_t ldc, void* stream) {
     if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
     return run(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-               stream);
+               nullptr, 0, stream);
 }
 
 SGEMM_F32_API int sgemm_f32_plan_ex(int layout, int transa, int transb, int64_t M, int64_t N,
                                     int64_t K, float alpha, const float* A, int64_t lda,
                                     const float* B, int64_t ldb, float beta, const float* C,
                                     int64_t ldc, int num_cus, int* variant) {
-    return plan(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, num_cus,
+    return plan(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, 0, num_cus,
                 variant);
+}
+
+SGEMM_F32_API int sgemm_f32_ws(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float* A, int64_t lda, const float* B,
+                               int64_t ldb, float beta, float* C, int64_t ldc, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return run(-1, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+               workspace_bytes, stream);
+}
+
+SGEMM_F32_API int sgemm_f32_variant_ws(int variant, int layout, int transa, int transb, int64_t M,
+                                       int64_t N, int64_t K, float alpha, const float* A,
+                                       int64_t lda, const float* B, int64_t ldb, float beta,
+                                       float* C, int64_t ldc, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    return run(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+               workspace, workspace_bytes, stream);
+}
+
+SGEMM_F32_API int sgemm_f32_plan_ws(int layout, int transa, int transb, int64_t M, int64_t N,
+                                    int64_t K, float alpha, const float* A, int64_t lda,
+                                    const float* B, int64_t ldb, float beta, const float* C,
+                                    int64_t ldc, size_t workspace_bytes, int num_cus,
+                                    int* variant) {
+    return plan(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                workspace_bytes, num_cus, variant);
+}
+
+SGEMM_F32_API int sgemm_f32_ws_size(int variant, int layout, int transa, int transb, int64_t M,
+                                    int64_t N, int64_t K, int num_cus, size_t* bytes) {
+    return ws_size(variant, layout, transa, transb, M, N, K, num_cus, bytes);
 }
 
 SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant) {
@@ -362,6 +463,8 @@ SGEMM_F32_API const char* sgemm_f32_strerror(int code) {
         case -13: return "layout is neither SGEMM_F32_ROW_MAJOR nor SGEMM_F32_COL_MAJOR";
         case -14: return "transa is neither SGEMM_F32_NO_TRANS nor SGEMM_F32_TRANS";
         case -15: return "transb is neither SGEMM_F32_NO_TRANS nor SGEMM_F32_TRANS";
+        case -16: return "workspace is NULL with a nonzero size, or not 16-byte aligned";
+        case SGEMM_F32_ERR_WORKSPACE: return "the stream-K variant needs a larger workspace (sgemm_f32_ws_size)";
         case SGEMM_F32_ERR_VARIANT: return "variant id out of range";
         case SGEMM_F32_ERR_UNSUPPORTED: return "variant cannot run this shape, alignment or transposition";
         case SGEMM_F32_ERR_TOO_LARGE: return "a size exceeds what the kernel can index";

@@ -88,13 +88,15 @@ __device__ __forceinline__ void buf_load_lds4(__amdgpu_buffer_rsrc_t r, const fl
 // ---------------------------------------------------------------------------
 constexpr int NUM_XCD = 8;
 
-__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int group_m,
-                                        bool xcd_remap, int& tm, int& tn) {
-    const int T = tiles_m * tiles_n;
+// tile_of_first: the renumbering applies to the ids below `first` only (a
+// bijection of [0, first)); ids from `first` on keep their order. The
+// stream-K kernels use it for their whole-tile workgroups.
+__device__ __forceinline__ void tile_of_first(int wg, int first, int tiles_m, int tiles_n,
+                                              int group_m, bool xcd_remap, int& tm, int& tn) {
     int L = wg;
-    if (xcd_remap) {
+    if (xcd_remap && wg < first) {
         const int x = wg % NUM_XCD, idx = wg / NUM_XCD;
-        const int q = T / NUM_XCD, r = T % NUM_XCD;
+        const int q = first / NUM_XCD, r = first % NUM_XCD;
         L = x * q + (x < r ? x : r) + idx;
     }
     const int per_group = group_m * tiles_n;
@@ -105,6 +107,33 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int gr
     tm = first_m + in % rows;
     tn = in / rows;
 }
+
+__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int group_m,
+                                        bool xcd_remap, int& tm, int& tn) {
+    tile_of_first(wg, tiles_m * tiles_n, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K work split (kernel argument of the stream-K kernels). Following
+// the pages' hybrid ("Optimizing Matrix Multiply on CUDA, Part 2",
+// "Distributing the Partially Filled Wave"), the tiles that fill whole rounds
+// of the compute units stay whole, and only the remaining tiles are split
+// along K: their slices, taken tile by tile, are dealt out in equal
+// contiguous runs to sk_wgs workgroups; the pieces of each split tile are
+// then summed in K order and written to C.
+//   workgroups [0, dp_tiles)                whole tiles 0 .. dp_tiles-1
+//   workgroups dp_tiles + j, j < sk_wgs     slices [j*upw, min((j+1)*upw, U))
+//                                           of tiles dp_tiles .. dp_tiles+sk_tiles-1,
+//                                           U = sk_tiles * slices, slice u in
+//                                           tile dp_tiles + u / slices
+// A workgroup's run crosses a tile boundary at most at its two ends, so it
+// has at most two partial pieces: its first (slot 2j) and its last (slot
+// 2j+1), each a BM x BN tile of partial sums in `partials`.
+// ---------------------------------------------------------------------------
+struct SkPlan {
+    int dp_tiles, sk_tiles, sk_wgs, upw, slices;
+    float* partials;   // 2 * sk_wgs slots of BM*BN floats
+};
 
 // LDS swizzle for a 16-float row of an untransposed A tile read with 16-byte
 // loads: 16-byte chunk q of row r is stored at chunk q ^ swz16(r). With 8

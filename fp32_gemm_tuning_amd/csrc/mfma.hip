@@ -325,76 +325,235 @@ struct SubstepMma {
 constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
 constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
 
-template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC, bool TA = false,
-          bool TB = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
-    constexpr int WAVES_N = BN / WN;
-    constexpr int NT = (BM / WM) * WAVES_N * 64;
-    constexpr int BI = WM / 32, BJ = WN / 32;
+// The body of k_mfma_tile, shared with its stream-K form: the product of the
+// slices [s_begin, s_end) of one tile, and the epilogue. The LDS stages are
+// the caller's (one object each); on return every wave has passed the last
+// barrier and no load into them is outstanding.
+template <int BM, int BN, int WM, int WN, int BK, bool VEC, bool TA, bool TB>
+struct TileCore {
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NT = (BM / WM) * WAVES_N * 64;
+    static constexpr int BI = WM / 32, BJ = WN / 32;
     using Dma = TileFillDma<BM, BN, BK, NT, VEC, TA, TB>;
-    constexpr int BNP = Dma::BNP;
-    constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
-    // One LDS object per stage, so that the compiler can tell the stage being
-    // filled from the stage being read.
-    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs0[BK * BNP];
-    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs1[BK * BNP];
+    static constexpr int BNP = Dma::BNP;
 
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
-    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w / WAVES_N, wn = w % WAVES_N;
-    const int h = lane >> 5, c = lane & 31;
+    int m0, n0, rows_valid, cols_valid, t, wm, wn, h, c;
 
-    f32x16 acc[BI][BJ];
-#pragma unroll
-    for (int i = 0; i < BI; ++i)
-#pragma unroll
-        for (int j = 0; j < BJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    __device__ __forceinline__ TileCore(const Args& a, int tm, int tn, int tid = threadIdx.x) {
+        m0 = tm * BM;
+        n0 = tn * BN;
+        rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+        cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+        t = tid;
+        const int lane = t & 63, w = t >> 6;
+        wm = w / WAVES_N;
+        wn = w % WAVES_N;
+        h = lane >> 5;
+        c = lane & 31;
+    }
 
-    const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, 0, 0);
-    auto compute = [&](const float* Ac, const float* Bc) { mma(Ac, Bc, acc); };
+    __device__ __forceinline__ static void zero(f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    }
 
     // One pipelined step: start filling slice s+1 into the other stage with
     // buffer-to-LDS loads, multiply slice s from this stage, barrier (which
     // also waits for this wave's loads). With one barrier per slice and two
     // stages, a stage is refilled only after every wave has passed the
     // barrier that ends the slice that read it.
-    const int nslices = (a.K + BK - 1) / BK;
-    const Dma dma;
-    auto step = [&](int s, float* Acur, float* Bcur, float* Anext, float* Bnext) {
-        if (s + 1 < nslices)
-            dma.issue(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid, Anext, Bnext);
-        compute(Acur, Bcur);
+    __device__ __forceinline__ void mainloop(const Args& a, int s_begin, int s_end, float* As0,
+                                             float* Bs0, float* As1, float* Bs1,
+                                             f32x16 (&acc)[BI][BJ]) const {
+        const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, 0, 0);
+        const Dma dma;
+        auto step = [&](int s, float* Acur, float* Bcur, float* Anext, float* Bnext) {
+            if (s + 1 < s_end)
+                dma.issue(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid, Anext, Bnext);
+            mma(Acur, Bcur, acc);
+            __syncthreads();
+        };
+        dma.issue(a, t, m0, n0, s_begin * BK, rows_valid, cols_valid, As0, Bs0);
         __syncthreads();
-    };
-
-    dma.issue(a, t, m0, n0, 0, rows_valid, cols_valid, As0, Bs0);
-    __syncthreads();
-    for (int s = 0; s < nslices; s += 2) {
-        step(s, As0, Bs0, As1, Bs1);
-        if (s + 1 < nslices) step(s + 1, As1, Bs1, As0, Bs0);
+        for (int s = s_begin; s < s_end; s += 2) {
+            step(s, As0, Bs0, As1, Bs1);
+            if (s + 1 < s_end) step(s + 1, As1, Bs1, As0, Bs0);
+        }
     }
 
+    __device__ __forceinline__ void store(const Args& a, const f32x16 (&acc)[BI][BJ]) const {
 #pragma unroll
-    for (int bi = 0; bi < BI; ++bi)
+        for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < BJ; ++bj)
+            for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int j = wn * WN + bj * 32 + c;
-                if (i < rows_valid && j < cols_valid)
-                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+                for (int r = 0; r < 16; ++r) {
+                    const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int j = wn * WN + bj * 32 + c;
+                    if (i < rows_valid && j < cols_valid)
+                        store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+                }
+    }
+};
+
+template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC, bool TA = false,
+          bool TB = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    using Core = TileCore<BM, BN, WM, WN, BK, VEC, TA, TB>;
+    // One LDS object per stage, so that the compiler can tell the stage being
+    // filled from the stage being read.
+    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs0[BK * Core::BNP];
+    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs1[BK * Core::BNP];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+    const Core core(a, tm, tn);
+    f32x16 acc[Core::BI][Core::BJ];
+    Core::zero(acc);
+    core.mainloop(a, 0, (a.K + BK - 1) / BK, As0, Bs0, As1, Bs1, acc);
+    core.store(a, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Stream-K (SkPlan in common.hpp). A run of slices that covers a whole tile
+// writes C directly; any other run leaves its partial tile in the workspace,
+// and a second kernel on the same stream (k_sk_fixup) sums the pieces of
+// each split tile in K order -- so the result does not depend on which
+// piece finished first -- and writes C. The kernel boundary orders the
+// partial stores before their reads. (The pages let the unit that computes
+// a tile's last piece combine the pieces inside the one kernel. On MI355X
+// that needs a release fence per piece and an acquire per tile at device
+// scope, and each of those writes back or invalidates a whole XCD's L2,
+// which cost 13-37 us per call at 1536^3-3072^3, against a few us for the
+// second launch.)
+//
+// Partial tiles travel as 16-byte vectors: vector q of thread t of a BM x BN
+// tile is at float offset (q * NT + t) * 4 of its slot, so each access of a
+// wave is 1 KiB contiguous, and the fixup kernel, with the same thread
+// layout, reads back exactly the values each of its threads owns.
+// ---------------------------------------------------------------------------
+template <int BI, int BJ, int NT>
+struct PartialIo {
+    static constexpr int Q = BI * BJ * 4;   // 16-byte vectors per lane
+
+    __device__ __forceinline__ static void put(float* slot, int t, const f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
+            *(f32x4*)(slot + ((size_t)q * NT + t) * 4) =
+                f32x4{acc[bi][bj][r0], acc[bi][bj][r0 + 1], acc[bi][bj][r0 + 2], acc[bi][bj][r0 + 3]};
+        }
+    }
+
+    // acc = slot (FIRST) or acc += slot, one 32x32 block at a time (the asm
+    // pin keeps the compiler from loading a whole partial tile at once).
+    template <bool FIRST>
+    __device__ __forceinline__ static void gather(const float* slot, int t, f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
+            const f32x4 v = *(const f32x4*)(slot + ((size_t)q * NT + t) * 4);
+            if (FIRST) {
+                acc[bi][bj][r0] = v.x;
+                acc[bi][bj][r0 + 1] = v.y;
+                acc[bi][bj][r0 + 2] = v.z;
+                acc[bi][bj][r0 + 3] = v.w;
+            } else {
+                acc[bi][bj][r0] += v.x;
+                acc[bi][bj][r0 + 1] += v.y;
+                acc[bi][bj][r0 + 2] += v.z;
+                acc[bi][bj][r0 + 3] += v.w;
             }
+            if (q % 4 == 3) asm volatile("" : "+v"(acc[bi][bj])::"memory");
+        }
+    }
+};
+
+// Slot of workgroup jj's piece of split tile st: its first run (slot 2jj)
+// if that run starts in the tile, else its last run (slot 2jj+1).
+__device__ __forceinline__ int sk_slot(const SkPlan& p, int jj, int st) {
+    return (jj * p.upw >= st * p.slices) ? 2 * jj : 2 * jj + 1;
+}
+
+// Stream-K form of k_mfma_tile: workgroups below p.dp_tiles compute whole
+// tiles as k_mfma_tile does; the others their runs of slices.
+template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC, bool TA = false,
+          bool TB = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_tile_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
+    using Core = TileCore<BM, BN, WM, WN, BK, VEC, TA, TB>;
+    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
+    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs0[BK * Core::BNP];
+    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs1[BK * Core::BNP];
+
+    const int b = blockIdx.x;
+    f32x16 acc[Core::BI][Core::BJ];
+    int tm, tn;
+    if (b < p.dp_tiles) {
+        tile_of_first(b, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+        const Core core(a, tm, tn);
+        Core::zero(acc);
+        core.mainloop(a, 0, p.slices, As0, Bs0, As1, Bs1, acc);
+        core.store(a, acc);
+        return;
+    }
+    const int j = b - p.dp_tiles;
+    const int U = p.sk_tiles * p.slices;
+    int u = j * p.upw;
+    const int u_end = (u + p.upw) < U ? (u + p.upw) : U;
+    while (u < u_end) {
+        const int st = u / p.slices;
+        const int s0 = u - st * p.slices;
+        const int s1 = (s0 + (u_end - u)) < p.slices ? (s0 + (u_end - u)) : p.slices;
+        tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M,
+                      xcd_remap != 0, tm, tn);
+        // The lane's fragment and epilogue offsets derive from its thread
+        // index; hidden from the compiler here, they are recomputed per run
+        // instead of being hoisted out of the loop (and spilled).
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const Core core(a, tm, tn, tid);
+        Core::zero(acc);
+        core.mainloop(a, s0, s1, As0, Bs0, As1, Bs1, acc);
+        if (s0 == 0 && s1 == p.slices)
+            core.store(a, acc);
+        else
+            Io::put(p.partials + (size_t)sk_slot(p, j, st) * BM * BN, core.t, acc);
+        u += s1 - s0;
+    }
+}
+
+// One workgroup per split tile: the sum of its pieces in K order, then the
+// epilogue. A tile covered by a single run was written by that run.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+void k_sk_fixup(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
+    using Core = TileCore<BM, BN, WM, WN, 16, true, false, false>;
+    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
+    const int st = blockIdx.x;
+    const int j0 = st * p.slices / p.upw, j1 = (st * p.slices + p.slices - 1) / p.upw;
+    if (j0 == j1) return;
+    int tm, tn;
+    tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0,
+                  tm, tn);
+    const Core core(a, tm, tn);
+    f32x16 acc[Core::BI][Core::BJ];
+    constexpr size_t TILE = (size_t)BM * BN;
+    Io::template gather<true>(p.partials + (size_t)sk_slot(p, j0, st) * TILE, core.t, acc);
+    for (int jj = j0 + 1; jj <= j1; ++jj)
+        Io::template gather<false>(p.partials + (size_t)sk_slot(p, jj, st) * TILE, core.t, acc);
+    core.store(a, acc);
 }
 
 // ===========================================================================
@@ -842,6 +1001,53 @@ struct TileInstance {
 using Tile128 = TileInstance<M128_BM, M128_BN, M128_WM, M128_WN>;
 using Tile64x128 = TileInstance<64, 128, 32, 64>;
 
+// Stream-K launch of a TileInstance tile: one workgroup per whole tile plus
+// the stream-K workgroups, then the fixup kernel on the same stream.
+template <int BM, int BN, int WM, int WN>
+struct TileSkInstance {
+    using Base = TileInstance<BM, BN, WM, WN>;
+    static SkSplit split(const Args& a, int cus) {
+        return sk_split(cdiv(a.M, BM) * cdiv(a.N, BN), cdiv(a.K, M128_BK), cus);
+    }
+    static size_t ws_size(const Args& a, int cus) { return sk_workspace_bytes(split(a, cus), BM, BN); }
+    static hipError_t launch_ws(const Args& a, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
+        const SkSplit sp = split(a, cus);
+        if (!sp.split()) return Base::launch(a, s);
+        if (ws == nullptr || ws_bytes < sk_workspace_bytes(sp, BM, BN)) return hipErrorInvalidValue;
+        SkPlan p;
+        p.dp_tiles = (int)sp.dp_tiles;
+        p.sk_tiles = (int)sp.sk_tiles;
+        p.sk_wgs = (int)sp.sk_wgs;
+        p.upw = (int)sp.upw;
+        p.slices = (int)sp.slices;
+        p.partials = (float*)ws;
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(Base::NT);
+        const bool vec = vec_ok(a);
+        const hipError_t e = with_trans(a, [&](auto ta, auto tb) {
+            constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+            if (vec)
+                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU,
+                                                   true, TA, TB>),
+                                   grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+            else
+                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, M128_BK, 3, false, TA, TB>), grid,
+                                   block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+            return hipGetLastError();
+        });
+        // Runs as long as a tile (upw == slices) cover whole tiles only.
+        if (e != hipSuccess || p.upw == p.slices) return e;
+        hipLaunchKernelGGL((k_sk_fixup<BM, BN, WM, WN>), dim3((unsigned)p.sk_tiles), block, 0, s, a,
+                           tm, tn, xcd_remap_enabled(), p);
+        return hipGetLastError();
+    }
+    static const void* kernel() {
+        return (const void*)k_mfma_tile_sk<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU, true>;
+    }
+};
+using Tile128Sk = TileSkInstance<M128_BM, M128_BN, M128_WM, M128_WN>;
+using Tile64x128Sk = TileSkInstance<64, 128, 32, 64>;
+
 static int check_mfma128(const Args& a) { return Tile128::check(a); }
 static hipError_t launch_mfma128(const Args& a, hipStream_t s) { return Tile128::launch(a, s); }
 static int check_mfma64x128(const Args& a) { return Tile64x128::check(a); }
@@ -851,6 +1057,11 @@ static hipError_t launch_mfma64x128(const Args& a, hipStream_t s) {
 
 Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
                     Tile128::kernel<true>(), Tile128::NT, true};
+// Stream-K forms (they need a workspace: sgemm_f32_ws).
+Variant kMfma128Sk = {"mfma_128x128_sk", check_mfma128, nullptr, Tile128Sk::kernel(), Tile128::NT,
+                      true, Tile128Sk::ws_size, Tile128Sk::launch_ws};
+Variant kMfma64x128Sk = {"mfma_64x128_sk", check_mfma64x128, nullptr, Tile64x128Sk::kernel(),
+                         Tile64x128::NT, true, Tile64x128Sk::ws_size, Tile64x128Sk::launch_ws};
 // 64x128 tile, 4 waves of 32x64: twice the tiles of mfma_128x128 for
 // medium shapes (e.g. 2048^3, where 256 tiles of 128x128 leave one
 // workgroup per compute unit).

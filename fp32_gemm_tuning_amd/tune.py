@@ -41,7 +41,13 @@ TILE: Dict[str, Tuple[int, int]] = {
     "mfma_64x128_kg4": (64, 128),
     "mfma_64x96_kg4": (64, 96),
     "mfma_128x128_kg4": (128, 128),
+    "mfma_128x128_sk": (128, 128),
+    "mfma_64x128_sk": (64, 128),
 }
+# Stream-K kernels and their K slice: their busiest unit holds floor(T/C)
+# whole tiles plus one run of slices (sk_split in the library), and they are
+# candidates only with a workspace, on shapes they split.
+SK_BK: Dict[str, int] = {"mfma_128x128_sk": 16, "mfma_64x128_sk": 16}
 PEAK_PER_CU = 4 * 64 * 2.4e9   # FP32 matrix FLOP/s of one MI355X compute unit
 
 # Shapes the built-in model was fitted on: square, flat, tall, odd, short-K.
@@ -60,42 +66,76 @@ QUICK_SHAPES: List[Tuple[int, int, int]] = [
 ]
 
 
-def bucket(n: int) -> int:
-    """Tiles-per-CU bucket of a model entry: n = 1, 2, 3-4, >= 5."""
+def bucket(n: float) -> int:
+    """Tiles-per-CU bucket of a model entry: n = 1, 2, 3-4, >= 5 (a
+    fractional stream-K share counts as its ceiling)."""
+    n = math.ceil(n)
     return 0 if n <= 1 else 1 if n == 2 else 2 if n <= 4 else 3
 
 
-def tiles_per_cu(variant: str, M: int, N: int, num_cus: int) -> int:
+def sk_split(tiles: int, slices: int, num_cus: int) -> Optional[Tuple[int, int, int, int]]:
+    """(dp_tiles, sk_tiles, sk_wgs, upw) as the library splits, or None
+    when it does not split."""
+    cus = max(1, num_cus)
+    R = tiles % cus
+    if R == 0 or slices < 1 or R * slices > 2**31 - 1:
+        return None
+    G = min(cus, 4 * R)
+    U = R * slices
+    upw = -(-U // G)
+    return tiles - R, R, -(-U // upw), upw
+
+
+def tiles_per_cu(variant: str, M: int, N: int, num_cus: int, K: int = 0) -> float:
+    """Tiles' worth of work on the busiest compute unit (0 for a stream-K
+    kernel that would not split the shape)."""
     bm, bn = TILE[variant]
-    return -(-(-(-M // bm) * -(-N // bn)) // max(1, num_cus))
+    tiles = -(-M // bm) * -(-N // bn)
+    cus = max(1, num_cus)
+    if variant in SK_BK:
+        sp = sk_split(tiles, -(-K // SK_BK[variant]), cus)
+        if sp is None:
+            return 0.0
+        return sp[0] // cus + sp[3] / -(-K // SK_BK[variant])
+    return float(-(-tiles // cus))
 
 
 def predict_us(entry: dict, M: int, N: int, K: int, num_cus: int,
                peak_per_cu: float = PEAK_PER_CU) -> float:
     """The library's prediction for one model entry (sgemm_f32_model_entry)."""
     bm, bn = TILE[entry["variant"]]
-    n = tiles_per_cu(entry["variant"], M, N, num_cus)
+    n = tiles_per_cu(entry["variant"], M, N, num_cus, K)
+    if n <= 0:
+        return math.inf
     return entry["overhead_us"] + 1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * entry["eff"][bucket(n)])
 
 
-def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int) -> str:
-    """The entry with the smallest prediction (earlier entries win ties)."""
+def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int,
+           workspace: bool = False) -> str:
+    """The entry with the smallest prediction (earlier entries win ties);
+    stream-K entries only with a workspace and on shapes they split;
+    mfma_128x128 when no entry applies."""
     best, best_us = None, 0.0
     for e in model:
+        if e["variant"] in SK_BK and not workspace:
+            continue
         us = predict_us(e, M, N, K, num_cus)
+        if us == math.inf:
+            continue
         if best is None or us < best_us:
             best, best_us = e["variant"], us
-    return best
+    return "mfma_128x128" if best is None else best
 
 
 def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[str]] = None,
             rounds: int = 3, calls: int = 4, device=None, log=None) -> List[dict]:
     """Median HIP-event time of each (kernel, shape), kernels interleaved.
-    Returns samples {variant, M, N, K, ms}; kernels that reject a shape are
-    left out."""
+    Returns samples {variant, M, N, K, ms}; kernels that reject a shape, and
+    stream-K kernels on shapes they do not split, are left out."""
     import torch
     dev = torch.device("cuda:0") if device is None else device
     stream = torch.cuda.current_stream(dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
     variants = list(TILE) if variants is None else list(variants)
     ids = {v: sg.sgemm_f32_variant_by_name(v) for v in variants}
     out = []
@@ -104,11 +144,16 @@ def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[
         A = torch.rand(M, K, device=dev, generator=g) * 2 - 1
         B = torch.rand(K, N, device=dev, generator=g) * 2 - 1
         C = torch.empty(M, N, device=dev)
+        _, wsb = sg.sgemm_f32_ws_size(-1, sg.ROW_MAJOR, 0, 0, M, N, K, cus)
+        ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=dev)
+
+        def call(v):
+            return sg.sgemm_f32_variant_ws(ids[v], sg.ROW_MAJOR, 0, 0, M, N, K, 1.0, A, K, B, N,
+                                           0.0, C, N, ws, wsb, stream.cuda_stream)
         times = {v: [] for v in variants}
         ok = {}
         for v in variants:    # first call of each kernel: warm-up and support check
-            ok[v] = sg.sgemm_f32_variant(ids[v], M, N, K, 1.0, A, K, B, N, 0.0, C, N,
-                                         stream.cuda_stream) == 0
+            ok[v] = call(v) == 0 and tiles_per_cu(v, M, N, cus, K) > 0
         torch.cuda.synchronize()
         live = [v for v in variants if ok[v]]
         for r in range(rounds):
@@ -118,8 +163,7 @@ def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[
                       for _ in range(calls)]
                 for a, b in ev:
                     a.record(stream)
-                    sg.sgemm_f32_variant(ids[v], M, N, K, 1.0, A, K, B, N, 0.0, C, N,
-                                         stream.cuda_stream)
+                    call(v)
                     b.record(stream)
                 torch.cuda.synchronize()
                 times[v] += [a.elapsed_time(b) for a, b in ev]
@@ -129,7 +173,7 @@ def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[
             out.append({"variant": v, "M": M, "N": N, "K": K, "ms": ms})
             if log:
                 log(f"{M}x{N}x{K} {v}: {ms:.4f} ms, {2.0 * M * N * K / ms / 1e9:.1f} TFLOP/s")
-        del A, B, C
+        del A, B, C, ws
     return out
 
 
@@ -142,7 +186,7 @@ def fit(samples: Sequence[dict], num_cus: int, peak_per_cu: float = PEAK_PER_CU,
     by_v: Dict[str, List[Tuple[int, float, float]]] = {}
     for s in samples:
         bm, bn = TILE[s["variant"]]
-        n = tiles_per_cu(s["variant"], s["M"], s["N"], num_cus)
+        n = tiles_per_cu(s["variant"], s["M"], s["N"], num_cus, s["K"])
         work_us = 1e6 * n * 2.0 * bm * bn * s["K"] / peak_per_cu   # at 100% of peak
         by_v.setdefault(s["variant"], []).append((n, work_us, s["ms"] * 1e3))
     model = []
@@ -183,7 +227,7 @@ def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[
     res = []
     for (M, N, K), d in by_shape.items():
         sub = [e for e in model if e["variant"] in d]
-        pick = choose(sub, M, N, K, num_cus)
+        pick = choose(sub, M, N, K, num_cus, workspace=True)
         fastest = min(d, key=d.get)
         res.append({"shape": [M, N, K], "picked": pick, "fastest": fastest,
                     "loss": round(d[pick] / d[fastest] - 1.0, 4)})
@@ -226,7 +270,12 @@ def main(argv=None) -> int:
         print(json.dumps({"installed": args.load, "rc": rc}))
         for (M, N, K) in shapes:
             _, v = sg.sgemm_f32_plan(M, N, K, 1.0, 0x1000, K, 0x1000, N, 0.0, 0x1000, N, cus)
-            print(json.dumps({"shape": [M, N, K], "plan": sg.sgemm_f32_variant_name(v)}))
+            _, wsb = sg.sgemm_f32_ws_size(-1, sg.ROW_MAJOR, 0, 0, M, N, K, cus)
+            _, vw = sg.sgemm_f32_plan_ws(sg.ROW_MAJOR, 0, 0, M, N, K, 1.0, 0x1000, K, 0x1000, N,
+                                         0.0, 0x1000, N, wsb, cus)
+            print(json.dumps({"shape": [M, N, K], "plan": sg.sgemm_f32_variant_name(v),
+                              "plan_with_workspace": sg.sgemm_f32_variant_name(vw),
+                              "workspace_bytes": wsb}))
         return 0 if rc == 0 else 1
     samples = measure(shapes, rounds=args.rounds, calls=args.calls,
                       log=lambda m: print(m, file=sys.stderr, flush=True))

@@ -47,6 +47,10 @@
  *                               leading dimension that is not a multiple of 4)
  *    SGEMM_F32_ERR_TOO_LARGE    a size exceeds what the kernel can index
  *    SGEMM_F32_ERR_DEVICE       no usable HIP device
+ *    SGEMM_F32_ERR_WORKSPACE    a forced stream-K variant was given less
+ *                               workspace than sgemm_f32_ws_size reports
+ *    -16                    (the _ws entry points) the workspace pointer is
+ *                           NULL with a nonzero size, or not 16-byte aligned
  *   > 0                     a hipError_t reported by the HIP runtime at launch
  *
  * Thread safety: all entry points are reentrant.
@@ -54,6 +58,7 @@
 #ifndef SGEMM_F32_H
 #define SGEMM_F32_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -71,6 +76,7 @@ extern "C" {
 #define SGEMM_F32_ERR_UNSUPPORTED (-101)
 #define SGEMM_F32_ERR_TOO_LARGE (-102)
 #define SGEMM_F32_ERR_DEVICE (-103)
+#define SGEMM_F32_ERR_WORKSPACE (-104)
 
 /* Kernel variants. The first six are the rungs of the pages' optimisation
  * ladder, rebuilt for wave64; the rest are the gfx950 kernels the automatic
@@ -130,7 +136,14 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_MFMA_64x96_KG4 = 15,
     /* the same with a 128x128 tile of 16 waves (4 groups of 4 waves of 64x64) */
     SGEMM_F32_MFMA_128x128_KG4 = 16,
-    SGEMM_F32_NUM_VARIANTS = 17
+    /* stream-K forms of MFMA_128 and MFMA_64x128 (sgemm_f32_ws): the tiles
+       that fill whole rounds of the compute units are computed whole; the
+       rest are split along K across the units, and the workgroup that
+       finishes a tile's last piece sums the pieces in K order and writes C.
+       They need a workspace (sgemm_f32_ws_size) */
+    SGEMM_F32_MFMA_128_SK = 17,
+    SGEMM_F32_MFMA_64x128_SK = 18,
+    SGEMM_F32_NUM_VARIANTS = 19
 };
 
 /* Storage order and operand transposition of the _ex entry points (the
@@ -206,8 +219,70 @@ SGEMM_F32_API int sgemm_f32_plan_ex(int layout, int transa, int transb, int64_t 
                                     const float *B, int64_t ldb, float beta, const float *C,
                                     int64_t ldc, int num_cus, int *variant);
 
+/* Stream-K with a caller-owned workspace. The pages split only the tiles
+ * that would form the last, partially filled round of the compute units
+ * along K, and combine the partial sums of each such tile ("Optimizing
+ * Matrix Multiply on CUDA, Part 2", "Distributing the Partially Filled
+ * Wave"). Here: with T tiles on C compute units, floor(T/C)*C tiles are
+ * computed whole; the other T mod C tiles' K slices are dealt out in equal
+ * runs to at most min(C, 4*(T mod C)) workgroups (a tile is cut into about
+ * four pieces at most, as the pages found best). A run that covers a whole
+ * tile writes C; the others write their partial tiles to the workspace, and
+ * a second kernel on the same stream sums each split tile's pieces in K
+ * order -- so results are deterministic for a given device and shape -- and
+ * applies alpha and beta. (The pages combine the pieces in the unit that
+ * finishes a tile's last piece; on MI355X the device-scope fences that
+ * needs write back or invalidate a whole XCD's L2 per piece, which costs
+ * more than the second launch.) No workgroup waits for another.
+ *
+ * sgemm_f32_ws is sgemm_f32_ex with a workspace: the automatic choice may
+ * then also pick a stream-K kernel (SGEMM_F32_MFMA_128_SK,
+ * SGEMM_F32_MFMA_64x128_SK) when the dispatch model predicts it faster and
+ * `workspace_bytes` covers what it needs. With workspace_bytes == 0 (the
+ * workspace may then be NULL) it is sgemm_f32_ex. The workspace is device
+ * memory of at least workspace_bytes bytes, 16-byte aligned, owned by the
+ * caller; its contents on entry do not matter, and on return they are
+ * undefined. Calls that may run at the same time (different streams) need
+ * different workspaces. */
+SGEMM_F32_API int sgemm_f32_ws(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               float alpha, const float *A, int64_t lda, const float *B,
+                               int64_t ldb, float beta, float *C, int64_t ldc, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* sgemm_f32_ws with the kernel forced to `variant`. A stream-K variant given
+ * less workspace than it needs returns SGEMM_F32_ERR_WORKSPACE; on a shape
+ * that it does not split (T a multiple of C) it needs none and runs as its
+ * whole-tile kernel. Other variants ignore the workspace. sgemm_f32_variant
+ * and sgemm_f32_variant_ex pass no workspace. */
+SGEMM_F32_API int sgemm_f32_variant_ws(int variant, int layout, int transa, int transb, int64_t M,
+                                       int64_t N, int64_t K, float alpha, const float *A,
+                                       int64_t lda, const float *B, int64_t ldb, float beta,
+                                       float *C, int64_t ldc, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/* The variant sgemm_f32_ws would launch with `workspace_bytes` of workspace,
+ * as sgemm_f32_plan (host-only). */
+SGEMM_F32_API int sgemm_f32_plan_ws(int layout, int transa, int transb, int64_t M, int64_t N,
+                                    int64_t K, float alpha, const float *A, int64_t lda,
+                                    const float *B, int64_t ldb, float beta, const float *C,
+                                    int64_t ldc, size_t workspace_bytes, int num_cus,
+                                    int *variant);
+
+/* Workspace bytes that stream-K `variant` needs for this problem on a device
+ * with num_cus compute units (0 if it would not split it, or if the variant
+ * is not a stream-K kernel); with variant == -1, the most any stream-K
+ * kernel the automatic choice may consider needs, so that passing that much
+ * to sgemm_f32_ws leaves every candidate open. Host-only. Writes *bytes and
+ * returns 0, or -13/-14/-15/-1/-2/-3 for a bad layout, flag or size, -12 if
+ * bytes is NULL, SGEMM_F32_ERR_VARIANT, or SGEMM_F32_ERR_TOO_LARGE. At most
+ * 2 * num_cus partial tiles of 128 x 128 floats: 33.6 MB on 256 compute
+ * units. */
+SGEMM_F32_API int sgemm_f32_ws_size(int variant, int layout, int transa, int transb, int64_t M,
+                                    int64_t N, int64_t K, int num_cus, size_t *bytes);
+
 /* 1 if `variant` reads transposed operands (mfma_128x128, mfma_256x256,
- * mfma_64x128 and the three K-group kernels), 0 if not, or
+ * mfma_64x128, the three K-group kernels and the stream-K kernels), 0 if
+ * not, or
  * SGEMM_F32_ERR_VARIANT. */
 SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
 
@@ -220,7 +295,12 @@ SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
  *     overhead_us + 1e6 * n * 2*BM*BN*K / (614.4e9 * eff[b]),
  * n = ceil(ceil(M/BM) * ceil(N/BN) / C), b = 0, 1, 2, 3 for n = 1, 2, 3-4, >= 5
  * (614.4e9 FLOP/s is one compute unit's FP32 matrix peak). The smallest
- * prediction wins; ties go to the earlier entry. M <= 32 and tiny products
+ * prediction wins; ties go to the earlier entry. For a stream-K entry n is
+ * the busiest unit's share, floor(T/C) whole tiles plus one run of slices
+ * (a fraction of a tile), with b taken for ceil(n); stream-K entries are
+ * considered only by sgemm_f32_ws, on shapes they split, and when the
+ * workspace suffices; if no entry applies, mfma_128x128 runs. M <= 32 and
+ * tiny products
  * bypass the model (mfma_skinny, mfma_direct). A call with a transposed
  * operand (after the column-major swap) uses the model for every shape,
  * restricted to the entries that read transposed operands (mfma_128x128 if
@@ -228,7 +308,8 @@ SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
 #define SGEMM_F32_MODEL_MAX 16
 typedef struct {
     int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,
-                           MFMA_64x128_KG4, MFMA_64x96_KG4 or MFMA_128x128_KG4 */
+                           MFMA_64x128_KG4, MFMA_64x96_KG4, MFMA_128x128_KG4,
+                           MFMA_128_SK or MFMA_64x128_SK */
     double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
     double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */
 } sgemm_f32_model_entry;

@@ -50,13 +50,21 @@ def run(variant, M, N, K, alpha, beta, A, B, C0, dev, offsets=(0, 0, 0), stream=
     print(f"[gpu] {tag} variant={name} M={M} N={N} K={K} alpha={alpha} beta={beta} "
           f"ld=({lda},{ldb},{ldc}) off={offsets}", flush=True)
     s = torch.cuda.current_stream() if stream is None else stream
+    # stream-K variants get the workspace they ask for (none on shapes they
+    # do not split)
+    wsb = 0
+    if variant is not None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        wsb = sg.sgemm_f32_ws_size(variant, sg.ROW_MAJOR, 0, 0, M, N, K, cus)[1]
+    ws = torch.full((max(16, wsb),), 0xFF, dtype=torch.uint8, device=dev)
     with torch.cuda.stream(s):
         if variant is None:
             rc = sg.sgemm_f32(M, N, K, alpha, pa, lda, pb, ldb, beta, pc, ldc, s.cuda_stream)
         else:
-            rc = sg.sgemm_f32_variant(variant, M, N, K, alpha, pa, lda, pb, ldb, beta, pc, ldc,
-                                      s.cuda_stream)
+            rc = sg.sgemm_f32_variant_ws(variant, sg.ROW_MAJOR, 0, 0, M, N, K, alpha, pa, lda, pb,
+                                         ldb, beta, pc, ldc, ws, wsb, s.cuda_stream)
     torch.cuda.synchronize()
+    del ws
     C = fc[offsets[2]:].cpu().numpy().reshape(C0.shape)
     del fa, fb, fc
     return rc, C

@@ -24,7 +24,7 @@ ROW, COL = sg.ROW_MAJOR, sg.COL_MAJOR
 NT, T = sg.NO_TRANS, sg.TRANS
 COMBOS = list(itertools.product((ROW, COL), (NT, T), (NT, T)))
 TRANS_KERNELS = ["mfma_128x128", "mfma_256x256", "mfma_64x128", "mfma_64x128_kg4",
-                 "mfma_64x96_kg4", "mfma_128x128_kg4"]
+                 "mfma_64x96_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk"]
 
 
 def combo_id(c):
@@ -88,18 +88,24 @@ def run_ex(variant, layout, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets=
     fb, pb = to_dev(B.buf, dev, offsets[1])
     fc, pc = to_dev(C.buf, dev, offsets[2])
     name = "auto" if variant is None else variant
+    # stream-K kernels get the workspace they ask for
+    vid = -1 if variant is None else sg.sgemm_f32_variant_by_name(variant)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rc, wsb = sg.sgemm_f32_ws_size(vid, layout, ta, tb, M, N, K, cus)
+    assert rc == 0
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     print(f"[gpu] {tag} ex variant={name} layout={layout} ta={ta} tb={tb} M={M} N={N} K={K} "
-          f"ld=({A.ld},{B.ld},{C.ld}) off={offsets}", flush=True)
+          f"ld=({A.ld},{B.ld},{C.ld}) off={offsets} ws={wsb}", flush=True)
     s = torch.cuda.current_stream()
     if variant is None:
         rc = sg.sgemm_f32_ex(layout, ta, tb, M, N, K, alpha, pa, A.ld, pb, B.ld, beta, pc, C.ld,
                              s.cuda_stream)
     else:
-        rc = sg.sgemm_f32_variant_ex(sg.sgemm_f32_variant_by_name(variant), layout, ta, tb, M, N,
-                                     K, alpha, pa, A.ld, pb, B.ld, beta, pc, C.ld, s.cuda_stream)
+        rc = sg.sgemm_f32_variant_ws(vid, layout, ta, tb, M, N, K, alpha, pa, A.ld, pb, B.ld,
+                                     beta, pc, C.ld, ws, wsb, s.cuda_stream)
     torch.cuda.synchronize()
     out = fc[offsets[2]:].cpu().numpy().reshape(C.buf.shape)
-    del fa, fb, fc
+    del fa, fb, fc, ws
     return rc, out
 
 

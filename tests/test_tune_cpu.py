@@ -23,6 +23,13 @@ def _plan(M, N, K, cus):
     return sg.sgemm_f32_variant_name(v)
 
 
+def _plan_ws(M, N, K, cus, ws_bytes=1 << 40):
+    rc, v = sg.sgemm_f32_plan_ws(sg.ROW_MAJOR, 0, 0, M, N, K, 1.0, P, K, P, N, 0.0, P, N,
+                                 ws_bytes, cus)
+    assert rc == 0
+    return sg.sgemm_f32_variant_name(v)
+
+
 def test_builtin_model_lists_the_tile_kernels_in_order():
     m = sg.sgemm_f32_get_model()
     assert [e["variant"] for e in m] == list(tune.TILE)
@@ -45,6 +52,8 @@ def test_library_choice_matches_the_tuner_formula():
             if M <= 32 or M * N * K < 64 * 1024 * 1024:
                 continue    # skinny and tiny shapes bypass the model
             assert _plan(M, N, K, cus) == tune.choose(model, M, N, K, cus), (model, M, N, K, cus)
+            assert _plan_ws(M, N, K, cus) == tune.choose(model, M, N, K, cus, workspace=True), \
+                (model, M, N, K, cus)
 
 
 def test_model_round_trip_and_restore():
@@ -77,6 +86,71 @@ def test_model_size_limits():
     assert lib.sgemm_f32_set_model(None, 3) == -1
     assert lib.sgemm_f32_get_model(None, 4) == -1
     assert lib.sgemm_f32_get_model(None, 0) == len(tune.TILE)
+
+
+@pytest.mark.parametrize("tiles,slices,cus", [(576, 192, 256), (144, 192, 256), (300, 7, 256),
+                                              (5, 7, 256), (1, 3, 256), (256, 64, 256),
+                                              (1000, 313, 304), (3, 1, 256), (17, 1000, 80)])
+def test_sk_split_matches_the_library(tiles, slices, cus):
+    # The tuner's copy of the split is what the library's plan implies: a
+    # stream-K kernel is planned exactly when the split exists, and its
+    # busiest share is whole tiles plus at most one run of slices.
+    sp = tune.sk_split(tiles, slices, cus)
+    R = tiles % cus
+    if R == 0:
+        assert sp is None
+        return
+    dp, sk, wgs, upw = sp
+    assert dp == tiles - R and sk == R and wgs <= min(cus, 4 * R)
+    assert (wgs - 1) * upw < R * slices <= wgs * upw     # every slice in exactly one run
+    pieces = [((t + 1) * slices - 1) // upw - (t * slices) // upw + 1 for t in range(R)]
+    assert max(pieces) <= -(-wgs // R) + 1                # about four pieces at most
+
+
+def test_stream_k_is_planned_only_with_a_workspace():
+    # 3072^3: 576 tiles of 128x128 on 256 units -> 2 whole tiles each + 64
+    # split four ways; without a workspace the stream-K kernels are no
+    # candidates.
+    M = N = K = 3072
+    assert not _plan(M, N, K, 256).endswith("_sk")
+    _, need = sg.sgemm_f32_ws_size(-1, sg.ROW_MAJOR, 0, 0, M, N, K, 256)
+    assert need > 0
+    _, need128 = sg.sgemm_f32_ws_size(sg.sgemm_f32_variant_by_name("mfma_128x128_sk"),
+                                      sg.ROW_MAJOR, 0, 0, M, N, K, 256)
+    assert 0 < need128 <= need
+    # 2 partial slots of 128 x 128 floats per stream-K workgroup (256 of them)
+    assert need128 == 2 * 256 * 128 * 128 * 4
+    # a workspace one byte short of every stream-K kernel's need keeps them out
+    got = _plan_ws(M, N, K, 256, ws_bytes=1)
+    assert not got.endswith("_sk")
+    # 4096^3 splits nothing (256 tiles of 256x256, 1024 of 128x128)
+    assert sg.sgemm_f32_ws_size(-1, sg.ROW_MAJOR, 0, 0, 4096, 4096, 4096, 256) == (0, 0)
+
+
+def test_ws_size_argument_errors():
+    f = sg.sgemm_f32_ws_size
+    assert f(-2, 0, 0, 0, 8, 8, 8, 256)[0] == sg.ERR_VARIANT
+    assert f(len(sg.VARIANTS), 0, 0, 0, 8, 8, 8, 256)[0] == sg.ERR_VARIANT
+    assert f(-1, 2, 0, 0, 8, 8, 8, 256)[0] == -13
+    assert f(-1, 0, 3, 0, 8, 8, 8, 256)[0] == -14
+    assert f(-1, 0, 0, 3, 8, 8, 8, 256)[0] == -15
+    assert f(-1, 0, 0, 0, -1, 8, 8, 256)[0] == -1
+    assert f(-1, 0, 0, 0, 8, -1, 8, 256)[0] == -2
+    assert f(-1, 0, 0, 0, 8, 8, -1, 256)[0] == -3
+    assert f(-1, 0, 0, 0, 0, 8, 8, 256) == (0, 0)
+    assert sg.lib().sgemm_f32_ws_size(-1, 0, 0, 0, 8, 8, 8, 256, None) == -12
+    # a non-stream-K variant needs nothing
+    assert f(sg.sgemm_f32_variant_by_name("mfma_128x128"), 0, 0, 0, 3072, 3072, 3072, 256) == (0, 0)
+
+
+def test_workspace_argument_checks():
+    # NULL or misaligned workspace with a nonzero size: -16, before any launch
+    a = (sg.ROW_MAJOR, 0, 0, 64, 64, 64, 1.0, P, 64, P, 64, 0.0, P, 64)
+    assert sg.sgemm_f32_ws(*a, 0, 1024, stream=0) == -16
+    assert sg.sgemm_f32_ws(*a, P + 4, 1024, stream=0) == -16
+    assert sg.sgemm_f32_variant_ws(0, *a, P + 8, 1024, stream=0) == -16
+    assert "workspace" in sg.sgemm_f32_strerror(-16)
+    assert "workspace" in sg.sgemm_f32_strerror(sg.ERR_WORKSPACE)
 
 
 def test_fit_recovers_synthetic_constants():
