@@ -391,7 +391,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every variant on --workloads (one JSON line each)")
-    ap.add_argument("--workloads", default="S256,R_odd,R_skinny,S2048,S4092,S4096,S8192")
+    ap.add_argument("--workloads",
+                    default="S256,R_odd,R_skinny,S2048,S4092,S4096,S8192,S4096_M8,S8192_M8")
     ap.add_argument("--variants", default="all",
                     help="comma-separated variant names, 'all', or 'none' (automatic choice only)")
     ap.add_argument("--context", action="store_true",

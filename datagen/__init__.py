@@ -100,6 +100,14 @@ WORKLOADS = {
            "odd edges (1000,1531,777), alpha=1 beta=0, U[-1,1)"),
         _w("R_skinny", 16, 8192, 8192, 1.0, 0.0, "uniform", 1601, 1602, None,
            "skinny near-GEMV (16,8192,8192), alpha=1 beta=0, U[-1,1)"),
+        # One GPU's share of an 8-way row split (each GPU holds M/8 rows of A
+        # and C and all of B; no exchange). Same seeds as the full problem:
+        # the generator fills row by row, so A is exactly the first M/8 rows
+        # of the full A.
+        _w("S4096_M8", 512, 4096, 4096, 1.0, 0.0, "uniform", 401, 402, None,
+           "8-way row shard of S4096: (512,4096,4096), alpha=1 beta=0, U[-1,1)"),
+        _w("S8192_M8", 1024, 8192, 8192, 1.0, 0.0, "normal", 801, 802, None,
+           "8-way row shard of S8192: (1024,8192,8192), alpha=1 beta=0, N(0,1)"),
     ]
 }
 

@@ -49,18 +49,23 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> tuple:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=(), csrc: str = CSRC) -> tuple:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *CXXFLAGS, *extra, "-c", os.path.join(csrc, src), "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     return src, obj, proc.returncode, proc.stdout + proc.stderr, cmd
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 4, verbose: bool = False, extra_flags=(), out_lib: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source (with `extra_flags`, e.g. -D tile macros) into
+    build_dir and link out_lib. Returns out_lib."""
+    os.makedirs(build_dir, exist_ok=True)
     objs, remarks = [], []
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        for src, obj, rc, out, cmd in ex.map(_compile, SOURCES):
+        futs = [ex.submit(_compile, src, build_dir, tuple(extra_flags)) for src in SOURCES]
+        for fut in futs:
+            src, obj, rc, out, cmd = fut.result()
             # Host-pass warnings about the device-only target feature are noise.
             lines = [ln for ln in out.splitlines()
                      if "packed-fp32-ops' is not a recognized feature" not in ln]
@@ -72,13 +77,13 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
             if verbose and errs:
                 sys.stderr.write("\n".join(errs) + "\n")
             objs.append(obj)
-    with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
+    with open(os.path.join(build_dir, "resource_usage.txt"), "w") as f:
         f.write("\n".join(remarks) + "\n")
-    tmp = LIB + ".tmp"
+    tmp = out_lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out_lib)
+    return out_lib
 
 
 def main() -> None:

@@ -88,7 +88,7 @@ static const TileKernel kTileKernels[] = {
     {SGEMM_F32_MFMA_128, 128, 128, 0},        {SGEMM_F32_MFMA_256, 256, 256, 0},
     {SGEMM_F32_MFMA_64x128, 64, 128, 0},      {SGEMM_F32_MFMA_64, 64, 64, 0},
     {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 0},  {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 0},
-    {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 0}, {SGEMM_F32_MFMA_128_SK, 128, 128, 16},
+    {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 0}, {SGEMM_F32_MFMA_128_SK, 128, 128, 32},
     {SGEMM_F32_MFMA_64x128_SK, 64, 128, 16},
 };
 static const TileKernel* tile_kernel(int variant) {
@@ -106,15 +106,15 @@ struct Model {
 // Built-in model, listed in order of preference when predictions tie.
 static const Model kDefaultModel = {9,
                                     {
-                                        {SGEMM_F32_MFMA_128, 128, 128, 11.5, {0.822, 0.864, 0.901, 0.905}},
-                                        {SGEMM_F32_MFMA_256, 256, 256, 17.5, {0.971, 0.923, 0.936, 0.936}},
-                                        {SGEMM_F32_MFMA_64x128, 64, 128, 7.5, {0.712, 0.788, 0.820, 0.854}},
-                                        {SGEMM_F32_MFMA_64, 64, 64, 7.5, {0.525, 0.626, 0.713, 0.796}},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 10.0, {0.807, 0.782, 0.796, 0.808}},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.5, {0.754, 0.732, 0.777, 0.759}},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 14.0, {0.897, 0.860, 0.863, 0.866}},
-                                        {SGEMM_F32_MFMA_128_SK, 128, 128, 24.0, {0.756, 0.849, 0.864, 0.890}},
-                                        {SGEMM_F32_MFMA_64x128_SK, 64, 128, 14.5, {0.681, 0.737, 0.838, 0.854}},
+                                        {SGEMM_F32_MFMA_128, 128, 128, 8.5, {0.885, 0.892, 0.900, 0.907}},
+                                        {SGEMM_F32_MFMA_256, 256, 256, 18.0, {0.974, 0.934, 0.943, 0.943}},
+                                        {SGEMM_F32_MFMA_64x128, 64, 128, 7.0, {0.713, 0.780, 0.828, 0.861}},
+                                        {SGEMM_F32_MFMA_64, 64, 64, 7.0, {0.512, 0.630, 0.717, 0.794}},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 9.0, {0.800, 0.787, 0.794, 0.809}},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 8.5, {0.745, 0.731, 0.774, 0.762}},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 11.0, {0.891, 0.865, 0.863, 0.869}},
+                                        {SGEMM_F32_MFMA_128_SK, 128, 128, 17.0, {0.798, 0.886, 0.889, 0.895}},
+                                        {SGEMM_F32_MFMA_64x128_SK, 64, 128, 15.0, {0.681, 0.746, 0.845, 0.856}},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a

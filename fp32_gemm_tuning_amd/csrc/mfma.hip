@@ -297,12 +297,16 @@ struct SubstepMma {
 // buffer-to-LDS loads of slice s+1 are in flight while slice s is
 // multiplied; one barrier per slice.
 //
-// mfma_128x128 is BM = BN = 128 with 4 waves of 64x64 (64 accumulator
-// registers per lane), BK = 16, and an occupancy target of 4 waves per SIMD
-// (4 workgroups per compute unit, accumulators in the unified VGPR file).
+// mfma_128x128 is BM = BN = 128 with 8 waves of 64x32 (32 accumulator
+// registers per lane), BK = 32, and an occupancy target of 4 waves per SIMD
+// (2 workgroups per compute unit); mfma_64x128 is 64x128 with 4 waves of
+// 64x32 and BK = 16. Both were chosen by sweeping block tile, wave tile,
+// BK and occupancy on MI355X (fp32_gemm_tuning_amd/autotune.py): against
+// the 4-waves-of-64x64, BK = 16 layout they gain 1-9% at 2048^3 to 8192^2 x
+// 1024 and lose nothing on the other shapes measured.
 // ===========================================================================
 #ifndef SGEMM_M128_BK
-#define SGEMM_M128_BK 16
+#define SGEMM_M128_BK 32
 #endif
 #ifndef SGEMM_M128_WAVES_PER_EU
 #define SGEMM_M128_WAVES_PER_EU 4
@@ -317,10 +321,19 @@ struct SubstepMma {
 #define SGEMM_M128_WM 64
 #endif
 #ifndef SGEMM_M128_WN
-#define SGEMM_M128_WN 64
+#define SGEMM_M128_WN 32
 #endif
 #ifndef SGEMM_M128_GROUP_M
 #define SGEMM_M128_GROUP_M 8
+#endif
+#ifndef SGEMM_M64x128_WM
+#define SGEMM_M64x128_WM 64
+#endif
+#ifndef SGEMM_M64x128_WN
+#define SGEMM_M64x128_WN 32
+#endif
+#ifndef SGEMM_M64x128_BK
+#define SGEMM_M64x128_BK 16
 #endif
 constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
 constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
@@ -331,6 +344,9 @@ constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = S
 // barrier and no load into them is outstanding.
 template <int BM, int BN, int WM, int WN, int BK, bool VEC, bool TA, bool TB>
 struct TileCore {
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0,
+                  "wave tiles are whole 32x32 blocks that divide the block tile");
+    static_assert((BM / WM) * (BN / WN) * 64 <= 1024, "at most 16 waves per workgroup");
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NT = (BM / WM) * WAVES_N * 64;
     static constexpr int BI = WM / 32, BJ = WN / 32;
@@ -599,6 +615,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     static_assert(BK == 16 || BK == 32, "slices of 16 or 32 k");
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0,
+                  "wave tiles are whole 32x32 blocks that divide the block tile");
+    static_assert((BM / WM) * (BN / WN) * 64 <= 1024, "at most 16 waves per workgroup");
     constexpr int P = BK / 8;   // parts of 4 MFMA k-steps per slice
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
@@ -787,7 +806,7 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 
 // ===========================================================================
 // mfma_64x128_kg4: a 64x128 tile computed by 16 waves in four K-groups of
-// four (each wave 32x64, as in mfma_64x128). Group g multiplies the slices
+// four (each wave 32x64). Group g multiplies the slices
 // g, g+4, g+8, ... from its own two LDS stages, so a compute unit holds 16
 // waves of one tile instead of 4, and a shape with fewer tiles than compute
 // units (the odd 1000x1531x777 has 192) still keeps four waves on every
@@ -967,16 +986,19 @@ static hipError_t with_trans(const Args& a, F&& f) {
 // Launch helpers for instances of k_mfma_tile. The 4-byte-fill instance keeps
 // more loads in flight per lane; at 4 waves per SIMD it would spill, so it
 // targets 3.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK>
 struct TileInstance {
     static constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    // Occupancy of the 4-byte-fill instance: 3 waves per SIMD, or as many
+    // as one workgroup puts on each SIMD if that is more.
+    static constexpr int WPE4 = NT / 256 > 3 ? NT / 256 : 3;
     template <bool VEC>
     static const void* kernel() {
-        return (const void*)k_mfma_tile<BM, BN, WM, WN, M128_BK,
-                                         VEC ? SGEMM_M128_WAVES_PER_EU : 3, VEC>;
+        return (const void*)k_mfma_tile<BM, BN, WM, WN, BK,
+                                         VEC ? SGEMM_M128_WAVES_PER_EU : WPE4, VEC>;
     }
     static int check(const Args& a) {
-        if (!extents_ok(a, BM, BN, M128_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+        if (!extents_ok(a, BM, BN, BK)) return SGEMM_F32_ERR_TOO_LARGE;
         const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
         return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
     }
@@ -987,27 +1009,27 @@ struct TileInstance {
         return with_trans(a, [&](auto ta, auto tb) {
             constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
             if (vec)
-                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU, true,
+                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, BK, SGEMM_M128_WAVES_PER_EU, true,
                                                 TA, TB>),
                                    grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
             else
-                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, M128_BK, 3, false, TA, TB>), grid,
+                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, BK, WPE4, false, TA, TB>), grid,
                                    block, 0, s, a, tm, tn, xcd_remap_enabled());
             return hipGetLastError();
         });
     }
 };
 
-using Tile128 = TileInstance<M128_BM, M128_BN, M128_WM, M128_WN>;
-using Tile64x128 = TileInstance<64, 128, 32, 64>;
+using Tile128 = TileInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK>;
+using Tile64x128 = TileInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK>;
 
 // Stream-K launch of a TileInstance tile: one workgroup per whole tile plus
 // the stream-K workgroups, then the fixup kernel on the same stream.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK>
 struct TileSkInstance {
-    using Base = TileInstance<BM, BN, WM, WN>;
+    using Base = TileInstance<BM, BN, WM, WN, BK>;
     static SkSplit split(const Args& a, int cus) {
-        return sk_split(cdiv(a.M, BM) * cdiv(a.N, BN), cdiv(a.K, M128_BK), cus);
+        return sk_split(cdiv(a.M, BM) * cdiv(a.N, BN), cdiv(a.K, BK), cus);
     }
     static size_t ws_size(const Args& a, int cus) { return sk_workspace_bytes(split(a, cus), BM, BN); }
     static hipError_t launch_ws(const Args& a, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
@@ -1027,11 +1049,11 @@ struct TileSkInstance {
         const hipError_t e = with_trans(a, [&](auto ta, auto tb) {
             constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
             if (vec)
-                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU,
+                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, BK, SGEMM_M128_WAVES_PER_EU,
                                                    true, TA, TB>),
                                    grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
             else
-                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, M128_BK, 3, false, TA, TB>), grid,
+                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, BK, Base::WPE4, false, TA, TB>), grid,
                                    block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
             return hipGetLastError();
         });
@@ -1042,11 +1064,12 @@ struct TileSkInstance {
         return hipGetLastError();
     }
     static const void* kernel() {
-        return (const void*)k_mfma_tile_sk<BM, BN, WM, WN, M128_BK, SGEMM_M128_WAVES_PER_EU, true>;
+        return (const void*)k_mfma_tile_sk<BM, BN, WM, WN, BK, SGEMM_M128_WAVES_PER_EU, true>;
     }
 };
-using Tile128Sk = TileSkInstance<M128_BM, M128_BN, M128_WM, M128_WN>;
-using Tile64x128Sk = TileSkInstance<64, 128, 32, 64>;
+using Tile128Sk = TileSkInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK>;
+using Tile64x128Sk =
+    TileSkInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK>;
 
 static int check_mfma128(const Args& a) { return Tile128::check(a); }
 static hipError_t launch_mfma128(const Args& a, hipStream_t s) { return Tile128::launch(a, s); }
@@ -1062,7 +1085,7 @@ Variant kMfma128Sk = {"mfma_128x128_sk", check_mfma128, nullptr, Tile128Sk::kern
                       true, Tile128Sk::ws_size, Tile128Sk::launch_ws};
 Variant kMfma64x128Sk = {"mfma_64x128_sk", check_mfma64x128, nullptr, Tile64x128Sk::kernel(),
                          Tile64x128::NT, true, Tile64x128Sk::ws_size, Tile64x128Sk::launch_ws};
-// 64x128 tile, 4 waves of 32x64: twice the tiles of mfma_128x128 for
+// 64x128 tile, 4 waves of 64x32: twice the tiles of mfma_128x128 for
 // medium shapes (e.g. 2048^3, where 256 tiles of 128x128 leave one
 // workgroup per compute unit).
 Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,

@@ -101,8 +101,9 @@ enum sgemm_f32_variant_id {
        conflict-free transposed A tile (Part 2 of "Optimizing Matrix
        Multiply on CUDA") */
     SGEMM_F32_VALU_MAIN = 6,
-    /* FP32 matrix-core kernel, 128x128 block tile (v_mfma_f32_32x32x2_f32),
-       LDS filled by buffer-to-LDS loads */
+    /* FP32 matrix-core kernel, 128x128 block tile of 8 waves of 64x32
+       (v_mfma_f32_32x32x2_f32), 32-deep K slices, LDS filled by
+       buffer-to-LDS loads */
     SGEMM_F32_MFMA_128 = 7,
     /* FP32 matrix-core kernel, 64x64 block tile for shapes with few 128x128
        tiles (v_mfma_f32_16x16x4_f32) */
@@ -119,7 +120,7 @@ enum sgemm_f32_variant_id {
        registers (no LDS tile, no barrier in the K loop), fixed-order
        reduction at the end */
     SGEMM_F32_MFMA_DIRECT = 11,
-    /* FP32 matrix-core kernel, 64x128 block tile (4 waves of 32x64,
+    /* FP32 matrix-core kernel, 64x128 block tile (4 waves of 64x32,
        v_mfma_f32_32x32x2_f32): twice the tiles of mfma_128x128 for medium
        shapes */
     SGEMM_F32_MFMA_64x128 = 12,

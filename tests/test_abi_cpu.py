@@ -102,7 +102,7 @@ def _plan(M, N, K, lda=None, ldb=None, ldc=None, cus=256, off=0):
 def test_plan_picks_matrix_core_kernels_for_the_workloads():
     w = WORKLOADS
     assert _plan(4096, 4096, 4096) == "mfma_256x256"
-    assert _plan(w["S2048"].M, w["S2048"].N, w["S2048"].K) == "mfma_128x128_kg4"
+    assert _plan(w["S2048"].M, w["S2048"].N, w["S2048"].K) == "mfma_128x128"
     assert _plan(w["S8192"].M, w["S8192"].N, w["S8192"].K) == "mfma_256x256"
     assert _plan(w["S4092"].M, w["S4092"].N, w["S4092"].K) == "mfma_256x256"
     # 1000 x 1531 is exactly 256 tiles of 64x96: one 12-wave K-split tile per CU
@@ -115,9 +115,9 @@ def test_plan_busiest_cu_rule():
     # 4096^2: one 256^2 tile per CU (16 waves of one workgroup) beats four
     # 128^2 tiles, eight 64x128 or sixteen 64^2 tiles.
     assert _plan(4096, 4096, 4096, cus=256) == "mfma_256x256"
-    # 2048^2: 64 tiles of 256^2 would leave 192 CUs idle; one 128^2 tile each,
-    # computed by 16 waves in four K-groups.
-    assert _plan(2048, 2048, 2048, cus=256) == "mfma_128x128_kg4"
+    # 2048^2: 64 tiles of 256^2 would leave 192 CUs idle; one 128^2 tile each
+    # (8 waves of 64x32, 32-deep slices).
+    assert _plan(2048, 2048, 2048, cus=256) == "mfma_128x128"
     # 4096 x 2048: 128 tiles of 256^2 (half the CUs) lose to two 128^2 per CU.
     assert _plan(4096, 2048, 4096, cus=256) == "mfma_128x128"
     # 1024x1536: 96 tiles of 128^2 keep 160 CUs idle; 256 tiles of 64x96 do not.

@@ -203,7 +203,7 @@ FULL_CHECK = {"S256", "S2048", "R_odd", "R_skinny"}
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
 @pytest.mark.parametrize("name", ["S256", "R_odd", "R_skinny", "S2048", "S4092", "S4096",
-                                  "S8192"])
+                                  "S8192", "S4096_M8", "S8192_M8"])
 def test_workloads(dev, name, integer):
     w = WORKLOADS[name]
     if integer:
