@@ -87,7 +87,9 @@ def cpu_baseline(w, A, B, C0, budget_s: float = 12.0):
 
 def measured_peaks(dev, stream, cus: int) -> dict:
     """TFLOP/s of the library's peak-rate probes (unpacked FP32 FMA and both
-    FP32 MFMA shapes), each timed with HIP events on the launch stream."""
+    FP32 MFMA shapes), each timed with HIP events on the launch stream; the
+    best of 10 launches (the clock moves between launches of a pure-MFMA
+    loop, which draws more power than the GEMM)."""
     import torch
 
     import fp32_gemm_tuning_amd as sg
@@ -97,7 +99,7 @@ def measured_peaks(dev, stream, cus: int) -> dict:
     for kind, name, iters in ((0, "valu_fma_f32", 4096), (1, "mfma_f32_32x32x2", 512),
                               (2, "mfma_f32_16x16x4", 512)):
         best = 0.0
-        for _ in range(3):
+        for _ in range(10):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             rc, flops = sg.sgemm_f32_peak_probe(kind, wgs, iters, out, stream.cuda_stream)
