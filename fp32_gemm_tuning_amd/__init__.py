@@ -58,7 +58,8 @@ NO_TRANS, TRANS = 0, 1
 VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", "valu_main",
             "mfma_128x128", "mfma_64x64", "mfma_skinny", "mfma_64x64_k4", "mfma_direct",
             "mfma_64x128", "mfma_256x256", "mfma_64x128_kg4",
-            "mfma_64x96_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk")
+            "mfma_64x96_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
+            "mfma_256x256_sk")
 
 
 class SgemmError(RuntimeError):

@@ -17,6 +17,7 @@ static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
     &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
     &kMfma256, &kMfmaKgroup, &kMfmaKgroup96, &kMfmaKgroup128, &kMfma128Sk, &kMfma64x128Sk,
+    &kMfma256Sk,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
@@ -89,7 +90,7 @@ static const TileKernel kTileKernels[] = {
     {SGEMM_F32_MFMA_64x128, 64, 128, 0},      {SGEMM_F32_MFMA_64, 64, 64, 0},
     {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 0},  {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 0},
     {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 0}, {SGEMM_F32_MFMA_128_SK, 128, 128, 32},
-    {SGEMM_F32_MFMA_64x128_SK, 64, 128, 16},
+    {SGEMM_F32_MFMA_64x128_SK, 64, 128, 16}, {SGEMM_F32_MFMA_256_SK, 256, 256, 16},
 };
 static const TileKernel* tile_kernel(int variant) {
     for (const TileKernel& k : kTileKernels)
@@ -104,17 +105,18 @@ struct Model {
 };
 
 // Built-in model, listed in order of preference when predictions tie.
-static const Model kDefaultModel = {9,
+static const Model kDefaultModel = {10,
                                     {
-                                        {SGEMM_F32_MFMA_128, 128, 128, 8.5, {0.885, 0.892, 0.900, 0.907}},
-                                        {SGEMM_F32_MFMA_256, 256, 256, 18.0, {0.974, 0.934, 0.943, 0.943}},
-                                        {SGEMM_F32_MFMA_64x128, 64, 128, 7.0, {0.713, 0.780, 0.828, 0.861}},
-                                        {SGEMM_F32_MFMA_64, 64, 64, 7.0, {0.512, 0.630, 0.717, 0.794}},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 9.0, {0.800, 0.787, 0.794, 0.809}},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 8.5, {0.745, 0.731, 0.774, 0.762}},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 11.0, {0.891, 0.865, 0.863, 0.869}},
-                                        {SGEMM_F32_MFMA_128_SK, 128, 128, 17.0, {0.798, 0.886, 0.889, 0.895}},
-                                        {SGEMM_F32_MFMA_64x128_SK, 64, 128, 15.0, {0.681, 0.746, 0.845, 0.856}},
+                                        {SGEMM_F32_MFMA_128, 128, 128, 11.5, {0.897, 0.902, 0.903, 0.905}},
+                                        {SGEMM_F32_MFMA_256, 256, 256, 20.0, {0.977, 0.929, 0.943, 0.943}},
+                                        {SGEMM_F32_MFMA_64x128, 64, 128, 6.0, {0.692, 0.796, 0.816, 0.855}},
+                                        {SGEMM_F32_MFMA_64, 64, 64, 6.0, {0.485, 0.617, 0.701, 0.792}},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 8.5, {0.784, 0.776, 0.794, 0.808}},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.0, {0.746, 0.727, 0.754, 0.763}},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 12.0, {0.884, 0.866, 0.864, 0.873}},
+                                        {SGEMM_F32_MFMA_128_SK, 128, 128, 17.5, {0.801, 0.885, 0.891, 0.891}},
+                                        {SGEMM_F32_MFMA_64x128_SK, 64, 128, 15.0, {0.680, 0.737, 0.841, 0.855}},
+                                        {SGEMM_F32_MFMA_256_SK, 256, 256, 28.5, {0.904, 0.898, 0.929, 0.929}},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a

@@ -609,199 +609,289 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
-          bool TA = false, bool TB = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+// The body of k_mfma_pipe, shared with its stream-K form: the product of
+// slices [s_begin, s_end) of one tile through the LDS ring, and the
+// epilogue. On return every load issued into the ring has landed and every
+// wave has passed the last barrier, so the ring may be refilled.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool VEC, bool FULL, bool TA,
+          bool TB>
+struct PipeCore {
     static_assert(BK == 16 || BK == 32, "slices of 16 or 32 k");
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0,
                   "wave tiles are whole 32x32 blocks that divide the block tile");
     static_assert((BM / WM) * (BN / WN) * 64 <= 1024, "at most 16 waves per workgroup");
-    constexpr int P = BK / 8;   // parts of 4 MFMA k-steps per slice
-    constexpr int WAVES_N = BN / WN;
-    constexpr int NT = (BM / WM) * WAVES_N * 64;
-    constexpr int BI = WM / 32, BJ = WN / 32;
+    static constexpr int P = BK / 8;   // parts of 4 MFMA k-steps per slice
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NT = (BM / WM) * WAVES_N * 64;
+    static constexpr int BI = WM / 32, BJ = WN / 32;
     using Dma = TileFillDma<BM, BN, BK, NT, VEC, TA, TB>;
-    constexpr int BNP = Dma::BNP, APITCH = BK;
+    static constexpr int BNP = Dma::BNP, APITCH = BK;
     // Deeper rings count outstanding loads, which must then be the same on
     // every wave; with two stages the barrier waits for all of them.
     static_assert(Dma::EVEN || STAGES == 2, "the ring barrier counts the same loads on every wave");
-    constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
+    static constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert((STAGES - 2) * G < 64, "outstanding loads exceed vmcnt");
     // The prologue leaves the later stages' loads in flight only when every
     // wave issues the same G loads per slice (G is the largest per-wave
     // count; a wave that issues fewer must wait for all of its own) and the
     // count fits the 6-bit field.
-    constexpr int PROLOGUE_VMCNT = (Dma::EVEN && (STAGES - 1) * G < 64) ? (STAGES - 1) * G : 0;
+    static constexpr int PROLOGUE_VMCNT = (Dma::EVEN && (STAGES - 1) * G < 64) ? (STAGES - 1) * G : 0;
+    static constexpr int LDS_A = BM * APITCH, LDS_B = BK * BNP;
+
+    int m0, n0, rows_valid, cols_valid, t, wm, wn, h, c;
+
+    __device__ __forceinline__ PipeCore(const Args& a, int tm, int tn, int tid = threadIdx.x) {
+        // The tile coordinates are workgroup-uniform; the integer divisions
+        // of the tile mapping leave them in vector registers, and a buffer
+        // resource built from a vector register costs a per-lane loop around
+        // every load, so move them to scalar registers explicitly.
+        m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+        n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+        rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+        cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+        t = tid;
+        const int lane = t & 63, w = t >> 6;
+        wm = w / WAVES_N;
+        wn = w % WAVES_N;
+        h = lane >> 5;
+        c = lane & 31;
+    }
+
+    __device__ __forceinline__ static void zero(f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    }
+
+    __device__ __forceinline__ void mainloop(const Args& a, int s_begin, int s_end,
+                                             float* const (&Ast)[4], float* const (&Bst)[4],
+                                             f32x16 (&acc)[BI][BJ]) const {
+        // Lanes 0-31 take k = s and lanes 32-63 take k = BK/2 + s at MFMA step s
+        // of the slice; part v covers steps 4v .. 4v+3, i.e. 16-byte chunk
+        // P*h + v of a k-contiguous row ([row][k], swizzled: A, or B stored
+        // transposed) and rows BK/2*h + 4v .. BK/2*h + 4v + 3 of a row-contiguous
+        // stage ([k][row]: B, or A stored transposed). A chunk address of part v
+        // is xrow + ((xchunk ^ v) << 2), computed per read (one XOR and one
+        // shift-or, hidden under the MFMAs) rather than held in P registers per
+        // block.
+        int arow[BI], achunk[BI], brow[BJ], bchunk[BJ];
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi) {
+            const int row = wm * WM + bi * 32 + c;
+            arow[bi] = TA ? (BK / 2) * h * BM + row : row * APITCH;
+            achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
+        }
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj) {
+            const int col = wn * WN + bj * 32 + c;
+            brow[bj] = TB ? col * BK : (BK / 2) * h * BNP + col;
+            bchunk[bj] = (P * h) ^ swz_chunk<BK>(col);
+        }
+
+        auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi) {
+                if constexpr (TA) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) f.a[bi][k] = Ac[arow[bi] + (4 * v + k) * BM];
+                } else {
+                    f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
+                }
+            }
+            if constexpr (TB) {
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj) {
+                    const f32x4 q = *(const f32x4*)&Bc[brow[bj] + ((bchunk[bj] ^ v) << 2)];
+                    f.b[bj][0] = q.x; f.b[bj][1] = q.y; f.b[bj][2] = q.z; f.b[bj][3] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[brow[bj] + (4 * v + k) * BNP];
+            }
+        };
+        auto mma_part = [&](const PartFrag<BI, BJ>& f, int k_begin = 0, int k_end = 4) {
+#pragma unroll
+            for (int k = k_begin; k < k_end; ++k)
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[bi][k], f.b[bj][k],
+                                                                           acc[bi][bj], 0, 0, 0);
+        };
+
+        const Dma dma;
+        PartFrag<BI, BJ> f0, f1;
+        // Prologue: fill every stage (stages past the last slice read zeros),
+        // wait for slice 0, read its first half. Every slice below issues exactly
+        // G loads per wave, whether or not its target slice exists, so the count
+        // of loads issued after any given one is the same on every path.
+#pragma unroll
+        for (int j = 0; j < STAGES; ++j)
+            dma.template issue<FULL>(a, t, m0, n0, (s_begin + j) * BK, rows_valid, cols_valid, Ast[j],
+                                     Bst[j]);
+        ring_barrier<PROLOGUE_VMCNT>();
+        read_part(f0, Ast[0], Bst[0], 0);
+
+        // Slice s lives in stage (Ac, Bc), slice s + 1 in (An, Bn); on entry f0
+        // holds (or is loading) part 0 of slice s; parts alternate between f0
+        // and f1 (P is even, so the last part is in f1). The barrier comes after
+        // the reads of the last part and before its MFMAs; at the barrier the
+        // loads of slices s + 2 .. s + STAGES - 1 may still be in flight.
+        // Scheduling fences pin the order: each half's fragment reads issue
+        // before the other half's MFMAs, and no MFMA moves across a barrier or
+        // into a neighbouring half (the scheduler would otherwise hoist the
+        // barrier, with its wait on the reads just issued, above the MFMAs, or
+        // pull MFMAs up next to the reads they depend on).
+        auto slice = [&](int s, float* Ac, float* Bc, const float* An, const float* Bn) {
+#pragma unroll
+            for (int v = 0; v + 1 < P; ++v) {
+                if (v & 1)
+                    read_part(f0, Ac, Bc, v + 1);
+                else
+                    read_part(f1, Ac, Bc, v + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (v & 1)
+                    mma_part(f1);
+                else
+                    mma_part(f0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            ring_barrier<(STAGES - 2) * G>();
+            read_part(f0, An, Bn, 0);   // past the last slice: read and unused
+            // The matrix cores restart on the last part's first two k-steps
+            // before the wave spends issue slots on the loads (about 1% faster
+            // than issuing the loads first).
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(f1, 0, 2);
+            __builtin_amdgcn_sched_barrier(0);
+            dma.template issue<FULL>(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_part(f1, 2, 4);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // Whole rounds of STAGES slices, free of conditionals, then the rest.
+        int s0 = s_begin;
+        for (; s0 + STAGES <= s_end; s0 += STAGES) {
+#pragma unroll
+            for (int j = 0; j < STAGES; ++j)
+                slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+        }
+#pragma unroll
+        for (int j = 0; j < STAGES - 1; ++j)
+            if (s0 + j < s_end)
+                slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+        // The zero-filling loads issued for slices past the end must land before
+        // the workgroup's LDS can be handed to another workgroup.
+        ring_barrier<0>();
+
+    }
+
+    __device__ __forceinline__ void store(const Args& a, const f32x16 (&acc)[BI][BJ]) const {
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int j = wn * WN + bj * 32 + c;
+                    if (i < rows_valid && j < cols_valid)
+                        store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+                }
+    }
+};
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
+          bool TA = false, bool TB = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB>;
     // One LDS object per stage, so that the compiler can tell the stage being
     // filled from the stages being read (unused stages are dropped).
-    __shared__ __attribute__((aligned(16))) float As0[BM * APITCH];
-    __shared__ __attribute__((aligned(16))) float Bs0[BK * BNP];
-    __shared__ __attribute__((aligned(16))) float As1[BM * APITCH];
-    __shared__ __attribute__((aligned(16))) float Bs1[BK * BNP];
-    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? BM * APITCH : 4];
-    __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? BK * BNP : 4];
-    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? BM * APITCH : 4];
-    __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? BK * BNP : 4];
+    __shared__ __attribute__((aligned(16))) float As0[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs0[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As1[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs1[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? Core::LDS_B : 4];
+    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? Core::LDS_B : 4];
     float* const Ast[4] = {As0, As1, As2, As3};
     float* const Bst[4] = {Bs0, Bs1, Bs2, Bs3};
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
-    // The tile coordinates are workgroup-uniform; the integer divisions of
-    // the tile mapping leave them in vector registers, and a buffer resource
-    // built from a vector register costs a per-lane loop around every load,
-    // so move them to scalar registers explicitly.
-    const int m0 = __builtin_amdgcn_readfirstlane(tm * BM);
-    const int n0 = __builtin_amdgcn_readfirstlane(tn * BN);
-    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
-    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w / WAVES_N, wn = w % WAVES_N;
-    const int h = lane >> 5, c = lane & 31;
+    const Core core(a, tm, tn);
+    f32x16 acc[Core::BI][Core::BJ];
+    Core::zero(acc);
+    core.mainloop(a, 0, (a.K + BK - 1) / BK, Ast, Bst, acc);
+    core.store(a, acc);
+}
 
-    f32x16 acc[BI][BJ];
-#pragma unroll
-    for (int i = 0; i < BI; ++i)
-#pragma unroll
-        for (int j = 0; j < BJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+// Stream-K form of k_mfma_pipe (SkPlan in common.hpp): workgroups below
+// p.dp_tiles compute whole tiles; the others their runs of slices, a run
+// covering a whole tile writing C, the others their partial tiles (summed by
+// k_sk_fixup).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
+          bool TA = false, bool TB = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
+    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB>;
+    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
+    __shared__ __attribute__((aligned(16))) float As0[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs0[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As1[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs1[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? Core::LDS_B : 4];
+    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? Core::LDS_B : 4];
+    float* const Ast[4] = {As0, As1, As2, As3};
+    float* const Bst[4] = {Bs0, Bs1, Bs2, Bs3};
 
-    // Lanes 0-31 take k = s and lanes 32-63 take k = BK/2 + s at MFMA step s
-    // of the slice; part v covers steps 4v .. 4v+3, i.e. 16-byte chunk
-    // P*h + v of a k-contiguous row ([row][k], swizzled: A, or B stored
-    // transposed) and rows BK/2*h + 4v .. BK/2*h + 4v + 3 of a row-contiguous
-    // stage ([k][row]: B, or A stored transposed). A chunk address of part v
-    // is xrow + ((xchunk ^ v) << 2), computed per read (one XOR and one
-    // shift-or, hidden under the MFMAs) rather than held in P registers per
-    // block.
-    int arow[BI], achunk[BI], brow[BJ], bchunk[BJ];
-#pragma unroll
-    for (int bi = 0; bi < BI; ++bi) {
-        const int row = wm * WM + bi * 32 + c;
-        arow[bi] = TA ? (BK / 2) * h * BM + row : row * APITCH;
-        achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
+    const int b = blockIdx.x;
+    f32x16 acc[Core::BI][Core::BJ];
+    int tm, tn;
+    if (b < p.dp_tiles) {
+        tile_of_first(b, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+        const Core core(a, tm, tn);
+        Core::zero(acc);
+        core.mainloop(a, 0, p.slices, Ast, Bst, acc);
+        core.store(a, acc);
+        return;
     }
-#pragma unroll
-    for (int bj = 0; bj < BJ; ++bj) {
-        const int col = wn * WN + bj * 32 + c;
-        brow[bj] = TB ? col * BK : (BK / 2) * h * BNP + col;
-        bchunk[bj] = (P * h) ^ swz_chunk<BK>(col);
+    const int j = b - p.dp_tiles;
+    const int U = p.sk_tiles * p.slices;
+    int u = j * p.upw;
+    const int u_end = (u + p.upw) < U ? (u + p.upw) : U;
+    while (u < u_end) {
+        const int st = u / p.slices;
+        const int s0 = u - st * p.slices;
+        const int s1 = (s0 + (u_end - u)) < p.slices ? (s0 + (u_end - u)) : p.slices;
+        tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M,
+                      xcd_remap != 0, tm, tn);
+        // Per-lane offsets recomputed per run rather than hoisted (and
+        // spilled), as in k_mfma_tile_sk.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const Core core(a, tm, tn, tid);
+        Core::zero(acc);
+        core.mainloop(a, s0, s1, Ast, Bst, acc);
+        if (s0 == 0 && s1 == p.slices)
+            core.store(a, acc);
+        else
+            Io::put(p.partials + (size_t)sk_slot(p, j, st) * BM * BN, core.t, acc);
+        u += s1 - s0;
     }
-
-    auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
-#pragma unroll
-        for (int bi = 0; bi < BI; ++bi) {
-            if constexpr (TA) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) f.a[bi][k] = Ac[arow[bi] + (4 * v + k) * BM];
-            } else {
-                f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
-            }
-        }
-        if constexpr (TB) {
-#pragma unroll
-            for (int bj = 0; bj < BJ; ++bj) {
-                const f32x4 q = *(const f32x4*)&Bc[brow[bj] + ((bchunk[bj] ^ v) << 2)];
-                f.b[bj][0] = q.x; f.b[bj][1] = q.y; f.b[bj][2] = q.z; f.b[bj][3] = q.w;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[brow[bj] + (4 * v + k) * BNP];
-        }
-    };
-    auto mma_part = [&](const PartFrag<BI, BJ>& f, int k_begin = 0, int k_end = 4) {
-#pragma unroll
-        for (int k = k_begin; k < k_end; ++k)
-#pragma unroll
-            for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < BJ; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[bi][k], f.b[bj][k],
-                                                                       acc[bi][bj], 0, 0, 0);
-    };
-
-    const int nslices = (a.K + BK - 1) / BK;
-    const Dma dma;
-    PartFrag<BI, BJ> f0, f1;
-    // Prologue: fill every stage (stages past the last slice read zeros),
-    // wait for slice 0, read its first half. Every slice below issues exactly
-    // G loads per wave, whether or not its target slice exists, so the count
-    // of loads issued after any given one is the same on every path.
-#pragma unroll
-    for (int j = 0; j < STAGES; ++j)
-        dma.template issue<FULL>(a, t, m0, n0, j * BK, rows_valid, cols_valid, Ast[j], Bst[j]);
-    ring_barrier<PROLOGUE_VMCNT>();
-    read_part(f0, Ast[0], Bst[0], 0);
-
-    // Slice s lives in stage (Ac, Bc), slice s + 1 in (An, Bn); on entry f0
-    // holds (or is loading) part 0 of slice s; parts alternate between f0
-    // and f1 (P is even, so the last part is in f1). The barrier comes after
-    // the reads of the last part and before its MFMAs; at the barrier the
-    // loads of slices s + 2 .. s + STAGES - 1 may still be in flight.
-    // Scheduling fences pin the order: each half's fragment reads issue
-    // before the other half's MFMAs, and no MFMA moves across a barrier or
-    // into a neighbouring half (the scheduler would otherwise hoist the
-    // barrier, with its wait on the reads just issued, above the MFMAs, or
-    // pull MFMAs up next to the reads they depend on).
-    auto slice = [&](int s, float* Ac, float* Bc, const float* An, const float* Bn) {
-#pragma unroll
-        for (int v = 0; v + 1 < P; ++v) {
-            if (v & 1)
-                read_part(f0, Ac, Bc, v + 1);
-            else
-                read_part(f1, Ac, Bc, v + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (v & 1)
-                mma_part(f1);
-            else
-                mma_part(f0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        ring_barrier<(STAGES - 2) * G>();
-        read_part(f0, An, Bn, 0);   // past the last slice: read and unused
-        // The matrix cores restart on the last part's first two k-steps
-        // before the wave spends issue slots on the loads (about 1% faster
-        // than issuing the loads first).
-        __builtin_amdgcn_sched_barrier(0);
-        mma_part(f1, 0, 2);
-        __builtin_amdgcn_sched_barrier(0);
-        dma.template issue<FULL>(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_part(f1, 2, 4);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // Whole rounds of STAGES slices, free of conditionals, then the rest.
-    int s0 = 0;
-    for (; s0 + STAGES <= nslices; s0 += STAGES) {
-#pragma unroll
-        for (int j = 0; j < STAGES; ++j)
-            slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
-    }
-#pragma unroll
-    for (int j = 0; j < STAGES - 1; ++j)
-        if (s0 + j < nslices)
-            slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
-    // The zero-filling loads issued for slices past the end must land before
-    // the workgroup's LDS can be handed to another workgroup.
-    ring_barrier<0>();
-
-#pragma unroll
-    for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < BJ; ++bj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int j = wn * WN + bj * 32 + c;
-                if (i < rows_valid && j < cols_valid)
-                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
-            }
 }
 
 // ===========================================================================
@@ -1160,6 +1250,58 @@ static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
 
 Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT,
                     true};
+
+// Stream-K form of mfma_256x256: one workgroup per compute unit, so a round
+// of whole tiles is one tile per unit; the remaining tiles' slices are split
+// (sk_split) and summed by k_sk_fixup.
+static SkSplit split_mfma256(const Args& a, int cus) {
+    return sk_split(cdiv(a.M, M256_BM) * cdiv(a.N, M256_BN), cdiv(a.K, M256_BK), cus);
+}
+static size_t ws_mfma256(const Args& a, int cus) {
+    return sk_workspace_bytes(split_mfma256(a, cus), M256_BM, M256_BN);
+}
+static hipError_t launch_ws_mfma256(const Args& a, void* ws, size_t ws_bytes, int cus,
+                                    hipStream_t s) {
+    const SkSplit sp = split_mfma256(a, cus);
+    if (!sp.split()) return launch_mfma256(a, s);
+    if (ws == nullptr || ws_bytes < sk_workspace_bytes(sp, M256_BM, M256_BN))
+        return hipErrorInvalidValue;
+    SkPlan p;
+    p.dp_tiles = (int)sp.dp_tiles;
+    p.sk_tiles = (int)sp.sk_tiles;
+    p.sk_wgs = (int)sp.sk_wgs;
+    p.upw = (int)sp.upw;
+    p.slices = (int)sp.slices;
+    p.partials = (float*)ws;
+    const int tm = (int)cdiv(a.M, M256_BM), tn = (int)cdiv(a.N, M256_BN);
+    const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(M256_NT);
+    const bool full = a.M % M256_BM == 0 && a.N % M256_BN == 0 && a.K % M256_BK == 0;
+    const bool vec = vec_ok(a);
+    const hipError_t e = with_trans(a, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (vec && full)
+            hipLaunchKernelGGL((k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                               SGEMM_M256_STAGES, SGEMM_M256_WPE, true, true, TA, TB>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+        else if (vec)
+            hipLaunchKernelGGL((k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                               SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false, TA, TB>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+        else
+            hipLaunchKernelGGL((k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                               SGEMM_M256_STAGES, SGEMM_M256_WPE, false, false, TA, TB>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+        return hipGetLastError();
+    });
+    if (e != hipSuccess || p.upw == p.slices) return e;
+    hipLaunchKernelGGL((k_sk_fixup<M256_BM, M256_BN, M256_WM, M256_WN>), dim3((unsigned)p.sk_tiles),
+                       block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+    return hipGetLastError();
+}
+Variant kMfma256Sk = {"mfma_256x256_sk", check_mfma256, nullptr,
+                      (const void*)k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
+                                                  SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false>,
+                      M256_NT, true, ws_mfma256, launch_ws_mfma256};
 
 template <int BM, int BN, int WM, int WN, int BK = 16>
 struct KgroupInstance {

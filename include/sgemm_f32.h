@@ -144,7 +144,10 @@ enum sgemm_f32_variant_id {
        They need a workspace (sgemm_f32_ws_size) */
     SGEMM_F32_MFMA_128_SK = 17,
     SGEMM_F32_MFMA_64x128_SK = 18,
-    SGEMM_F32_NUM_VARIANTS = 19
+    /* the same for MFMA_256 (one workgroup per compute unit, so whole tiles
+       come in rounds of one tile per unit) */
+    SGEMM_F32_MFMA_256_SK = 19,
+    SGEMM_F32_NUM_VARIANTS = 20
 };
 
 /* Storage order and operand transposition of the _ex entry points (the
@@ -238,7 +241,7 @@ SGEMM_F32_API int sgemm_f32_plan_ex(int layout, int transa, int transb, int64_t 
  *
  * sgemm_f32_ws is sgemm_f32_ex with a workspace: the automatic choice may
  * then also pick a stream-K kernel (SGEMM_F32_MFMA_128_SK,
- * SGEMM_F32_MFMA_64x128_SK) when the dispatch model predicts it faster and
+ * SGEMM_F32_MFMA_64x128_SK, SGEMM_F32_MFMA_256_SK) when the dispatch model predicts it faster and
  * `workspace_bytes` covers what it needs. With workspace_bytes == 0 (the
  * workspace may then be NULL) it is sgemm_f32_ex. The workspace is device
  * memory of at least workspace_bytes bytes, 16-byte aligned, owned by the
@@ -276,8 +279,8 @@ SGEMM_F32_API int sgemm_f32_plan_ws(int layout, int transa, int transb, int64_t 
  * to sgemm_f32_ws leaves every candidate open. Host-only. Writes *bytes and
  * returns 0, or -13/-14/-15/-1/-2/-3 for a bad layout, flag or size, -12 if
  * bytes is NULL, SGEMM_F32_ERR_VARIANT, or SGEMM_F32_ERR_TOO_LARGE. At most
- * 2 * num_cus partial tiles of 128 x 128 floats: 33.6 MB on 256 compute
- * units. */
+ * 2 * num_cus partial tiles of the kernel's block tile: 134 MB for the
+ * 256 x 256 tiles on 256 compute units, 33.6 MB for 128 x 128. */
 SGEMM_F32_API int sgemm_f32_ws_size(int variant, int layout, int transa, int transb, int64_t M,
                                     int64_t N, int64_t K, int num_cus, size_t *bytes);
 
@@ -310,7 +313,7 @@ SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
 typedef struct {
     int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,
                            MFMA_64x128_KG4, MFMA_64x96_KG4, MFMA_128x128_KG4,
-                           MFMA_128_SK or MFMA_64x128_SK */
+                           MFMA_128_SK, MFMA_64x128_SK or MFMA_256_SK */
     double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
     double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */
 } sgemm_f32_model_entry;

@@ -22,7 +22,7 @@ from fp32_gemm_tuning_amd import tune  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-SK = ["mfma_128x128_sk", "mfma_64x128_sk"]
+SK = ["mfma_128x128_sk", "mfma_64x128_sk", "mfma_256x256_sk"]
 ROW = sg.ROW_MAJOR
 
 

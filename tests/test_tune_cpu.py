@@ -170,3 +170,17 @@ def test_fit_recovers_synthetic_constants():
         for b in range(4):
             assert abs(got[v]["eff"][b] - eff[b]) <= 0.02 * eff[b]
     assert all(r["loss"] == 0.0 for r in tune.check(model, samples, cus))
+
+
+@pytest.mark.parametrize("variant", sorted(tune.SK_BK))
+@pytest.mark.parametrize("M,N,K", [(3072, 3072, 3072), (1000, 1531, 777), (5000, 5000, 5000),
+                                   (2176, 2176, 250), (4096, 4096, 4096), (128, 128, 48)])
+def test_library_split_matches_the_tuner(variant, M, N, K):
+    # The workspace the library asks for is what the tuner's copy of the split
+    # (block tile and K slice per stream-K kernel) implies, so the model's
+    # busiest-unit share and the kernel's real split agree.
+    bm, bn = tune.TILE[variant]
+    sp = tune.sk_split(-(-M // bm) * -(-N // bn), -(-K // tune.SK_BK[variant]), 256)
+    want = 0 if sp is None else 2 * sp[2] * bm * bn * 4
+    v = sg.sgemm_f32_variant_by_name(variant)
+    assert sg.sgemm_f32_ws_size(v, sg.ROW_MAJOR, 0, 0, M, N, K, 256) == (0, want)
