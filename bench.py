@@ -181,8 +181,9 @@ def sweep(args, dev) -> int:
         ws = torch.empty(max(16, wsb), dtype=torch.uint8, device=dev)
         # Untimed: bring the clock up before the first timed row, so that the
         # rows of a workload compare kernels rather than clock ramps.
-        clock_warmup(lambda: sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta, dC,
-                                          w.N, sp))
+        if not args.no_clock_warmup:
+            clock_warmup(lambda: sg.sgemm_f32(w.M, w.N, w.K, w.alpha, dA, w.K, dB, w.N, w.beta,
+                                              dC, w.N, sp))
         for vname in ["auto"] + (["auto_ws"] if args.ws else []) + names:
             if vname in SLOW_RUNGS and wname not in SLOW_OK:
                 continue
@@ -416,6 +417,9 @@ def main() -> int:
     ap.add_argument("--context", action="store_true",
                     help="in a sweep, also time torch's FP32 matmul (vendor library, "
                          "TF32 off) as context")
+    ap.add_argument("--no-clock-warmup", action="store_true",
+                    help="in a sweep, skip the untimed clock warm-up before each workload "
+                         "(counter runs, which count every dispatch)")
     ap.add_argument("--ws", action="store_true",
                     help="in a sweep, also time the automatic choice with a workspace "
                          "(sgemm_f32_ws, which may pick a stream-K kernel)")

@@ -71,7 +71,7 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // 26 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
 // (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
 // the fastest whole-tile kernel on 23 of them, with one the fastest of all
-// on 22, and in both cases one within 8% on the rest.
+// on 23, and in both cases one within 7% on the rest.
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;

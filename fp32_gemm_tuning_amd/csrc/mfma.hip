@@ -1342,8 +1342,8 @@ using Kg96 = KgroupInstance<64, 96, 64, 32, SGEMM_KG96_BK>;
 Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT,
                          true};
 // 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
-// tile per compute unit for medium shapes such as 2048^3 (256 tiles), where
-// mfma_128x128 would leave one wave per SIMD.
+// tile per compute unit with four waves per SIMD, for shapes with at most
+// about one 128x128 tile per compute unit and long K.
 using Kg128x128 = KgroupInstance<128, 128, 64, 64>;
 Variant kMfmaKgroup128 = {"mfma_128x128_kg4", Kg128x128::check, Kg128x128::launch,
                           Kg128x128::kernel(), Kg128x128::NT, true};
