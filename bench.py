@@ -32,8 +32,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FP32_PEAK_TFLOPS = 157.3        # MI355X dense FP32 (matrix and packed-vector) peak
-FP32_VALU_PEAK_TFLOPS = 78.6    # unpacked v_fma_f32: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3        # MI355X dense FP32 matrix peak (one 32x32x2 MFMA / 64 clk / SIMD)
+# MI355X FP32 vector peak: 256 CU x 4 SIMD x 32 FMA lanes x 2 FLOP x 2.4 GHz. The kernels are built
+# without packed FP32, and plain v_fmac_f32 still runs above half of this (the peak probe and the
+# vector-FMA kernel both exceed 78.6 TFLOP/s), so half-rate is no ceiling and the full figure is
+# the one to price against.
+FP32_VALU_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["fp32_gemm_tuning_amd/csrc/mfma.hip", "fp32_gemm_tuning_amd/csrc/valu_main.hip",
