@@ -17,6 +17,7 @@ or raw device addresses as ints; they return the C status code):
     sgemm_f32_plan_ex(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                       num_cus) -> (code, variant)
     sgemm_f32_variant_trans_ok(variant)
+    sgemm_f32_variant_tile(variant) -> (code, bm, bn, bk)
     sgemm_f32_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                  workspace, workspace_bytes, stream=None)
     sgemm_f32_variant_ws(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb,
@@ -120,6 +121,9 @@ def _load() -> ctypes.CDLL:
     lib.sgemm_f32_ws_size.restype = c_int
     lib.sgemm_f32_variant_trans_ok.argtypes = [c_int]
     lib.sgemm_f32_variant_trans_ok.restype = c_int
+    ip = ctypes.POINTER(c_int)
+    lib.sgemm_f32_variant_tile.argtypes = [c_int, ip, ip, ip]
+    lib.sgemm_f32_variant_tile.restype = c_int
     lib.sgemm_f32_num_variants.argtypes = []
     lib.sgemm_f32_num_variants.restype = c_int
     lib.sgemm_f32_variant_name.argtypes = [c_int]
@@ -246,6 +250,13 @@ def sgemm_f32_ws_size(variant, layout, transa, transb, M, N, K, num_cus) -> Tupl
 
 def sgemm_f32_variant_trans_ok(variant: int) -> int:
     return int(_lib.sgemm_f32_variant_trans_ok(int(variant)))
+
+
+def sgemm_f32_variant_tile(variant: int) -> Tuple[int, int, int, int]:
+    bm, bn, bk = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    rc = int(_lib.sgemm_f32_variant_tile(int(variant), ctypes.byref(bm), ctypes.byref(bn),
+                                         ctypes.byref(bk)))
+    return rc, bm.value, bn.value, bk.value
 
 
 def sgemm_f32_num_variants() -> int:

@@ -7,11 +7,12 @@ from scratch", Module 08; "Optimizing Matrix Multiply on CUDA, Part 2",
 macros of csrc/mfma.hip, so a sweep builds one copy of the library per
 configuration and times the kernel the configuration changes:
 
-  space "tile" (mfma_128x128, k_mfma_tile): block tile BM x BN, wave tile
-        WM x WN, K slice BK, waves per SIMD (occupancy target), tile-grouping
-        band GROUP_M (SGEMM_M128_*)
-  space "pipe" (mfma_256x256, k_mfma_pipe): block and wave tile, BK, LDS
-        stages (SGEMM_M256_*)
+  space "tile" (mfma_128x128): block tile BM x BN, wave tile WM x WN, K
+        slice BK, waves per SIMD (occupancy target), tile-grouping band
+        GROUP_M (SGEMM_M128_*)
+  space "pipe" (mfma_256x256): block and wave tile, BK, LDS stages
+        (SGEMM_M256_*)
+  (both variants are instances of the pipelined kernel k_mfma_pipe)
   space "kg96" (mfma_64x96_kg4): K slice (SGEMM_KG96_BK)
 
 build (on any machine with hipcc; no GPU):
@@ -48,13 +49,14 @@ from typing import Dict, List, Optional, Sequence, Tuple
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 # Each space: the variant it changes, the kernel whose resource report
-# matters, and the values of its macros. A parameter written "A,B" sets two
+# matters (a pattern of its mangled name, filled in from the configuration),
+# and the values of its macros. A parameter written "A,B" sets two
 # macros together (a block tile or a wave tile). The first value of each list
 # is the in-tree default, so the first configuration is the in-tree build.
 SPACES: Dict[str, dict] = {
     "tile": {
         "variant": "mfma_128x128",
-        "kernel": "k_mfma_tile",
+        "kernel": "k_mfma_pipeILi{SGEMM_M128_BM}ELi{SGEMM_M128_BN}ELi{SGEMM_M128_WM}ELi{SGEMM_M128_WN}E",
         "params": {
             "SGEMM_M128_BM,SGEMM_M128_BN": [(128, 128), (64, 128), (128, 64), (256, 128),
                                             (128, 256)],
@@ -66,7 +68,7 @@ SPACES: Dict[str, dict] = {
     },
     "pipe": {
         "variant": "mfma_256x256",
-        "kernel": "k_mfma_pipe",
+        "kernel": "k_mfma_pipeILi{SGEMM_M256_BM}ELi{SGEMM_M256_BN}ELi{SGEMM_M256_WM}ELi{SGEMM_M256_WN}E",
         "params": {
             "SGEMM_M256_BM,SGEMM_M256_BN": [(256, 256), (256, 128), (128, 256), (128, 128)],
             "SGEMM_M256_WM,SGEMM_M256_WN": [(64, 64)],
@@ -138,6 +140,12 @@ def config_name(space: str, c: Dict[str, int]) -> str:
     return space + "_" + "_".join(f"{k}{v}" for k, v in short.items())
 
 
+def kernel_pattern(space: str, c: Dict[str, int]) -> str:
+    """The part of the mangled kernel name that picks out the instances a
+    configuration builds."""
+    return SPACES[space]["kernel"].format(**c)
+
+
 def flags(c: Dict[str, int]) -> List[str]:
     return [f"-D{k}={v}" for k, v in c.items()]
 
@@ -178,8 +186,6 @@ def build(space: str, out: str, jobs: int = 4, limit: Optional[int] = None, log=
     os.makedirs(out, exist_ok=True)
     shared = [os.path.join(b.BUILD, os.path.splitext(s)[0] + ".o") for s in b.SOURCES
               if s != "mfma.hip"]
-    kernel = SPACES[space]["kernel"]
-
     def one(c):
         name = config_name(space, c)
         d = os.path.join(out, name)
@@ -195,7 +201,7 @@ def build(space: str, out: str, jobs: int = 4, limit: Optional[int] = None, log=
         os.remove(obj)
         entry["built"] = r.returncode == 0
         entry["lib"] = os.path.relpath(lib, out)
-        entry.update(_resources(text, kernel))
+        entry.update(_resources(text, kernel_pattern(space, c)))
         return entry
 
     cs = configs(space, limit)

@@ -70,32 +70,28 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Both were fitted per kernel to interleaved timings of every candidate on
 // 26 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
 // (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
-// the fastest whole-tile kernel on 23 of them, with one the fastest of all
-// on 23, and in both cases one within 7% on the rest.
+// the fastest whole-tile kernel on 23 of them and one within 2% on the rest,
+// with one the fastest of all on 22 and one within 4% on the rest.
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
-    int bm, bn;
     double overhead_us;
     double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 tiles per CU
 };
 
-// The tile kernels the model can choose among, with their block tiles (and,
-// for the stream-K kernels, their K slice).
-struct TileKernel {
-    int variant, bm, bn, bk;
+// The variants the model can choose among: the matrix-core tile kernels,
+// whose block tile and (for the stream-K kernels) K slice the variant table
+// records.
+static const int kModelVariants[] = {
+    SGEMM_F32_MFMA_128,      SGEMM_F32_MFMA_256,       SGEMM_F32_MFMA_64x128,
+    SGEMM_F32_MFMA_64,       SGEMM_F32_MFMA_64x128_KG4, SGEMM_F32_MFMA_64x96_KG4,
+    SGEMM_F32_MFMA_128x128_KG4, SGEMM_F32_MFMA_128_SK, SGEMM_F32_MFMA_64x128_SK,
+    SGEMM_F32_MFMA_256_SK,
 };
-static const TileKernel kTileKernels[] = {
-    {SGEMM_F32_MFMA_128, 128, 128, 0},        {SGEMM_F32_MFMA_256, 256, 256, 0},
-    {SGEMM_F32_MFMA_64x128, 64, 128, 0},      {SGEMM_F32_MFMA_64, 64, 64, 0},
-    {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 0},  {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 0},
-    {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 0}, {SGEMM_F32_MFMA_128_SK, 128, 128, 32},
-    {SGEMM_F32_MFMA_64x128_SK, 64, 128, 16}, {SGEMM_F32_MFMA_256_SK, 256, 256, 16},
-};
-static const TileKernel* tile_kernel(int variant) {
-    for (const TileKernel& k : kTileKernels)
-        if (k.variant == variant) return &k;
-    return nullptr;
+static bool model_variant(int variant) {
+    for (int v : kModelVariants)
+        if (v == variant) return true;
+    return false;
 }
 
 static constexpr int kMaxModel = SGEMM_F32_MODEL_MAX;
@@ -107,16 +103,16 @@ struct Model {
 // Built-in model, listed in order of preference when predictions tie.
 static const Model kDefaultModel = {10,
                                     {
-                                        {SGEMM_F32_MFMA_128, 128, 128, 11.5, {0.897, 0.902, 0.903, 0.905}},
-                                        {SGEMM_F32_MFMA_256, 256, 256, 20.0, {0.977, 0.929, 0.943, 0.943}},
-                                        {SGEMM_F32_MFMA_64x128, 64, 128, 6.0, {0.692, 0.796, 0.816, 0.855}},
-                                        {SGEMM_F32_MFMA_64, 64, 64, 6.0, {0.485, 0.617, 0.701, 0.792}},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 64, 128, 8.5, {0.784, 0.776, 0.794, 0.808}},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 64, 96, 9.0, {0.746, 0.727, 0.754, 0.763}},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 128, 128, 12.0, {0.884, 0.866, 0.864, 0.873}},
-                                        {SGEMM_F32_MFMA_128_SK, 128, 128, 17.5, {0.801, 0.885, 0.891, 0.891}},
-                                        {SGEMM_F32_MFMA_64x128_SK, 64, 128, 15.0, {0.680, 0.737, 0.841, 0.855}},
-                                        {SGEMM_F32_MFMA_256_SK, 256, 256, 28.5, {0.904, 0.898, 0.929, 0.929}},
+                                        {SGEMM_F32_MFMA_128, 6.0, {0.918, 0.925, 0.939, 0.946}},
+                                        {SGEMM_F32_MFMA_256, 18.5, {1.000, 0.952, 0.968, 0.968}},
+                                        {SGEMM_F32_MFMA_64x128, 7.0, {0.836, 0.871, 0.881, 0.909}},
+                                        {SGEMM_F32_MFMA_64, 4.5, {0.446, 0.595, 0.708, 0.797}},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 9.0, {0.790, 0.775, 0.800, 0.810}},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 9.5, {0.754, 0.729, 0.758, 0.762}},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 10.5, {0.883, 0.860, 0.863, 0.869}},
+                                        {SGEMM_F32_MFMA_128_SK, 17.5, {0.815, 0.949, 0.942, 0.906}},
+                                        {SGEMM_F32_MFMA_64x128_SK, 14.0, {0.803, 0.886, 0.922, 0.879}},
+                                        {SGEMM_F32_MFMA_256_SK, 30.5, {0.927, 0.917, 0.959, 0.959}},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a
@@ -138,11 +134,10 @@ static double eff_at(const Candidate& c, double n) {
 // Tiles' worth of work on the busiest compute unit for a candidate: whole
 // tiles dealt out breadth-first, or, for a stream-K kernel, the whole tiles
 // plus one run of slices (sk_split). 0 if a stream-K kernel would not split.
-static double busiest_tiles(const Candidate& c, int64_t M, int64_t N, int64_t K, int num_cus) {
-    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
-    const TileKernel* k = tile_kernel(c.variant);
-    if (k != nullptr && k->bk > 0) {
-        const SkSplit sp = sk_split(tiles, cdiv(K, k->bk), num_cus);
+static double busiest_tiles(const Variant& v, int64_t M, int64_t N, int64_t K, int num_cus) {
+    const int64_t tiles = cdiv(M, v.bm) * cdiv(N, v.bn);
+    if (v.ws_size != nullptr) {
+        const SkSplit sp = sk_split(tiles, cdiv(K, v.bk), num_cus);
         return sp.split() ? sp.busiest_tiles(num_cus) : 0.0;
     }
     return (double)cdiv(tiles, num_cus);
@@ -168,10 +163,10 @@ static int choose(const Args& a, int num_cus, size_t ws_bytes) {
         const Variant& v = *kTable[c.variant];
         if (trans && !v.trans_ok) continue;
         if (v.ws_size != nullptr && (ws_bytes == 0 || v.ws_size(a, num_cus) > ws_bytes)) continue;
-        const double n = busiest_tiles(c, M, N, K, num_cus);
+        const double n = busiest_tiles(v, M, N, K, num_cus);
         if (n <= 0.0) continue;
         const double us = c.overhead_us +
-                          1e6 * n * 2.0 * c.bm * c.bn * (double)K / (kPeakPerCu * eff_at(c, std::ceil(n)));
+                          1e6 * n * 2.0 * v.bm * v.bn * (double)K / (kPeakPerCu * eff_at(c, std::ceil(n)));
         if (!found || us < best_us) {
             best = c.variant;
             best_us = us;
@@ -432,6 +427,16 @@ SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant) {
     return kTable[variant]->trans_ok ? 1 : 0;
 }
 
+SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int* bm, int* bn, int* bk) {
+    if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    const bool tile = model_variant(variant);
+    const Variant& v = *kTable[variant];
+    if (bm != nullptr) *bm = tile ? v.bm : 0;
+    if (bn != nullptr) *bn = tile ? v.bn : 0;
+    if (bk != nullptr) *bk = tile ? v.bk : 0;
+    return tile ? 1 : 0;
+}
+
 SGEMM_F32_API int sgemm_f32_num_variants(void) { return SGEMM_F32_NUM_VARIANTS; }
 
 SGEMM_F32_API const char* sgemm_f32_variant_name(int variant) {
@@ -511,15 +516,14 @@ extern "C" SGEMM_F32_API int sgemm_f32_set_model(const sgemm_f32_model_entry* en
     m->n = n;
     for (int i = 0; i < n; ++i) {
         const sgemm_f32_model_entry& e = entries[i];
-        const TileKernel* k = tile_kernel(e.variant);
-        bool ok = k != nullptr && e.overhead_us >= 0.0 && e.overhead_us <= 1e6;
+        bool ok = model_variant(e.variant) && e.overhead_us >= 0.0 && e.overhead_us <= 1e6;
         for (int b = 0; b < 4; ++b) ok = ok && e.eff[b] > 0.0 && e.eff[b] <= 1.5;
         for (int p = 0; p < i; ++p) ok = ok && entries[p].variant != e.variant;
         if (!ok) {
             delete m;
             return -3;
         }
-        m->c[i] = Candidate{e.variant, k->bm, k->bn, e.overhead_us, {e.eff[0], e.eff[1], e.eff[2], e.eff[3]}};
+        m->c[i] = Candidate{e.variant, e.overhead_us, {e.eff[0], e.eff[1], e.eff[2], e.eff[3]}};
     }
     g_model.store(m, std::memory_order_release);
     return 0;

@@ -29,6 +29,10 @@ struct Variant {
     // Stream-K variants only (else null): `launch` is then unused.
     ws_size_fn ws_size;
     launch_ws_fn launch_ws;
+    // Matrix-core tile kernels the dispatch model chooses among: the output
+    // tile of one workgroup and the K slice of one pipeline step (the unit
+    // of a stream-K split). 0 for the other variants.
+    int bm = 0, bn = 0, bk = 0;
 };
 
 // ---------------------------------------------------------------------------

@@ -294,19 +294,17 @@ struct SubstepMma {
 };
 
 // ===========================================================================
-// Tiled FP32 MFMA kernel, generic over the block tile BM x BN and the wave
-// tile WM x WN (each wave owns WM/32 x WN/32 blocks of 32x32 accumulated
-// with v_mfma_f32_32x32x2_f32). BK-deep slices, double-buffered LDS: the
-// buffer-to-LDS loads of slice s+1 are in flight while slice s is
-// multiplied; one barrier per slice.
-//
-// mfma_128x128 is BM = BN = 128 with 8 waves of 64x32 (32 accumulator
-// registers per lane), BK = 32, and an occupancy target of 4 waves per SIMD
-// (2 workgroups per compute unit); mfma_64x128 is 64x128 with 4 waves of
-// 64x32 and BK = 16. Both were chosen by sweeping block tile, wave tile,
-// BK and occupancy on MI355X (fp32_gemm_tuning_amd/autotune.py): against
-// the 4-waves-of-64x64, BK = 16 layout they gain 1-9% at 2048^3 to 8192^2 x
-// 1024 and lose nothing on the other shapes measured.
+// Tile parameters of mfma_128x128 and mfma_64x128, two instances of the
+// pipelined kernel below (k_mfma_pipe), set at compile time so that the
+// autotuner (fp32_gemm_tuning_amd/autotune.py) can sweep them. mfma_128x128
+// is BM = BN = 128 with 8 waves of 64x32 (32 accumulator registers per
+// lane), BK = 32, and an occupancy target of 4 waves per SIMD (2 workgroups
+// per compute unit); mfma_64x128 is 64x128 with 4 waves of 64x32, BK = 32
+// and 3 workgroups per compute unit. The block and wave tiles came from a sweep of the earlier
+// single-buffered tile kernel on MI355X; moved onto the pipelined kernel
+// they gain 3-20% (2048^3 122.6 -> 130.5, 512x4096x4096 108.8 -> 130.5
+// TFLOP/s) and lose 4% only on the 1000x1531x777 odd shape, which the
+// dispatch gives to a K-group kernel.
 // ===========================================================================
 #ifndef SGEMM_M128_BK
 #define SGEMM_M128_BK 32
@@ -336,110 +334,10 @@ struct SubstepMma {
 #define SGEMM_M64x128_WN 32
 #endif
 #ifndef SGEMM_M64x128_BK
-#define SGEMM_M64x128_BK 16
+#define SGEMM_M64x128_BK 32
 #endif
 constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
 constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN, M128_GROUP_M = SGEMM_M128_GROUP_M;
-
-// The body of k_mfma_tile, shared with its stream-K form: the product of the
-// slices [s_begin, s_end) of one tile, and the epilogue. The LDS stages are
-// the caller's (one object each); on return every wave has passed the last
-// barrier and no load into them is outstanding.
-template <int BM, int BN, int WM, int WN, int BK, bool VEC, bool TA, bool TB>
-struct TileCore {
-    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0,
-                  "wave tiles are whole 32x32 blocks that divide the block tile");
-    static_assert((BM / WM) * (BN / WN) * 64 <= 1024, "at most 16 waves per workgroup");
-    static constexpr int WAVES_N = BN / WN;
-    static constexpr int NT = (BM / WM) * WAVES_N * 64;
-    static constexpr int BI = WM / 32, BJ = WN / 32;
-    using Dma = TileFillDma<BM, BN, BK, NT, VEC, TA, TB>;
-    static constexpr int BNP = Dma::BNP;
-
-    int m0, n0, rows_valid, cols_valid, t, wm, wn, h, c;
-
-    __device__ __forceinline__ TileCore(const Args& a, int tm, int tn, int tid = threadIdx.x) {
-        m0 = tm * BM;
-        n0 = tn * BN;
-        rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
-        cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
-        t = tid;
-        const int lane = t & 63, w = t >> 6;
-        wm = w / WAVES_N;
-        wn = w % WAVES_N;
-        h = lane >> 5;
-        c = lane & 31;
-    }
-
-    __device__ __forceinline__ static void zero(f32x16 (&acc)[BI][BJ]) {
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-#pragma unroll
-            for (int j = 0; j < BJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    }
-
-    // One pipelined step: start filling slice s+1 into the other stage with
-    // buffer-to-LDS loads, multiply slice s from this stage, barrier (which
-    // also waits for this wave's loads). With one barrier per slice and two
-    // stages, a stage is refilled only after every wave has passed the
-    // barrier that ends the slice that read it.
-    __device__ __forceinline__ void mainloop(const Args& a, int s_begin, int s_end, float* As0,
-                                             float* Bs0, float* As1, float* Bs1,
-                                             f32x16 (&acc)[BI][BJ]) const {
-        const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, 0, 0);
-        const Dma dma;
-        auto step = [&](int s, float* Acur, float* Bcur, float* Anext, float* Bnext) {
-            if (s + 1 < s_end)
-                dma.issue(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid, Anext, Bnext);
-            mma(Acur, Bcur, acc);
-            __syncthreads();
-        };
-        dma.issue(a, t, m0, n0, s_begin * BK, rows_valid, cols_valid, As0, Bs0);
-        __syncthreads();
-        for (int s = s_begin; s < s_end; s += 2) {
-            step(s, As0, Bs0, As1, Bs1);
-            if (s + 1 < s_end) step(s + 1, As1, Bs1, As0, Bs0);
-        }
-    }
-
-    __device__ __forceinline__ void store(const Args& a, const f32x16 (&acc)[BI][BJ]) const {
-#pragma unroll
-        for (int bi = 0; bi < BI; ++bi)
-#pragma unroll
-            for (int bj = 0; bj < BJ; ++bj)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int j = wn * WN + bj * 32 + c;
-                    if (i < rows_valid && j < cols_valid)
-                        store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
-                }
-    }
-};
-
-template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC, bool TA = false,
-          bool TB = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void k_mfma_tile(Args a, int tiles_m, int tiles_n, int xcd_remap) {
-    using Core = TileCore<BM, BN, WM, WN, BK, VEC, TA, TB>;
-    // One LDS object per stage, so that the compiler can tell the stage being
-    // filled from the stage being read.
-    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs0[BK * Core::BNP];
-    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs1[BK * Core::BNP];
-
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
-    const Core core(a, tm, tn);
-    f32x16 acc[Core::BI][Core::BJ];
-    Core::zero(acc);
-    core.mainloop(a, 0, (a.K + BK - 1) / BK, As0, Bs0, As1, Bs1, acc);
-    core.store(a, acc);
-}
 
 // ---------------------------------------------------------------------------
 // Stream-K (SkPlan in common.hpp). A run of slices that covers a whole tile
@@ -500,79 +398,6 @@ struct PartialIo {
 // if that run starts in the tile, else its last run (slot 2jj+1).
 __device__ __forceinline__ int sk_slot(const SkPlan& p, int jj, int st) {
     return (jj * p.upw >= st * p.slices) ? 2 * jj : 2 * jj + 1;
-}
-
-// Stream-K form of k_mfma_tile: workgroups below p.dp_tiles compute whole
-// tiles as k_mfma_tile does; the others their runs of slices.
-template <int BM, int BN, int WM, int WN, int BK, int WPE, bool VEC, bool TA = false,
-          bool TB = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void k_mfma_tile_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
-    using Core = TileCore<BM, BN, WM, WN, BK, VEC, TA, TB>;
-    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
-    __shared__ __attribute__((aligned(16))) float As0[BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs0[BK * Core::BNP];
-    __shared__ __attribute__((aligned(16))) float As1[BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs1[BK * Core::BNP];
-
-    const int b = blockIdx.x;
-    f32x16 acc[Core::BI][Core::BJ];
-    int tm, tn;
-    if (b < p.dp_tiles) {
-        tile_of_first(b, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
-        const Core core(a, tm, tn);
-        Core::zero(acc);
-        core.mainloop(a, 0, p.slices, As0, Bs0, As1, Bs1, acc);
-        core.store(a, acc);
-        return;
-    }
-    const int j = b - p.dp_tiles;
-    const int U = p.sk_tiles * p.slices;
-    int u = j * p.upw;
-    const int u_end = (u + p.upw) < U ? (u + p.upw) : U;
-    while (u < u_end) {
-        const int st = u / p.slices;
-        const int s0 = u - st * p.slices;
-        const int s1 = (s0 + (u_end - u)) < p.slices ? (s0 + (u_end - u)) : p.slices;
-        tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M,
-                      xcd_remap != 0, tm, tn);
-        // The lane's fragment and epilogue offsets derive from its thread
-        // index; hidden from the compiler here, they are recomputed per run
-        // instead of being hoisted out of the loop (and spilled).
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        const Core core(a, tm, tn, tid);
-        Core::zero(acc);
-        core.mainloop(a, s0, s1, As0, Bs0, As1, Bs1, acc);
-        if (s0 == 0 && s1 == p.slices)
-            core.store(a, acc);
-        else
-            Io::put(p.partials + (size_t)sk_slot(p, j, st) * BM * BN, core.t, acc);
-        u += s1 - s0;
-    }
-}
-
-// One workgroup per split tile: the sum of its pieces in K order, then the
-// epilogue. A tile covered by a single run was written by that run.
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
-void k_sk_fixup(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
-    using Core = TileCore<BM, BN, WM, WN, 16, true, false, false>;
-    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
-    const int st = blockIdx.x;
-    const int j0 = st * p.slices / p.upw, j1 = (st * p.slices + p.slices - 1) / p.upw;
-    if (j0 == j1) return;
-    int tm, tn;
-    tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0,
-                  tm, tn);
-    const Core core(a, tm, tn);
-    f32x16 acc[Core::BI][Core::BJ];
-    constexpr size_t TILE = (size_t)BM * BN;
-    Io::template gather<true>(p.partials + (size_t)sk_slot(p, j0, st) * TILE, core.t, acc);
-    for (int jj = j0 + 1; jj <= j1; ++jj)
-        Io::template gather<false>(p.partials + (size_t)sk_slot(p, jj, st) * TILE, core.t, acc);
-    core.store(a, acc);
 }
 
 // ===========================================================================
@@ -912,8 +737,9 @@ void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
         const int s1 = (s0 + (u_end - u)) < p.slices ? (s0 + (u_end - u)) : p.slices;
         tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M,
                       xcd_remap != 0, tm, tn);
-        // Per-lane offsets recomputed per run rather than hoisted (and
-        // spilled), as in k_mfma_tile_sk.
+        // The lane's fragment and epilogue offsets derive from its thread
+        // index; hidden from the compiler here, they are recomputed per run
+        // instead of being hoisted out of the loop (and spilled).
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
         const Core core(a, tm, tn, tid);
@@ -925,6 +751,28 @@ void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
             Io::put(p.partials + (size_t)sk_slot(p, j, st) * BM * BN, core.t, acc);
         u += s1 - s0;
     }
+}
+
+// One workgroup per split tile: the sum of its pieces in K order, then the
+// epilogue. A tile covered by a single run was written by that run.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+void k_sk_fixup(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
+    using Core = PipeCore<BM, BN, WM, WN, 16, 2, true, false, false, false>;
+    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
+    const int st = blockIdx.x;
+    const int j0 = st * p.slices / p.upw, j1 = (st * p.slices + p.slices - 1) / p.upw;
+    if (j0 == j1) return;
+    int tm, tn;
+    tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0,
+                  tm, tn);
+    const Core core(a, tm, tn);
+    f32x16 acc[Core::BI][Core::BJ];
+    constexpr size_t TILE = (size_t)BM * BN;
+    Io::template gather<true>(p.partials + (size_t)sk_slot(p, j0, st) * TILE, core.t, acc);
+    for (int jj = j0 + 1; jj <= j1; ++jj)
+        Io::template gather<false>(p.partials + (size_t)sk_slot(p, jj, st) * TILE, core.t, acc);
+    core.store(a, acc);
 }
 
 // ===========================================================================
@@ -945,7 +793,6 @@ __global__ __launch_bounds__(4 * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN), (BM / WM) * (BN / WN))))
 void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     constexpr int KG = 4;
-    constexpr int STEPS = BK / 16;   // 16-deep sub-steps per slice
     constexpr int GT = (BM / WM) * (BN / WN) * 64;  // threads per K-group
     constexpr int WAVES_N = BN / WN;
     constexpr int BI = WM / 32, BJ = WN / 32;
@@ -1106,121 +953,12 @@ static hipError_t with_trans(const Args& a, F&& f) {
     return a.tb ? f(N{}, T{}) : f(N{}, N{});
 }
 
-// Launch helpers for instances of k_mfma_tile. The 4-byte-fill instance keeps
-// more loads in flight per lane; at 4 waves per SIMD it would spill, so it
-// targets 3.
-template <int BM, int BN, int WM, int WN, int BK>
-struct TileInstance {
-    static constexpr int NT = (BM / WM) * (BN / WN) * 64;
-    // Occupancy of the 4-byte-fill instance: 3 waves per SIMD, or as many
-    // as one workgroup puts on each SIMD if that is more.
-    static constexpr int WPE4 = NT / 256 > 3 ? NT / 256 : 3;
-    template <bool VEC>
-    static const void* kernel() {
-        return (const void*)k_mfma_tile<BM, BN, WM, WN, BK,
-                                         VEC ? SGEMM_M128_WAVES_PER_EU : WPE4, VEC>;
-    }
-    static int check(const Args& a) {
-        if (!extents_ok(a, BM, BN, BK)) return SGEMM_F32_ERR_TOO_LARGE;
-        const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
-        return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
-    }
-    static hipError_t launch(const Args& a, hipStream_t s) {
-        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
-        const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
-        const bool vec = vec_ok(a);
-        return with_trans(a, [&](auto ta, auto tb) {
-            constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-            if (vec)
-                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, BK, SGEMM_M128_WAVES_PER_EU, true,
-                                                TA, TB>),
-                                   grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-            else
-                hipLaunchKernelGGL((k_mfma_tile<BM, BN, WM, WN, BK, WPE4, false, TA, TB>), grid,
-                                   block, 0, s, a, tm, tn, xcd_remap_enabled());
-            return hipGetLastError();
-        });
-    }
-};
-
-using Tile128 = TileInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK>;
-using Tile64x128 = TileInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK>;
-
-// Stream-K launch of a TileInstance tile: one workgroup per whole tile plus
-// the stream-K workgroups, then the fixup kernel on the same stream.
-template <int BM, int BN, int WM, int WN, int BK>
-struct TileSkInstance {
-    using Base = TileInstance<BM, BN, WM, WN, BK>;
-    static SkSplit split(const Args& a, int cus) {
-        return sk_split(cdiv(a.M, BM) * cdiv(a.N, BN), cdiv(a.K, BK), cus);
-    }
-    static size_t ws_size(const Args& a, int cus) { return sk_workspace_bytes(split(a, cus), BM, BN); }
-    static hipError_t launch_ws(const Args& a, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
-        const SkSplit sp = split(a, cus);
-        if (!sp.split()) return Base::launch(a, s);
-        if (ws == nullptr || ws_bytes < sk_workspace_bytes(sp, BM, BN)) return hipErrorInvalidValue;
-        SkPlan p;
-        p.dp_tiles = (int)sp.dp_tiles;
-        p.sk_tiles = (int)sp.sk_tiles;
-        p.sk_wgs = (int)sp.sk_wgs;
-        p.upw = (int)sp.upw;
-        p.slices = (int)sp.slices;
-        p.partials = (float*)ws;
-        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
-        const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(Base::NT);
-        const bool vec = vec_ok(a);
-        const hipError_t e = with_trans(a, [&](auto ta, auto tb) {
-            constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-            if (vec)
-                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, BK, SGEMM_M128_WAVES_PER_EU,
-                                                   true, TA, TB>),
-                                   grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
-            else
-                hipLaunchKernelGGL((k_mfma_tile_sk<BM, BN, WM, WN, BK, Base::WPE4, false, TA, TB>), grid,
-                                   block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
-            return hipGetLastError();
-        });
-        // Runs as long as a tile (upw == slices) cover whole tiles only.
-        if (e != hipSuccess || p.upw == p.slices) return e;
-        hipLaunchKernelGGL((k_sk_fixup<BM, BN, WM, WN>), dim3((unsigned)p.sk_tiles), block, 0, s, a,
-                           tm, tn, xcd_remap_enabled(), p);
-        return hipGetLastError();
-    }
-    static const void* kernel() {
-        return (const void*)k_mfma_tile_sk<BM, BN, WM, WN, BK, SGEMM_M128_WAVES_PER_EU, true>;
-    }
-};
-using Tile128Sk = TileSkInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK>;
-using Tile64x128Sk =
-    TileSkInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK>;
-
-static int check_mfma128(const Args& a) { return Tile128::check(a); }
-static hipError_t launch_mfma128(const Args& a, hipStream_t s) { return Tile128::launch(a, s); }
-static int check_mfma64x128(const Args& a) { return Tile64x128::check(a); }
-static hipError_t launch_mfma64x128(const Args& a, hipStream_t s) {
-    return Tile64x128::launch(a, s);
-}
-
-Variant kMfma128 = {"mfma_128x128", check_mfma128, launch_mfma128,
-                    Tile128::kernel<true>(), Tile128::NT, true};
-// Stream-K forms (they need a workspace: sgemm_f32_ws).
-Variant kMfma128Sk = {"mfma_128x128_sk", check_mfma128, nullptr, Tile128Sk::kernel(), Tile128::NT,
-                      true, Tile128Sk::ws_size, Tile128Sk::launch_ws};
-Variant kMfma64x128Sk = {"mfma_64x128_sk", check_mfma64x128, nullptr, Tile64x128Sk::kernel(),
-                         Tile64x128::NT, true, Tile64x128Sk::ws_size, Tile64x128Sk::launch_ws};
-// 64x128 tile, 4 waves of 64x32: twice the tiles of mfma_128x128 for
-// medium shapes (e.g. 2048^3, where 256 tiles of 128x128 leave one
-// workgroup per compute unit).
-Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
-                       Tile64x128::kernel<true>(), Tile64x128::NT, true};
-
-// mfma_256x256: the pipelined kernel with a 256x256 block tile, 16 waves of
-// 64x64 (four per SIMD, all of one workgroup), one workgroup per compute
-// unit (2 x 32 KiB LDS stages). With every wave of a compute unit in one
-// workgroup there is no staggered finish between workgroups sharing a SIMD,
-// and the A and B panels are read from L2 half as often as with 128x128
-// tiles. The 4-byte-fill instance spills a few registers at this occupancy
-// (correct, slower); shapes that need it are rarely large.
+// mfma_256x256 tile parameters: the pipelined kernel with a 256x256 block
+// tile, 16 waves of 64x64 (four per SIMD, all of one workgroup), one
+// workgroup per compute unit (2 x 32 KiB LDS stages). With every wave of a
+// compute unit in one workgroup there is no staggered finish between
+// workgroups sharing a SIMD, and the A and B panels are read from L2 half as
+// often as with 128x128 tiles.
 #ifndef SGEMM_M256_BM
 #define SGEMM_M256_BM 256
 #endif
@@ -1242,103 +980,124 @@ Variant kMfma64x128 = {"mfma_64x128", check_mfma64x128, launch_mfma64x128,
 #ifndef SGEMM_M256_BK
 #define SGEMM_M256_BK 16
 #endif
-constexpr int M256_BM = SGEMM_M256_BM, M256_BN = SGEMM_M256_BN, M256_WM = SGEMM_M256_WM,
-              M256_WN = SGEMM_M256_WN, M256_BK = SGEMM_M256_BK;
-constexpr int M256_NT = (M256_BM / M256_WM) * (M256_BN / M256_WN) * 64;
 
-template <bool VEC>
-static const void* kernel_mfma256() {
-    return (const void*)k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                    SGEMM_M256_STAGES, SGEMM_M256_WPE, VEC, false>;
-}
+// An instance of the pipelined kernel (k_mfma_pipe, and k_mfma_pipe_sk for
+// stream-K): block tile, wave tile, K slice, LDS stages and occupancy
+// target. Per call it picks the FULL form (tile grid and K slices exactly
+// cover the problem: no range masks) or the masked one, and the 16-byte or
+// 4-byte fill (vec_ok). The 4-byte-fill form keeps more loads in flight per
+// lane; it targets 3 waves per SIMD, or as many as one workgroup puts on
+// each SIMD if that is more, since it would spill at 4.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE>
+struct PipeInstance {
+    static constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    static constexpr int kBM = BM, kBN = BN, kBK = BK;
+    static constexpr int WPE4 = NT / 256 > 3 ? NT / 256 : 3;
 
-static int check_mfma256(const Args& a) {
-    if (!extents_ok(a, M256_BM, M256_BN, M256_BK)) return SGEMM_F32_ERR_TOO_LARGE;
-    const int64_t tiles = cdiv(a.M, M256_BM) * cdiv(a.N, M256_BN);
-    return tiles <= max_workgroups(M256_NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
-}
+    static const void* kernel() {
+        return (const void*)k_mfma_pipe<BM, BN, WM, WN, BK, STAGES, WPE, true, false>;
+    }
+    static const void* sk_kernel() {
+        return (const void*)k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, WPE, true, false>;
+    }
+    static int check(const Args& a) {
+        if (!extents_ok(a, BM, BN, BK)) return SGEMM_F32_ERR_TOO_LARGE;
+        const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
+        return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+    }
+    // f(VEC, FULL, TA, TB), each a std::integral_constant<bool>.
+    template <class F>
+    static hipError_t forms(const Args& a, F&& f) {
+        using T = std::true_type;
+        using N = std::false_type;
+        const bool vec = vec_ok(a);
+        const bool full = a.M % BM == 0 && a.N % BN == 0 && a.K % BK == 0;
+        return with_trans(a, [&](auto ta, auto tb) {
+            if (vec && full) return f(T{}, T{}, ta, tb);
+            if (vec) return f(T{}, N{}, ta, tb);
+            return f(N{}, N{}, ta, tb);
+        });
+    }
+    static hipError_t launch(const Args& a, hipStream_t s) {
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
+        return forms(a, [&](auto vec, auto full, auto ta, auto tb) {
+            constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
+            hipLaunchKernelGGL((k_mfma_pipe<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
+                                            decltype(ta)::value, decltype(tb)::value>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+            return hipGetLastError();
+        });
+    }
 
-static hipError_t launch_mfma256(const Args& a, hipStream_t s) {
-    const int tm = (int)cdiv(a.M, M256_BM), tn = (int)cdiv(a.N, M256_BN);
-    const dim3 grid((unsigned)((int64_t)tm * tn)), block(M256_NT);
-    const bool full = a.M % M256_BM == 0 && a.N % M256_BN == 0 && a.K % M256_BK == 0;
-    const bool vec = vec_ok(a);
-    return with_trans(a, [&](auto ta, auto tb) {
-        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-        if (vec && full)
-            hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                            SGEMM_M256_STAGES, SGEMM_M256_WPE, true, true, TA, TB>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-        else if (vec)
-            hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                            SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false, TA, TB>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-        else
-            hipLaunchKernelGGL((k_mfma_pipe<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                            SGEMM_M256_STAGES, SGEMM_M256_WPE, false, false, TA, TB>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    // Stream-K: one workgroup per whole tile of the first rounds, then the
+    // stream-K workgroups (sk_split), then k_sk_fixup on the same stream.
+    static SkSplit split(const Args& a, int cus) {
+        return sk_split(cdiv(a.M, BM) * cdiv(a.N, BN), cdiv(a.K, BK), cus);
+    }
+    static size_t ws_size(const Args& a, int cus) { return sk_workspace_bytes(split(a, cus), BM, BN); }
+    static hipError_t launch_ws(const Args& a, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
+        const SkSplit sp = split(a, cus);
+        if (!sp.split()) return launch(a, s);
+        if (ws == nullptr || ws_bytes < sk_workspace_bytes(sp, BM, BN)) return hipErrorInvalidValue;
+        SkPlan p;
+        p.dp_tiles = (int)sp.dp_tiles;
+        p.sk_tiles = (int)sp.sk_tiles;
+        p.sk_wgs = (int)sp.sk_wgs;
+        p.upw = (int)sp.upw;
+        p.slices = (int)sp.slices;
+        p.partials = (float*)ws;
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(NT);
+        const hipError_t e = forms(a, [&](auto vec, auto full, auto ta, auto tb) {
+            constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
+            hipLaunchKernelGGL((k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
+                                               decltype(ta)::value, decltype(tb)::value>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+            return hipGetLastError();
+        });
+        // Runs as long as a tile (upw == slices) cover whole tiles only.
+        if (e != hipSuccess || p.upw == p.slices) return e;
+        hipLaunchKernelGGL((k_sk_fixup<BM, BN, WM, WN>), dim3((unsigned)p.sk_tiles), block, 0, s, a,
+                           tm, tn, xcd_remap_enabled(), p);
         return hipGetLastError();
-    });
-}
+    }
+};
 
-Variant kMfma256 = {"mfma_256x256", check_mfma256, launch_mfma256, kernel_mfma256<true>(), M256_NT,
-                    true};
+using Pipe256 = PipeInstance<SGEMM_M256_BM, SGEMM_M256_BN, SGEMM_M256_WM, SGEMM_M256_WN,
+                             SGEMM_M256_BK, SGEMM_M256_STAGES, SGEMM_M256_WPE>;
+using Pipe128 = PipeInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK, 2,
+                             SGEMM_M128_WAVES_PER_EU>;
+// Two 24 KiB LDS stages per 4-wave workgroup: three workgroups per compute
+// unit, so three waves per SIMD.
+using Pipe64x128 =
+    PipeInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK, 2, 3>;
 
-// Stream-K form of mfma_256x256: one workgroup per compute unit, so a round
-// of whole tiles is one tile per unit; the remaining tiles' slices are split
-// (sk_split) and summed by k_sk_fixup.
-static SkSplit split_mfma256(const Args& a, int cus) {
-    return sk_split(cdiv(a.M, M256_BM) * cdiv(a.N, M256_BN), cdiv(a.K, M256_BK), cus);
-}
-static size_t ws_mfma256(const Args& a, int cus) {
-    return sk_workspace_bytes(split_mfma256(a, cus), M256_BM, M256_BN);
-}
-static hipError_t launch_ws_mfma256(const Args& a, void* ws, size_t ws_bytes, int cus,
-                                    hipStream_t s) {
-    const SkSplit sp = split_mfma256(a, cus);
-    if (!sp.split()) return launch_mfma256(a, s);
-    if (ws == nullptr || ws_bytes < sk_workspace_bytes(sp, M256_BM, M256_BN))
-        return hipErrorInvalidValue;
-    SkPlan p;
-    p.dp_tiles = (int)sp.dp_tiles;
-    p.sk_tiles = (int)sp.sk_tiles;
-    p.sk_wgs = (int)sp.sk_wgs;
-    p.upw = (int)sp.upw;
-    p.slices = (int)sp.slices;
-    p.partials = (float*)ws;
-    const int tm = (int)cdiv(a.M, M256_BM), tn = (int)cdiv(a.N, M256_BN);
-    const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(M256_NT);
-    const bool full = a.M % M256_BM == 0 && a.N % M256_BN == 0 && a.K % M256_BK == 0;
-    const bool vec = vec_ok(a);
-    const hipError_t e = with_trans(a, [&](auto ta, auto tb) {
-        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-        if (vec && full)
-            hipLaunchKernelGGL((k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                               SGEMM_M256_STAGES, SGEMM_M256_WPE, true, true, TA, TB>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
-        else if (vec)
-            hipLaunchKernelGGL((k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                               SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false, TA, TB>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
-        else
-            hipLaunchKernelGGL((k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                               SGEMM_M256_STAGES, SGEMM_M256_WPE, false, false, TA, TB>),
-                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
-        return hipGetLastError();
-    });
-    if (e != hipSuccess || p.upw == p.slices) return e;
-    hipLaunchKernelGGL((k_sk_fixup<M256_BM, M256_BN, M256_WM, M256_WN>), dim3((unsigned)p.sk_tiles),
-                       block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
-    return hipGetLastError();
-}
-Variant kMfma256Sk = {"mfma_256x256_sk", check_mfma256, nullptr,
-                      (const void*)k_mfma_pipe_sk<M256_BM, M256_BN, M256_WM, M256_WN, M256_BK,
-                                                  SGEMM_M256_STAGES, SGEMM_M256_WPE, true, false>,
-                      M256_NT, true, ws_mfma256, launch_ws_mfma256};
+Variant kMfma256 = {"mfma_256x256", Pipe256::check, Pipe256::launch, Pipe256::kernel(),
+                    Pipe256::NT, true, nullptr, nullptr, Pipe256::kBM, Pipe256::kBN, Pipe256::kBK};
+Variant kMfma128 = {"mfma_128x128", Pipe128::check, Pipe128::launch, Pipe128::kernel(),
+                    Pipe128::NT, true, nullptr, nullptr, Pipe128::kBM, Pipe128::kBN, Pipe128::kBK};
+// 64x128: twice the tiles of mfma_128x128 for medium shapes (e.g. 3072^3,
+// whose 576 tiles of 128x128 leave the second round of workgroups a third
+// full).
+Variant kMfma64x128 = {"mfma_64x128", Pipe64x128::check, Pipe64x128::launch,
+                       Pipe64x128::kernel(), Pipe64x128::NT, true, nullptr, nullptr,
+                       Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK};
+// Stream-K forms (they need a workspace: sgemm_f32_ws).
+Variant kMfma256Sk = {"mfma_256x256_sk", Pipe256::check, nullptr, Pipe256::sk_kernel(),
+                      Pipe256::NT, true, Pipe256::ws_size, Pipe256::launch_ws,
+                      Pipe256::kBM, Pipe256::kBN, Pipe256::kBK};
+Variant kMfma128Sk = {"mfma_128x128_sk", Pipe128::check, nullptr, Pipe128::sk_kernel(),
+                      Pipe128::NT, true, Pipe128::ws_size, Pipe128::launch_ws,
+                      Pipe128::kBM, Pipe128::kBN, Pipe128::kBK};
+Variant kMfma64x128Sk = {"mfma_64x128_sk", Pipe64x128::check, nullptr, Pipe64x128::sk_kernel(),
+                         Pipe64x128::NT, true, Pipe64x128::ws_size, Pipe64x128::launch_ws,
+                         Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK};
 
 template <int BM, int BN, int WM, int WN, int BK = 16>
 struct KgroupInstance {
     static constexpr int NT = 4 * (BM / WM) * (BN / WN) * 64;
+    static constexpr int kBM = BM, kBN = BN, kBK = BK;
     static int check(const Args& a) {
         if (!extents_ok(a, BM, BN, BK)) return SGEMM_F32_ERR_TOO_LARGE;
         const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
@@ -1365,7 +1124,7 @@ struct KgroupInstance {
 // 64x128 tile, 4 groups of 4 waves of 32x64 (16 waves, 96 KB LDS).
 using Kg128 = KgroupInstance<64, 128, 32, 64>;
 Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::kernel(), Kg128::NT,
-                       true};
+                       true, nullptr, nullptr, Kg128::kBM, Kg128::kBN, Kg128::kBK};
 // 64x96 tile, 4 groups of 3 waves of 64x32 (12 waves, 80 KB LDS): the odd
 // 1000x1531 output is exactly 256 such tiles.
 #ifndef SGEMM_KG96_BK
@@ -1373,13 +1132,14 @@ Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::ke
 #endif
 using Kg96 = KgroupInstance<64, 96, 64, 32, SGEMM_KG96_BK>;
 Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT,
-                         true};
+                         true, nullptr, nullptr, Kg96::kBM, Kg96::kBN, Kg96::kBK};
 // 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
 // tile per compute unit with four waves per SIMD, for shapes with at most
 // about one 128x128 tile per compute unit and long K.
 using Kg128x128 = KgroupInstance<128, 128, 64, 64>;
 Variant kMfmaKgroup128 = {"mfma_128x128_kg4", Kg128x128::check, Kg128x128::launch,
-                          Kg128x128::kernel(), Kg128x128::NT, true};
+                          Kg128x128::kernel(), Kg128x128::NT, true, nullptr, nullptr,
+                          Kg128x128::kBM, Kg128x128::kBN, Kg128x128::kBK};
 
 // ===========================================================================
 // mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2
@@ -1481,7 +1241,7 @@ static hipError_t launch_mfma64(const Args& a, hipStream_t s) {
 }
 
 Variant kMfma64 = {"mfma_64x64", check_mfma64, launch_mfma64, (const void*)k_mfma64<true>,
-                         256};
+                   256, false, nullptr, nullptr, M64_BM, M64_BN, M64_BK};
 
 // ===========================================================================
 // mfma_64x64_k4: a 64x64 tile whose 4 waves split every 64-deep K slice four

@@ -48,7 +48,7 @@ TILE: Dict[str, Tuple[int, int]] = {
 # Stream-K kernels and their K slice: their busiest unit holds floor(T/C)
 # whole tiles plus one run of slices (sk_split in the library), and they are
 # candidates only with a workspace, on shapes they split.
-SK_BK: Dict[str, int] = {"mfma_128x128_sk": 32, "mfma_64x128_sk": 16, "mfma_256x256_sk": 16}
+SK_BK: Dict[str, int] = {"mfma_128x128_sk": 32, "mfma_64x128_sk": 32, "mfma_256x256_sk": 16}
 PEAK_PER_CU = 4 * 64 * 2.4e9   # FP32 matrix FLOP/s of one MI355X compute unit
 
 # Shapes the built-in model was fitted on: square, flat, tall, odd, short-K.

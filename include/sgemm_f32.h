@@ -102,8 +102,9 @@ enum sgemm_f32_variant_id {
        Multiply on CUDA") */
     SGEMM_F32_VALU_MAIN = 6,
     /* FP32 matrix-core kernel, 128x128 block tile of 8 waves of 64x32
-       (v_mfma_f32_32x32x2_f32), 32-deep K slices, LDS filled by
-       buffer-to-LDS loads */
+       (v_mfma_f32_32x32x2_f32), 32-deep K slices in a ring of two LDS
+       stages filled by buffer-to-LDS loads, software-pipelined as
+       MFMA_256 */
     SGEMM_F32_MFMA_128 = 7,
     /* FP32 matrix-core kernel, 64x64 block tile for shapes with few 128x128
        tiles (v_mfma_f32_16x16x4_f32) */
@@ -121,8 +122,8 @@ enum sgemm_f32_variant_id {
        reduction at the end */
     SGEMM_F32_MFMA_DIRECT = 11,
     /* FP32 matrix-core kernel, 64x128 block tile (4 waves of 64x32,
-       v_mfma_f32_32x32x2_f32): twice the tiles of mfma_128x128 for medium
-       shapes */
+       v_mfma_f32_32x32x2_f32, 32-deep K slices), pipelined as MFMA_256:
+       twice the tiles of mfma_128x128 for medium shapes */
     SGEMM_F32_MFMA_64x128 = 12,
     /* FP32 matrix-core kernel, 256x256 block tile of 16 waves (one
        workgroup per compute unit), software-pipelined: the LDS reads of one
@@ -139,9 +140,9 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_MFMA_128x128_KG4 = 16,
     /* stream-K forms of MFMA_128 and MFMA_64x128 (sgemm_f32_ws): the tiles
        that fill whole rounds of the compute units are computed whole; the
-       rest are split along K across the units, and the workgroup that
-       finishes a tile's last piece sums the pieces in K order and writes C.
-       They need a workspace (sgemm_f32_ws_size) */
+       rest are split along K across the units, which leave their partial
+       tiles in the workspace, and a second kernel sums each tile's pieces
+       in K order and writes C. They need a workspace (sgemm_f32_ws_size) */
     SGEMM_F32_MFMA_128_SK = 17,
     SGEMM_F32_MFMA_64x128_SK = 18,
     /* the same for MFMA_256 (one workgroup per compute unit, so whole tiles
@@ -289,6 +290,16 @@ SGEMM_F32_API int sgemm_f32_ws_size(int variant, int layout, int transa, int tra
  * not, or
  * SGEMM_F32_ERR_VARIANT. */
 SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
+
+/* Geometry of a matrix-core tile kernel, the variants the dispatch model
+ * (below) chooses among: *bm x *bn is the block of C one workgroup
+ * computes, *bk the K depth of one step of its K loop, which is also the
+ * unit in which a stream-K kernel splits K (sgemm_f32_ws_size). These are
+ * compile-time parameters of the library, so a tuner reads them here rather
+ * than assuming them. Host-only. Returns 1 and writes the non-NULL pointers
+ * for a tile kernel; 0, writing zeros, for any other variant;
+ * SGEMM_F32_ERR_VARIANT for an id out of range. */
+SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int *bm, int *bn, int *bk);
 
 /* The dispatch model sgemm_f32 uses to choose among the tiled matrix-core
  * kernels (sgemm_f32_plan reports the choice). It follows the pages' kernel

@@ -64,19 +64,29 @@ def test_tile_rules():
 
 def test_resource_report_parsing():
     text = "\n".join([
-        "remark: x: Function Name: _ZN5sgemm11k_mfma_tileILi128E",
-        "remark: x:     VGPRs: 116",
+        "remark: x: Function Name: _ZN5sgemm11k_mfma_pipeILi128ELi128ELi64ELi32ELi32ELi2ELi4ELb1ELb1E",
+        "remark: x:     VGPRs: 92",
         "remark: x:     ScratchSize [bytes/lane]: 0",
-        "remark: x: Function Name: _ZN5sgemm11k_mfma_tileILi256E",
-        "remark: x:     VGPRs: 128",
+        "remark: x: Function Name: _ZN5sgemm11k_mfma_pipeILi128ELi128ELi64ELi32ELi32ELi2ELi3ELb0ELb0E",
+        "remark: x:     VGPRs: 134",
         "remark: x:     ScratchSize [bytes/lane]: 12",
-        "remark: x: Function Name: _ZN5sgemm11k_mfma_pipeILi256E",
-        "remark: x:     VGPRs: 200",
+        "remark: x: Function Name: _ZN5sgemm11k_mfma_pipeILi256ELi256ELi64ELi64ELi16ELi2ELi4ELb1ELb1E",
+        "remark: x:     VGPRs: 128",
         "remark: x:     ScratchSize [bytes/lane]: 64",
     ])
-    assert at._resources(text, "k_mfma_tile") == {"vgpr": 128, "scratch": 12}
-    assert at._resources(text, "k_mfma_pipe") == {"vgpr": 200, "scratch": 64}
+    tile0, pipe0 = at.configs("tile")[0], at.configs("pipe")[0]
+    assert at._resources(text, at.kernel_pattern("tile", tile0)) == {"vgpr": 134, "scratch": 12}
+    assert at._resources(text, at.kernel_pattern("pipe", pipe0)) == {"vgpr": 128, "scratch": 64}
     assert at._resources(text, "k_mfma_kgroup") == {"vgpr": 0, "scratch": 0}
+
+
+@pytest.mark.parametrize("space", sorted(at.SPACES))
+def test_kernel_pattern_names_the_configured_instance(space):
+    # Each configuration's pattern is a fragment of an Itanium-mangled name
+    # with that configuration's tile sizes.
+    for c in at.configs(space):
+        pat = at.kernel_pattern(space, c)
+        assert "{" not in pat and pat.startswith("k_mfma_")
 
 
 def test_shapes_argument():

@@ -172,6 +172,22 @@ def test_fit_recovers_synthetic_constants():
     assert all(r["loss"] == 0.0 for r in tune.check(model, samples, cus))
 
 
+def test_tile_geometry_matches_the_library():
+    # The tuner's block tiles and stream-K slices are the ones the library
+    # was compiled with (sgemm_f32_variant_tile); every other variant
+    # reports no tile.
+    for i, name in enumerate(sg.VARIANTS):
+        rc, bm, bn, bk = sg.sgemm_f32_variant_tile(i)
+        if name in tune.TILE:
+            assert (rc, bm, bn) == (1, *tune.TILE[name]), name
+            if name in tune.SK_BK:
+                assert bk == tune.SK_BK[name], name
+        else:
+            assert (rc, bm, bn, bk) == (0, 0, 0, 0), name
+    assert sg.sgemm_f32_variant_tile(-1)[0] == sg.ERR_VARIANT
+    assert sg.sgemm_f32_variant_tile(len(sg.VARIANTS))[0] == sg.ERR_VARIANT
+
+
 @pytest.mark.parametrize("variant", sorted(tune.SK_BK))
 @pytest.mark.parametrize("M,N,K", [(3072, 3072, 3072), (1000, 1531, 777), (5000, 5000, 5000),
                                    (2176, 2176, 250), (4096, 4096, 4096), (128, 128, 48)])
