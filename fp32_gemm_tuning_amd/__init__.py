@@ -75,7 +75,7 @@ MODEL_MAX = 16
 class ModelEntry(ctypes.Structure):
     """sgemm_f32_model_entry: one candidate of the dispatch model."""
     _fields_ = [("variant", ctypes.c_int), ("overhead_us", ctypes.c_double),
-                ("eff", ctypes.c_double * 4)]
+                ("eff", ctypes.c_double * 4), ("fill4", ctypes.c_double)]
 
 
 def _load() -> ctypes.CDLL:
@@ -295,8 +295,9 @@ def sgemm_f32_peak_probe(kind: int, workgroups: int, iters: int, out, stream=Non
 
 def sgemm_f32_set_model(entries) -> int:
     """Replace the dispatch model. `entries`: sequence of dicts with keys
-    variant (id or name), overhead_us, eff (4 floats); empty or None restores
-    the built-in model. Returns the C status code."""
+    variant (id or name), overhead_us, eff (4 floats) and optionally fill4
+    (default 1.0); empty or None restores the built-in model. Returns the C
+    status code."""
     entries = list(entries or [])
     arr = (ModelEntry * max(1, len(entries)))()
     for i, e in enumerate(entries):
@@ -305,6 +306,7 @@ def sgemm_f32_set_model(entries) -> int:
         arr[i].overhead_us = float(e["overhead_us"])
         for b in range(4):
             arr[i].eff[b] = float(e["eff"][b])
+        arr[i].fill4 = float(e.get("fill4", 1.0))
     return int(_lib.sgemm_f32_set_model(arr, len(entries)))
 
 
@@ -313,7 +315,8 @@ def sgemm_f32_get_model() -> list:
     arr = (ModelEntry * MODEL_MAX)()
     n = int(_lib.sgemm_f32_get_model(arr, MODEL_MAX))
     return [{"variant": sgemm_f32_variant_name(arr[i].variant),
-             "overhead_us": float(arr[i].overhead_us), "eff": [float(x) for x in arr[i].eff]}
+             "overhead_us": float(arr[i].overhead_us), "eff": [float(x) for x in arr[i].eff],
+             "fill4": float(arr[i].fill4)}
             for i in range(min(n, MODEL_MAX))]
 
 

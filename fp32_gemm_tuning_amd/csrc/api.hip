@@ -66,17 +66,20 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // workgroups breadth-first), the busiest unit holds n = ceil(T / C) tiles;
 // the prediction is a fixed cost (launch, first fill, epilogue) plus that
 // unit's n * 2*BM*BN*K FLOP at a fraction of its peak that depends on n
-// (few tiles per unit leave the matrix cores waiting on fills and barriers).
-// Both were fitted per kernel to interleaved timings of every candidate on
-// 26 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
+// (few tiles per unit leave the matrix cores waiting on fills and barriers),
+// times a per-kernel factor when the operands need 4-byte fills. All three
+// were fitted per kernel to interleaved timings of every candidate on 30
+// shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
 // (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
-// the fastest whole-tile kernel on 23 of them and one within 2% on the rest,
-// with one the fastest of all on 22 and one within 4% on the rest.
+// the fastest whole-tile kernel on 25 of them, with one the fastest of all
+// on 24, in both cases one within 8% on the rest (0.5% and 0.9% lost on
+// average).
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
     double overhead_us;
     double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 tiles per CU
+    double fill4;   // factor on eff when the operands need the 4-byte fill
 };
 
 // The variants the model can choose among: the matrix-core tile kernels,
@@ -103,16 +106,16 @@ struct Model {
 // Built-in model, listed in order of preference when predictions tie.
 static const Model kDefaultModel = {10,
                                     {
-                                        {SGEMM_F32_MFMA_128, 6.0, {0.918, 0.925, 0.939, 0.946}},
-                                        {SGEMM_F32_MFMA_256, 18.5, {1.000, 0.952, 0.968, 0.968}},
-                                        {SGEMM_F32_MFMA_64x128, 7.0, {0.836, 0.871, 0.881, 0.909}},
-                                        {SGEMM_F32_MFMA_64, 4.5, {0.446, 0.595, 0.708, 0.797}},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 9.0, {0.790, 0.775, 0.800, 0.810}},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 9.5, {0.754, 0.729, 0.758, 0.762}},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 10.5, {0.883, 0.860, 0.863, 0.869}},
-                                        {SGEMM_F32_MFMA_128_SK, 17.5, {0.815, 0.949, 0.942, 0.906}},
-                                        {SGEMM_F32_MFMA_64x128_SK, 14.0, {0.803, 0.886, 0.922, 0.879}},
-                                        {SGEMM_F32_MFMA_256_SK, 30.5, {0.927, 0.917, 0.959, 0.959}},
+                                        {SGEMM_F32_MFMA_128, 8.0, {0.954, 0.941, 0.947, 0.948}, 0.82},
+                                        {SGEMM_F32_MFMA_256, 12.0, {0.996, 0.945, 0.969, 0.969}, 0.86},
+                                        {SGEMM_F32_MFMA_64x128, 4.5, {0.766, 0.844, 0.874, 0.904}, 0.70},
+                                        {SGEMM_F32_MFMA_64, 5.5, {0.456, 0.634, 0.700, 0.797}, 0.84},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 8.5, {0.809, 0.758, 0.804, 0.809}, 0.86},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 9.0, {0.757, 0.710, 0.756, 0.767}, 0.84},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 11.0, {0.897, 0.874, 0.861, 0.872}, 0.86},
+                                        {SGEMM_F32_MFMA_128_SK, 16.0, {0.810, 0.931, 0.932, 0.912}, 0.78},
+                                        {SGEMM_F32_MFMA_64x128_SK, 12.5, {0.733, 0.850, 0.993, 0.883}, 0.70},
+                                        {SGEMM_F32_MFMA_256_SK, 30.5, {0.938, 0.920, 0.960, 0.960}, 0.78},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a
@@ -155,6 +158,7 @@ static int choose(const Args& a, int num_cus, size_t ws_bytes) {
     if (!trans && M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
     if (!trans && (double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
     const Model* m = g_model.load(std::memory_order_acquire);
+    const bool vec = vec_ok(a);
     int best = SGEMM_F32_MFMA_128;
     double best_us = 0.0;
     bool found = false;
@@ -165,8 +169,8 @@ static int choose(const Args& a, int num_cus, size_t ws_bytes) {
         if (v.ws_size != nullptr && (ws_bytes == 0 || v.ws_size(a, num_cus) > ws_bytes)) continue;
         const double n = busiest_tiles(v, M, N, K, num_cus);
         if (n <= 0.0) continue;
-        const double us = c.overhead_us +
-                          1e6 * n * 2.0 * v.bm * v.bn * (double)K / (kPeakPerCu * eff_at(c, std::ceil(n)));
+        const double eff = eff_at(c, std::ceil(n)) * (vec ? 1.0 : c.fill4);
+        const double us = c.overhead_us + 1e6 * n * 2.0 * v.bm * v.bn * (double)K / (kPeakPerCu * eff);
         if (!found || us < best_us) {
             best = c.variant;
             best_us = us;
@@ -516,14 +520,16 @@ extern "C" SGEMM_F32_API int sgemm_f32_set_model(const sgemm_f32_model_entry* en
     m->n = n;
     for (int i = 0; i < n; ++i) {
         const sgemm_f32_model_entry& e = entries[i];
-        bool ok = model_variant(e.variant) && e.overhead_us >= 0.0 && e.overhead_us <= 1e6;
+        bool ok = model_variant(e.variant) && e.overhead_us >= 0.0 && e.overhead_us <= 1e6 &&
+                  e.fill4 > 0.0 && e.fill4 <= 1.5;
         for (int b = 0; b < 4; ++b) ok = ok && e.eff[b] > 0.0 && e.eff[b] <= 1.5;
         for (int p = 0; p < i; ++p) ok = ok && entries[p].variant != e.variant;
         if (!ok) {
             delete m;
             return -3;
         }
-        m->c[i] = Candidate{e.variant, e.overhead_us, {e.eff[0], e.eff[1], e.eff[2], e.eff[3]}};
+        m->c[i] = Candidate{e.variant, e.overhead_us, {e.eff[0], e.eff[1], e.eff[2], e.eff[3]},
+                            e.fill4};
     }
     g_model.store(m, std::memory_order_release);
     return 0;
@@ -537,6 +543,7 @@ extern "C" SGEMM_F32_API int sgemm_f32_get_model(sgemm_f32_model_entry* out, int
         out[i].variant = c.variant;
         out[i].overhead_us = c.overhead_us;
         for (int b = 0; b < 4; ++b) out[i].eff[b] = c.eff[b];
+        out[i].fill4 = c.fill4;
     }
     return m->n;
 }

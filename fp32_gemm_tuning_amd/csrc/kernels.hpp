@@ -99,6 +99,12 @@ extern Variant kMfma128, kMfma64, kMfmaSkinny, kMfmaKsplit, kMfmaDirect, kMfma64
 
 // Common host checks.
 bool aligned16(const void* p);
+// Whether the tiled matrix-core kernels can fill both operands with 16-byte
+// loads: the contiguous extent of each operand (K of A, N of B; M of a
+// transposed A, K of a transposed B), both leading dimensions and both base
+// addresses in whole 16-byte chunks. Otherwise they use 4-byte loads, and the
+// dispatch model applies each kernel's 4-byte-fill factor.
+bool vec_ok(const Args& a);
 // Largest workgroup count a 1-D dispatch of `threads`-lane workgroups allows.
 int64_t max_workgroups(int threads);
 // 1 unless the environment sets SGEMM_F32_XCD_REMAP=0 (for measuring the

@@ -934,10 +934,7 @@ static bool extents_ok(const Args& a, int BM, int BN, int BK) {
     return ea < (int64_t)OOB && eb < (int64_t)OOB;
 }
 
-// 16-byte fills need the contiguous extent of each operand (K of A, N of B;
-// M of a transposed A, K of a transposed B), both leading dimensions and
-// both base addresses in whole 16-byte chunks.
-static bool vec_ok(const Args& a) {
+bool vec_ok(const Args& a) {
     const int ca = a.ta ? a.M : a.K, cb = a.tb ? a.K : a.N;
     return !((ca & 3) || (cb & 3) || (a.lda & 3) || (a.ldb & 3) || !aligned16(a.A) ||
              !aligned16(a.B));

@@ -51,7 +51,8 @@ TILE: Dict[str, Tuple[int, int]] = {
 SK_BK: Dict[str, int] = {"mfma_128x128_sk": 32, "mfma_64x128_sk": 32, "mfma_256x256_sk": 16}
 PEAK_PER_CU = 4 * 64 * 2.4e9   # FP32 matrix FLOP/s of one MI355X compute unit
 
-# Shapes the built-in model was fitted on: square, flat, tall, odd, short-K.
+# Shapes the built-in model was fitted on: square, flat, tall, odd, short-K,
+# and the two 8-way row shards of 4096^3 and 8192^3.
 DEFAULT_SHAPES: List[Tuple[int, int, int]] = [
     (512, 512, 512), (768, 768, 768), (1024, 1024, 1024), (1280, 1280, 1280),
     (1536, 1536, 1536), (2048, 2048, 2048), (2560, 2560, 2560), (3072, 3072, 3072),
@@ -59,12 +60,20 @@ DEFAULT_SHAPES: List[Tuple[int, int, int]] = [
     (8192, 8192, 8192), (1000, 1531, 777), (1024, 1536, 768), (1000, 1531, 1500),
     (2000, 1531, 777), (8192, 1024, 8192), (4096, 2048, 4096), (1024, 8192, 1024),
     (3000, 3000, 500), (500, 3000, 3000), (4000, 4000, 256), (2048, 2048, 8192),
-    (1024, 1024, 4096), (2048, 4096, 2048),
+    (1024, 1024, 4096), (2048, 4096, 2048), (1531, 1000, 777), (2050, 2050, 2050),
+    (512, 4096, 4096), (1024, 8192, 8192),
 ]
 QUICK_SHAPES: List[Tuple[int, int, int]] = [
     (1024, 1024, 1024), (1000, 1531, 777), (2048, 2048, 2048), (3072, 3072, 3072),
     (4096, 4096, 4096), (8192, 1024, 8192),
 ]
+
+
+def packed_vec(M: int, N: int, K: int) -> bool:
+    """Whether a packed row-major product (lda = K, ldb = N, 16-byte aligned
+    bases) lets the tile kernels fill with 16-byte loads (the library's
+    vec_ok); otherwise the model applies the kernel's fill4 factor."""
+    return K % 4 == 0 and N % 4 == 0
 
 
 def bucket(n: float) -> int:
@@ -101,18 +110,20 @@ def tiles_per_cu(variant: str, M: int, N: int, num_cus: int, K: int = 0) -> floa
     return float(-(-tiles // cus))
 
 
-def predict_us(entry: dict, M: int, N: int, K: int, num_cus: int,
+def predict_us(entry: dict, M: int, N: int, K: int, num_cus: int, vec: bool = True,
                peak_per_cu: float = PEAK_PER_CU) -> float:
-    """The library's prediction for one model entry (sgemm_f32_model_entry)."""
+    """The library's prediction for one model entry (sgemm_f32_model_entry);
+    `vec`: the operands take 16-byte fills (else fill4 scales eff)."""
     bm, bn = TILE[entry["variant"]]
     n = tiles_per_cu(entry["variant"], M, N, num_cus, K)
     if n <= 0:
         return math.inf
-    return entry["overhead_us"] + 1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * entry["eff"][bucket(n)])
+    eff = entry["eff"][bucket(n)] * (1.0 if vec else entry.get("fill4", 1.0))
+    return entry["overhead_us"] + 1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * eff)
 
 
 def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int,
-           workspace: bool = False) -> str:
+           workspace: bool = False, vec: bool = True) -> str:
     """The entry with the smallest prediction (earlier entries win ties);
     stream-K entries only with a workspace and on shapes they split;
     mfma_128x128 when no entry applies."""
@@ -120,7 +131,7 @@ def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int,
     for e in model:
         if e["variant"] in SK_BK and not workspace:
             continue
-        us = predict_us(e, M, N, K, num_cus)
+        us = predict_us(e, M, N, K, num_cus, vec)
         if us == math.inf:
             continue
         if best is None or us < best_us:
@@ -171,7 +182,8 @@ def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[
         for v in live:
             ts = sorted(times[v])
             ms = ts[len(ts) // 2]
-            out.append({"variant": v, "M": M, "N": N, "K": K, "ms": ms})
+            out.append({"variant": v, "M": M, "N": N, "K": K, "ms": ms,
+                        "vec": packed_vec(M, N, K)})
             if log:
                 log(f"{M}x{N}x{K} {v}: {ms:.4f} ms, {2.0 * M * N * K / ms / 1e9:.1f} TFLOP/s")
         del A, B, C, ws
@@ -179,43 +191,57 @@ def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[
 
 
 def fit(samples: Sequence[dict], num_cus: int, peak_per_cu: float = PEAK_PER_CU,
-        t0_grid_us: Optional[Sequence[float]] = None) -> List[dict]:
-    """Per kernel: fixed cost (from the grid) and per-bucket fractions of peak
-    (medians, at most 1), choosing the fixed cost whose predictions best match
-    the measured times. Buckets without samples borrow the nearest filled one."""
+        t0_grid_us: Optional[Sequence[float]] = None,
+        fill4_grid: Optional[Sequence[float]] = None) -> List[dict]:
+    """Per kernel: fixed cost and 4-byte-fill factor (both from grids) and
+    per-bucket fractions of peak (medians of the measured fractions, those
+    of 4-byte-fill samples divided by the factor; at most 1), choosing the
+    pair whose predictions best match the measured times. Buckets without
+    samples borrow the nearest filled one; a kernel without 4-byte-fill
+    samples keeps fill4 = 1."""
     grid = [0.5 * i for i in range(81)] if t0_grid_us is None else list(t0_grid_us)
-    by_v: Dict[str, List[Tuple[int, float, float]]] = {}
+    # fill4 is searched in [0.7, 1]: a kernel meets only a few 4-byte-fill
+    # shapes in a fit, and unbounded it followed two of them down to 0.58,
+    # which misranked other shapes by up to 10% on MI355X.
+    f4_grid = [0.70 + 0.02 * i for i in range(16)] if fill4_grid is None else list(fill4_grid)
+    by_v: Dict[str, List[Tuple[int, float, float, bool]]] = {}
     for s in samples:
         bm, bn = TILE[s["variant"]]
         n = tiles_per_cu(s["variant"], s["M"], s["N"], num_cus, s["K"])
         work_us = 1e6 * n * 2.0 * bm * bn * s["K"] / peak_per_cu   # at 100% of peak
-        by_v.setdefault(s["variant"], []).append((n, work_us, s["ms"] * 1e3))
+        vec = s.get("vec", packed_vec(s["M"], s["N"], s["K"]))
+        by_v.setdefault(s["variant"], []).append((n, work_us, s["ms"] * 1e3, vec))
     model = []
     for v in TILE:
         ds = by_v.get(v)
         if not ds:
             continue
+        f4s = f4_grid if any(not vec for _, _, _, vec in ds) else [1.0]
         best = None
         for t0 in grid:
-            per_b: Dict[int, List[float]] = {}
-            for n, w, t in ds:
-                # A fraction of peak above 1 is not physical: such a fixed
-                # cost is too large, and the capped rate shows it in the error.
-                e = w / (t - t0) if t > t0 else 1.0
-                per_b.setdefault(bucket(n), []).append(min(1.0, max(1e-3, e)))
-            eff = {b: sorted(x)[len(x) // 2] for b, x in per_b.items()}
-            full = []
-            for b in range(4):
-                if b in eff:
-                    full.append(eff[b])
-                else:
-                    near = min(eff, key=lambda k: (abs(k - b), -k))
-                    full.append(eff[near])
-            err = sum(abs(math.log((t0 + w / full[bucket(n)]) / t)) for n, w, t in ds) / len(ds)
-            if best is None or err < best[0]:
-                best = (err, t0, full)
+            for f4 in f4s:
+                per_b: Dict[int, List[float]] = {}
+                for n, w, t, vec in ds:
+                    # A fraction of peak above 1 is not physical: such a fixed
+                    # cost is too large, and the capped rate shows it in the error.
+                    e = w / (t - t0) if t > t0 else 1.0
+                    e = e if vec else e / f4
+                    per_b.setdefault(bucket(n), []).append(min(1.0, max(1e-3, e)))
+                eff = {b: sorted(x)[len(x) // 2] for b, x in per_b.items()}
+                full = []
+                for b in range(4):
+                    if b in eff:
+                        full.append(eff[b])
+                    else:
+                        near = min(eff, key=lambda k: (abs(k - b), -k))
+                        full.append(eff[near])
+                err = sum(abs(math.log((t0 + w / (full[bucket(n)] * (1.0 if vec else f4))) / t))
+                          for n, w, t, vec in ds) / len(ds)
+                if best is None or err < best[0]:
+                    best = (err, t0, full, f4)
         model.append({"variant": v, "overhead_us": round(best[1], 3),
-                      "eff": [round(x, 4) for x in best[2]], "fit_error": round(best[0], 4)})
+                      "eff": [round(x, 4) for x in best[2]], "fill4": round(best[3], 4),
+                      "fit_error": round(best[0], 4)})
     return model
 
 
@@ -228,7 +254,7 @@ def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[
     res = []
     for (M, N, K), d in by_shape.items():
         sub = [e for e in model if e["variant"] in d]
-        pick = choose(sub, M, N, K, num_cus, workspace=True)
+        pick = choose(sub, M, N, K, num_cus, workspace=True, vec=packed_vec(M, N, K))
         fastest = min(d, key=d.get)
         res.append({"shape": [M, N, K], "picked": pick, "fastest": fastest,
                     "loss": round(d[pick] / d[fastest] - 1.0, 4)})
@@ -237,7 +263,8 @@ def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[
 
 def install(model: Sequence[dict]) -> int:
     """Hand the model to the library; returns its status code."""
-    return sg.sgemm_f32_set_model([{k: e[k] for k in ("variant", "overhead_us", "eff")}
+    return sg.sgemm_f32_set_model([{"variant": e["variant"], "overhead_us": e["overhead_us"],
+                                    "eff": e["eff"], "fill4": e.get("fill4", 1.0)}
                                    for e in model])
 
 
@@ -255,7 +282,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--out", help="write the fitted model here (JSON)")
     ap.add_argument("--load", help="install a saved model and print the plans of the shapes")
-    ap.add_argument("--quick", action="store_true", help="6 shapes instead of 26")
+    ap.add_argument("--quick", action="store_true", help="6 shapes instead of 30")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--calls", type=int, default=4)
     args = ap.parse_args(argv)

@@ -307,9 +307,13 @@ SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int *bm, int *bn, int *bk)
  * Part 2", "Selecting Among Three Kernels"), with measured constants: for a
  * candidate with block tile BM x BN on a device with C compute units, the
  * predicted time in microseconds is
- *     overhead_us + 1e6 * n * 2*BM*BN*K / (614.4e9 * eff[b]),
+ *     overhead_us + 1e6 * n * 2*BM*BN*K / (614.4e9 * eff[b] * f),
  * n = ceil(ceil(M/BM) * ceil(N/BN) / C), b = 0, 1, 2, 3 for n = 1, 2, 3-4, >= 5
- * (614.4e9 FLOP/s is one compute unit's FP32 matrix peak). The smallest
+ * (614.4e9 FLOP/s is one compute unit's FP32 matrix peak), f = 1 when both
+ * operands can be filled with 16-byte loads and f = fill4 when not (a
+ * leading dimension, the contiguous extent of an operand or a base address
+ * that is not a whole number of 16-byte chunks: the kernels then load 4
+ * bytes per lane, several times as many loads per slice). The smallest
  * prediction wins; ties go to the earlier entry. For a stream-K entry n is
  * the busiest unit's share, floor(T/C) whole tiles plus one run of slices
  * (a fraction of a tile), with b taken for ceil(n); stream-K entries are
@@ -327,6 +331,7 @@ typedef struct {
                            MFMA_128_SK, MFMA_64x128_SK or MFMA_256_SK */
     double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
     double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */
+    double fill4;       /* factor on eff for calls that need the 4-byte fill, in (0, 1.5] */
 } sgemm_f32_model_entry;
 
 /* Replace the process-wide dispatch model by entries[0..n). n = 0 restores the

@@ -88,6 +88,10 @@ CASES = [
     (2176, 2176, 250, 1.0, 0.5, "uniform"),
     (700, 600, 16, 1.0, 0.0, "integer"),      # one slice per tile: never split
     (1000, 1531, 777, 1.0, 0.0, "uniform"),
+    # tile grid and K slices exact for all three tiles (the unmasked instance),
+    # still split into pieces that cross tiles
+    (512, 512, 64, 1.0, 0.0, "integer"),
+    (768, 512, 96, 1.0, 0.5, "uniform"),
 ]
 
 

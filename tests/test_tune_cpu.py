@@ -35,6 +35,7 @@ def test_builtin_model_lists_the_tile_kernels_in_order():
     assert [e["variant"] for e in m] == list(tune.TILE)
     for e in m:
         assert e["overhead_us"] >= 0 and all(0 < x <= 1.5 for x in e["eff"])
+        assert 0 < e["fill4"] <= 1.5
 
 
 def test_library_choice_matches_the_tuner_formula():
@@ -43,7 +44,7 @@ def test_library_choice_matches_the_tuner_formula():
     for trial in range(40):
         model = builtin if trial == 0 else [
             {"variant": v, "overhead_us": rng.uniform(0, 30),
-             "eff": [rng.uniform(0.3, 1.0) for _ in range(4)]}
+             "eff": [rng.uniform(0.3, 1.0) for _ in range(4)], "fill4": rng.uniform(0.3, 1.0)}
             for v in rng.sample(list(tune.TILE), rng.randint(1, len(tune.TILE)))]
         assert sg.sgemm_f32_set_model(model) == 0
         for _ in range(25):
@@ -51,14 +52,18 @@ def test_library_choice_matches_the_tuner_formula():
             cus = rng.choice([1, 80, 256, 304])
             if M <= 32 or M * N * K < 64 * 1024 * 1024:
                 continue    # skinny and tiny shapes bypass the model
-            assert _plan(M, N, K, cus) == tune.choose(model, M, N, K, cus), (model, M, N, K, cus)
-            assert _plan_ws(M, N, K, cus) == tune.choose(model, M, N, K, cus, workspace=True), \
+            # odd K or N: 4-byte fills, so each entry's fill4 applies
+            vec = tune.packed_vec(M, N, K)
+            assert _plan(M, N, K, cus) == tune.choose(model, M, N, K, cus, vec=vec), \
                 (model, M, N, K, cus)
+            assert _plan_ws(M, N, K, cus) == tune.choose(model, M, N, K, cus, workspace=True,
+                                                         vec=vec), (model, M, N, K, cus)
 
 
 def test_model_round_trip_and_restore():
-    m = [{"variant": "mfma_64x64", "overhead_us": 3.0, "eff": [0.5, 0.6, 0.7, 0.8]},
-         {"variant": "mfma_128x128", "overhead_us": 12.5, "eff": [0.8, 0.85, 0.9, 0.95]}]
+    m = [{"variant": "mfma_64x64", "overhead_us": 3.0, "eff": [0.5, 0.6, 0.7, 0.8], "fill4": 0.75},
+         {"variant": "mfma_128x128", "overhead_us": 12.5, "eff": [0.8, 0.85, 0.9, 0.95],
+          "fill4": 1.0}]
     assert sg.sgemm_f32_set_model(m) == 0
     assert sg.sgemm_f32_get_model() == m
     assert _plan(4096, 4096, 4096, 256) in ("mfma_64x64", "mfma_128x128")
@@ -72,6 +77,8 @@ def test_model_round_trip_and_restore():
     [{"variant": "mfma_64x64", "overhead_us": -1.0, "eff": [0.5] * 4}],     # negative cost
     [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5, 0.0, 0.5, 0.5]}],
     [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5, 0.5, 2.0, 0.5]}],
+    [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5] * 4, "fill4": 0.0}],
+    [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5] * 4, "fill4": 1.6}],
 ])
 def test_bad_models_are_rejected_and_leave_the_model(bad):
     before = sg.sgemm_f32_get_model()
@@ -154,19 +161,22 @@ def test_workspace_argument_checks():
 
 
 def test_fit_recovers_synthetic_constants():
-    truth = {"mfma_128x128": (11.0, [0.80, 0.87, 0.90, 0.91]),
-             "mfma_64x64": (7.5, [0.52, 0.61, 0.69, 0.78])}
+    truth = {"mfma_128x128": (11.0, [0.80, 0.87, 0.90, 0.91], 0.70),
+             "mfma_64x64": (7.5, [0.52, 0.61, 0.69, 0.78], 0.86)}
     cus = 256
     samples = []
+    assert any(not tune.packed_vec(*s) for s in tune.DEFAULT_SHAPES)
     for (M, N, K) in tune.DEFAULT_SHAPES:
-        for v, (t0, eff) in truth.items():
-            e = {"variant": v, "overhead_us": t0, "eff": eff}
-            samples.append({"variant": v, "M": M, "N": N, "K": K,
-                            "ms": tune.predict_us(e, M, N, K, cus) / 1e3})
+        vec = tune.packed_vec(M, N, K)
+        for v, (t0, eff, f4) in truth.items():
+            e = {"variant": v, "overhead_us": t0, "eff": eff, "fill4": f4}
+            samples.append({"variant": v, "M": M, "N": N, "K": K, "vec": vec,
+                            "ms": tune.predict_us(e, M, N, K, cus, vec) / 1e3})
     model = tune.fit(samples, cus)
     got = {e["variant"]: e for e in model}
-    for v, (t0, eff) in truth.items():
+    for v, (t0, eff, f4) in truth.items():
         assert abs(got[v]["overhead_us"] - t0) <= 0.5
+        assert abs(got[v]["fill4"] - f4) <= 0.02
         for b in range(4):
             assert abs(got[v]["eff"][b] - eff[b]) <= 0.02 * eff[b]
     assert all(r["loss"] == 0.0 for r in tune.check(model, samples, cus))
