@@ -75,7 +75,8 @@ MODEL_MAX = 16
 class ModelEntry(ctypes.Structure):
     """sgemm_f32_model_entry: one candidate of the dispatch model."""
     _fields_ = [("variant", ctypes.c_int), ("overhead_us", ctypes.c_double),
-                ("eff", ctypes.c_double * 4), ("fill4", ctypes.c_double)]
+                ("eff", ctypes.c_double * 4), ("fill4", ctypes.c_double),
+                ("tile_us", ctypes.c_double)]
 
 
 def _load() -> ctypes.CDLL:
@@ -296,8 +297,8 @@ def sgemm_f32_peak_probe(kind: int, workgroups: int, iters: int, out, stream=Non
 def sgemm_f32_set_model(entries) -> int:
     """Replace the dispatch model. `entries`: sequence of dicts with keys
     variant (id or name), overhead_us, eff (4 floats) and optionally fill4
-    (default 1.0); empty or None restores the built-in model. Returns the C
-    status code."""
+    (default 1.0) and tile_us (default 0.0); empty or None restores the
+    built-in model. Returns the C status code."""
     entries = list(entries or [])
     arr = (ModelEntry * max(1, len(entries)))()
     for i, e in enumerate(entries):
@@ -307,6 +308,7 @@ def sgemm_f32_set_model(entries) -> int:
         for b in range(4):
             arr[i].eff[b] = float(e["eff"][b])
         arr[i].fill4 = float(e.get("fill4", 1.0))
+        arr[i].tile_us = float(e.get("tile_us", 0.0))
     return int(_lib.sgemm_f32_set_model(arr, len(entries)))
 
 
@@ -316,7 +318,7 @@ def sgemm_f32_get_model() -> list:
     n = int(_lib.sgemm_f32_get_model(arr, MODEL_MAX))
     return [{"variant": sgemm_f32_variant_name(arr[i].variant),
              "overhead_us": float(arr[i].overhead_us), "eff": [float(x) for x in arr[i].eff],
-             "fill4": float(arr[i].fill4)}
+             "fill4": float(arr[i].fill4), "tile_us": float(arr[i].tile_us)}
             for i in range(min(n, MODEL_MAX))]
 
 

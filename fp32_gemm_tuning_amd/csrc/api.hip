@@ -67,12 +67,13 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // the prediction is a fixed cost (launch, first fill, epilogue) plus that
 // unit's n * 2*BM*BN*K FLOP at a fraction of its peak that depends on n
 // (few tiles per unit leave the matrix cores waiting on fills and barriers),
-// times a per-kernel factor when the operands need 4-byte fills. All three
-// were fitted per kernel to interleaved timings of every candidate on 30
-// shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
+// times a per-kernel factor when the operands need 4-byte fills, plus a
+// fixed cost per tile on that unit (a tile's first fill and epilogue). All
+// four were fitted per kernel to interleaved timings of every candidate on
+// 30 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
 // (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
-// the fastest whole-tile kernel on 25 of them, with one the fastest of all
-// on 24, in both cases one within 8% on the rest (0.5% and 0.9% lost on
+// the fastest whole-tile kernel on 26 of them, with one the fastest of all
+// on 24, in both cases one within 8% on the rest (0.3% and 0.7% lost on
 // average).
 // ---------------------------------------------------------------------------
 struct Candidate {
@@ -80,6 +81,7 @@ struct Candidate {
     double overhead_us;
     double eff[4];  // fraction of peak with n = 1, 2, 3-4, >= 5 tiles per CU
     double fill4;   // factor on eff when the operands need the 4-byte fill
+    double tile_us; // fixed cost per tile (or stream-K run) on the busiest unit
 };
 
 // The variants the model can choose among: the matrix-core tile kernels,
@@ -106,16 +108,16 @@ struct Model {
 // Built-in model, listed in order of preference when predictions tie.
 static const Model kDefaultModel = {10,
                                     {
-                                        {SGEMM_F32_MFMA_128, 8.0, {0.954, 0.941, 0.947, 0.948}, 0.82},
-                                        {SGEMM_F32_MFMA_256, 12.0, {0.996, 0.945, 0.969, 0.969}, 0.86},
-                                        {SGEMM_F32_MFMA_64x128, 4.5, {0.766, 0.844, 0.874, 0.904}, 0.70},
-                                        {SGEMM_F32_MFMA_64, 5.5, {0.456, 0.634, 0.700, 0.797}, 0.84},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 8.5, {0.809, 0.758, 0.804, 0.809}, 0.86},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 9.0, {0.757, 0.710, 0.756, 0.767}, 0.84},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 11.0, {0.897, 0.874, 0.861, 0.872}, 0.86},
-                                        {SGEMM_F32_MFMA_128_SK, 16.0, {0.810, 0.931, 0.932, 0.912}, 0.78},
-                                        {SGEMM_F32_MFMA_64x128_SK, 12.5, {0.733, 0.850, 0.993, 0.883}, 0.70},
-                                        {SGEMM_F32_MFMA_256_SK, 30.5, {0.938, 0.920, 0.960, 0.960}, 0.78},
+                                        {SGEMM_F32_MFMA_128, 0.0, {0.919, 0.947, 0.963, 0.963}, 0.82, 6.0},
+                                        {SGEMM_F32_MFMA_256, 0.0, {0.996, 0.950, 0.974, 0.974}, 0.86, 12.0},
+                                        {SGEMM_F32_MFMA_64x128, 1.5, {0.761, 0.857, 0.903, 0.923}, 0.70, 2.5},
+                                        {SGEMM_F32_MFMA_64, 4.0, {0.451, 0.627, 0.703, 0.819}, 0.86, 1.0},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 2.5, {0.787, 0.787, 0.825, 0.835}, 0.86, 5.0},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 4.5, {0.756, 0.755, 0.775, 0.798}, 0.86, 4.5},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 2.0, {0.892, 0.883, 0.892, 0.890}, 0.86, 8.5},
+                                        {SGEMM_F32_MFMA_128_SK, 11.5, {0.810, 0.954, 0.957, 0.925}, 0.78, 4.5},
+                                        {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.733, 0.892, 1.000, 0.943}, 0.70, 2.5},
+                                        {SGEMM_F32_MFMA_256_SK, 10.5, {0.938, 0.930, 0.972, 0.972}, 0.78, 20.0},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a
@@ -170,7 +172,8 @@ static int choose(const Args& a, int num_cus, size_t ws_bytes) {
         const double n = busiest_tiles(v, M, N, K, num_cus);
         if (n <= 0.0) continue;
         const double eff = eff_at(c, std::ceil(n)) * (vec ? 1.0 : c.fill4);
-        const double us = c.overhead_us + 1e6 * n * 2.0 * v.bm * v.bn * (double)K / (kPeakPerCu * eff);
+        const double us = c.overhead_us + std::ceil(n) * c.tile_us +
+                          1e6 * n * 2.0 * v.bm * v.bn * (double)K / (kPeakPerCu * eff);
         if (!found || us < best_us) {
             best = c.variant;
             best_us = us;
@@ -521,7 +524,7 @@ extern "C" SGEMM_F32_API int sgemm_f32_set_model(const sgemm_f32_model_entry* en
     for (int i = 0; i < n; ++i) {
         const sgemm_f32_model_entry& e = entries[i];
         bool ok = model_variant(e.variant) && e.overhead_us >= 0.0 && e.overhead_us <= 1e6 &&
-                  e.fill4 > 0.0 && e.fill4 <= 1.5;
+                  e.fill4 > 0.0 && e.fill4 <= 1.5 && e.tile_us >= 0.0 && e.tile_us <= 1e4;
         for (int b = 0; b < 4; ++b) ok = ok && e.eff[b] > 0.0 && e.eff[b] <= 1.5;
         for (int p = 0; p < i; ++p) ok = ok && entries[p].variant != e.variant;
         if (!ok) {
@@ -529,7 +532,7 @@ extern "C" SGEMM_F32_API int sgemm_f32_set_model(const sgemm_f32_model_entry* en
             return -3;
         }
         m->c[i] = Candidate{e.variant, e.overhead_us, {e.eff[0], e.eff[1], e.eff[2], e.eff[3]},
-                            e.fill4};
+                            e.fill4, e.tile_us};
     }
     g_model.store(m, std::memory_order_release);
     return 0;
@@ -544,6 +547,7 @@ extern "C" SGEMM_F32_API int sgemm_f32_get_model(sgemm_f32_model_entry* out, int
         out[i].overhead_us = c.overhead_us;
         for (int b = 0; b < 4; ++b) out[i].eff[b] = c.eff[b];
         out[i].fill4 = c.fill4;
+        out[i].tile_us = c.tile_us;
     }
     return m->n;
 }

@@ -119,7 +119,8 @@ def predict_us(entry: dict, M: int, N: int, K: int, num_cus: int, vec: bool = Tr
     if n <= 0:
         return math.inf
     eff = entry["eff"][bucket(n)] * (1.0 if vec else entry.get("fill4", 1.0))
-    return entry["overhead_us"] + 1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * eff)
+    return (entry["overhead_us"] + math.ceil(n) * entry.get("tile_us", 0.0) +
+            1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * eff))
 
 
 def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int,
@@ -192,19 +193,23 @@ def measure(shapes: Iterable[Tuple[int, int, int]], variants: Optional[Sequence[
 
 def fit(samples: Sequence[dict], num_cus: int, peak_per_cu: float = PEAK_PER_CU,
         t0_grid_us: Optional[Sequence[float]] = None,
+        tile_grid_us: Optional[Sequence[float]] = None,
         fill4_grid: Optional[Sequence[float]] = None) -> List[dict]:
-    """Per kernel: fixed cost and 4-byte-fill factor (both from grids) and
-    per-bucket fractions of peak (medians of the measured fractions, those
-    of 4-byte-fill samples divided by the factor; at most 1), choosing the
-    pair whose predictions best match the measured times. Buckets without
-    samples borrow the nearest filled one; a kernel without 4-byte-fill
-    samples keeps fill4 = 1."""
-    grid = [0.5 * i for i in range(81)] if t0_grid_us is None else list(t0_grid_us)
+    """Per kernel: fixed cost per call, fixed cost per tile and 4-byte-fill
+    factor (all three from grids) and per-bucket fractions of peak (medians
+    of the measured fractions once the fixed costs are taken off, those of
+    4-byte-fill samples divided by the factor; at most 1), choosing the
+    triple whose predictions best match the measured times (mean absolute
+    log error). Buckets without samples borrow the nearest filled one; a
+    kernel without 4-byte-fill samples keeps fill4 = 1."""
+    import numpy as np
+    t0s = [0.5 * i for i in range(61)] if t0_grid_us is None else list(t0_grid_us)
+    tts = [0.5 * i for i in range(41)] if tile_grid_us is None else list(tile_grid_us)
     # fill4 is searched in [0.7, 1]: a kernel meets only a few 4-byte-fill
     # shapes in a fit, and unbounded it followed two of them down to 0.58,
     # which misranked other shapes by up to 10% on MI355X.
     f4_grid = [0.70 + 0.02 * i for i in range(16)] if fill4_grid is None else list(fill4_grid)
-    by_v: Dict[str, List[Tuple[int, float, float, bool]]] = {}
+    by_v: Dict[str, List[Tuple[float, float, float, bool]]] = {}
     for s in samples:
         bm, bn = TILE[s["variant"]]
         n = tiles_per_cu(s["variant"], s["M"], s["N"], num_cus, s["K"])
@@ -216,33 +221,39 @@ def fit(samples: Sequence[dict], num_cus: int, peak_per_cu: float = PEAK_PER_CU,
         ds = by_v.get(v)
         if not ds:
             continue
-        f4s = f4_grid if any(not vec for _, _, _, vec in ds) else [1.0]
+        n = np.array([d[0] for d in ds]); w = np.array([d[1] for d in ds])
+        t = np.array([d[2] for d in ds]); vec = np.array([d[3] for d in ds])
+        nc = np.ceil(n)
+        b = np.array([bucket(x) for x in n])
+        filled = sorted(set(b.tolist()))
+        near = [min(filled, key=lambda k: (abs(k - q), -k)) for q in range(4)]
+        f4s = f4_grid if (~vec).any() else [1.0]
         best = None
-        for t0 in grid:
-            for f4 in f4s:
-                per_b: Dict[int, List[float]] = {}
-                for n, w, t, vec in ds:
-                    # A fraction of peak above 1 is not physical: such a fixed
-                    # cost is too large, and the capped rate shows it in the error.
-                    e = w / (t - t0) if t > t0 else 1.0
-                    e = e if vec else e / f4
-                    per_b.setdefault(bucket(n), []).append(min(1.0, max(1e-3, e)))
-                eff = {b: sorted(x)[len(x) // 2] for b, x in per_b.items()}
-                full = []
-                for b in range(4):
-                    if b in eff:
-                        full.append(eff[b])
-                    else:
-                        near = min(eff, key=lambda k: (abs(k - b), -k))
-                        full.append(eff[near])
-                err = sum(abs(math.log((t0 + w / (full[bucket(n)] * (1.0 if vec else f4))) / t))
-                          for n, w, t, vec in ds) / len(ds)
-                if best is None or err < best[0]:
-                    best = (err, t0, full, f4)
-        model.append({"variant": v, "overhead_us": round(best[1], 3),
-                      "eff": [round(x, 4) for x in best[2]], "fill4": round(best[3], 4),
+        for t0 in t0s:
+            for tt in tts:
+                rem = t - t0 - nc * tt
+                # A fraction of peak above 1 is not physical: such fixed costs
+                # are too large, and the capped rate shows it in the error.
+                e_raw = np.where(rem > 0, w / np.where(rem > 0, rem, 1.0), 1.0)
+                for f4 in f4s:
+                    e = np.clip(np.where(vec, e_raw, e_raw / f4), 1e-3, 1.0)
+                    med = {q: _middle(e[b == q]) for q in filled}
+                    full = [med[near[q]] for q in range(4)]
+                    eff = np.array([full[q] for q in b]) * np.where(vec, 1.0, f4)
+                    err = float(np.mean(np.abs(np.log((t0 + nc * tt + w / eff) / t))))
+                    if best is None or err < best[0]:
+                        best = (err, t0, tt, full, f4)
+        model.append({"variant": v, "overhead_us": round(best[1], 3), "tile_us": round(best[2], 3),
+                      "eff": [round(x, 4) for x in best[3]], "fill4": round(best[4], 4),
                       "fit_error": round(best[0], 4)})
     return model
+
+
+def _middle(x) -> float:
+    """The median as the fit takes it: the middle element of the sorted
+    values, the upper of the two middle ones for an even count."""
+    xs = sorted(float(v) for v in x)
+    return xs[len(xs) // 2]
 
 
 def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[dict]:
@@ -264,7 +275,8 @@ def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[
 def install(model: Sequence[dict]) -> int:
     """Hand the model to the library; returns its status code."""
     return sg.sgemm_f32_set_model([{"variant": e["variant"], "overhead_us": e["overhead_us"],
-                                    "eff": e["eff"], "fill4": e.get("fill4", 1.0)}
+                                    "eff": e["eff"], "fill4": e.get("fill4", 1.0),
+                                    "tile_us": e.get("tile_us", 0.0)}
                                    for e in model])
 
 

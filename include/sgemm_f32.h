@@ -307,7 +307,7 @@ SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int *bm, int *bn, int *bk)
  * Part 2", "Selecting Among Three Kernels"), with measured constants: for a
  * candidate with block tile BM x BN on a device with C compute units, the
  * predicted time in microseconds is
- *     overhead_us + 1e6 * n * 2*BM*BN*K / (614.4e9 * eff[b] * f),
+ *     overhead_us + ceil(n) * tile_us + 1e6 * n * 2*BM*BN*K / (614.4e9 * eff[b] * f),
  * n = ceil(ceil(M/BM) * ceil(N/BN) / C), b = 0, 1, 2, 3 for n = 1, 2, 3-4, >= 5
  * (614.4e9 FLOP/s is one compute unit's FP32 matrix peak), f = 1 when both
  * operands can be filled with 16-byte loads and f = fill4 when not (a
@@ -332,6 +332,8 @@ typedef struct {
     double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
     double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */
     double fill4;       /* factor on eff for calls that need the 4-byte fill, in (0, 1.5] */
+    double tile_us;     /* fixed cost per tile (or stream-K run) on the busiest unit, in
+                           [0, 1e4] microseconds: a tile's first fill and its epilogue */
 } sgemm_f32_model_entry;
 
 /* Replace the process-wide dispatch model by entries[0..n). n = 0 restores the

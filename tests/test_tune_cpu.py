@@ -35,7 +35,7 @@ def test_builtin_model_lists_the_tile_kernels_in_order():
     assert [e["variant"] for e in m] == list(tune.TILE)
     for e in m:
         assert e["overhead_us"] >= 0 and all(0 < x <= 1.5 for x in e["eff"])
-        assert 0 < e["fill4"] <= 1.5
+        assert 0 < e["fill4"] <= 1.5 and 0 <= e["tile_us"] <= 1e4
 
 
 def test_library_choice_matches_the_tuner_formula():
@@ -44,7 +44,8 @@ def test_library_choice_matches_the_tuner_formula():
     for trial in range(40):
         model = builtin if trial == 0 else [
             {"variant": v, "overhead_us": rng.uniform(0, 30),
-             "eff": [rng.uniform(0.3, 1.0) for _ in range(4)], "fill4": rng.uniform(0.3, 1.0)}
+             "eff": [rng.uniform(0.3, 1.0) for _ in range(4)], "fill4": rng.uniform(0.3, 1.0),
+             "tile_us": rng.choice([0.0, rng.uniform(0, 20)])}
             for v in rng.sample(list(tune.TILE), rng.randint(1, len(tune.TILE)))]
         assert sg.sgemm_f32_set_model(model) == 0
         for _ in range(25):
@@ -61,9 +62,10 @@ def test_library_choice_matches_the_tuner_formula():
 
 
 def test_model_round_trip_and_restore():
-    m = [{"variant": "mfma_64x64", "overhead_us": 3.0, "eff": [0.5, 0.6, 0.7, 0.8], "fill4": 0.75},
+    m = [{"variant": "mfma_64x64", "overhead_us": 3.0, "eff": [0.5, 0.6, 0.7, 0.8], "fill4": 0.75,
+          "tile_us": 2.5},
          {"variant": "mfma_128x128", "overhead_us": 12.5, "eff": [0.8, 0.85, 0.9, 0.95],
-          "fill4": 1.0}]
+          "fill4": 1.0, "tile_us": 0.0}]
     assert sg.sgemm_f32_set_model(m) == 0
     assert sg.sgemm_f32_get_model() == m
     assert _plan(4096, 4096, 4096, 256) in ("mfma_64x64", "mfma_128x128")
@@ -79,6 +81,8 @@ def test_model_round_trip_and_restore():
     [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5, 0.5, 2.0, 0.5]}],
     [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5] * 4, "fill4": 0.0}],
     [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5] * 4, "fill4": 1.6}],
+    [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5] * 4, "tile_us": -0.5}],
+    [{"variant": "mfma_64x64", "overhead_us": 1.0, "eff": [0.5] * 4, "tile_us": 2e4}],
 ])
 def test_bad_models_are_rejected_and_leave_the_model(bad):
     before = sg.sgemm_f32_get_model()
@@ -161,21 +165,22 @@ def test_workspace_argument_checks():
 
 
 def test_fit_recovers_synthetic_constants():
-    truth = {"mfma_128x128": (11.0, [0.80, 0.87, 0.90, 0.91], 0.70),
-             "mfma_64x64": (7.5, [0.52, 0.61, 0.69, 0.78], 0.86)}
+    truth = {"mfma_128x128": (11.0, [0.80, 0.87, 0.90, 0.91], 0.70, 3.5),
+             "mfma_64x64": (7.5, [0.52, 0.61, 0.69, 0.78], 0.86, 0.0)}
     cus = 256
     samples = []
     assert any(not tune.packed_vec(*s) for s in tune.DEFAULT_SHAPES)
     for (M, N, K) in tune.DEFAULT_SHAPES:
         vec = tune.packed_vec(M, N, K)
-        for v, (t0, eff, f4) in truth.items():
-            e = {"variant": v, "overhead_us": t0, "eff": eff, "fill4": f4}
+        for v, (t0, eff, f4, tt) in truth.items():
+            e = {"variant": v, "overhead_us": t0, "eff": eff, "fill4": f4, "tile_us": tt}
             samples.append({"variant": v, "M": M, "N": N, "K": K, "vec": vec,
                             "ms": tune.predict_us(e, M, N, K, cus, vec) / 1e3})
     model = tune.fit(samples, cus)
     got = {e["variant"]: e for e in model}
-    for v, (t0, eff, f4) in truth.items():
+    for v, (t0, eff, f4, tt) in truth.items():
         assert abs(got[v]["overhead_us"] - t0) <= 0.5
+        assert abs(got[v]["tile_us"] - tt) <= 0.5
         assert abs(got[v]["fill4"] - f4) <= 0.02
         for b in range(4):
             assert abs(got[v]["eff"][b] - eff[b]) <= 0.02 * eff[b]
