@@ -16,12 +16,12 @@
 //   16x16x4: A operand lane l = A[l%16][l/16], B operand = B[l/16][l%16],
 //            result register r of lane l = C[4*(l/16) + r][l%16].
 // The k index inside one MFMA is only a summation index, so each half (or
-// quarter) of the wave walks its own contiguous run of k: lane l feeds the
-// instruction's k slot l/32 (l/16) from k = 8*(l/32) + s (4*(l/16) + s) at
-// step s. A lane's A values for a slice are then 8 (4) consecutive floats of
-// one row of the untransposed A tile, read with 16-byte LDS loads, and no
-// transposed copy of A is needed; the B values are single floats of one row
-// of the B tile, consecutive across lanes.
+// quarter) of the wave walks its own contiguous run of k: in a BK-deep slice
+// lane l feeds the instruction's k slot l/32 (l/16) from k = BK/2*(l/32) + s
+// (BK/4*(l/16) + s) at step s. A lane's A values for a slice are then BK/2
+// (BK/4) consecutive floats of one row of the untransposed A tile, read with
+// 16-byte LDS loads, and no transposed copy of A is needed; the B values are
+// single floats of one row of the B tile, consecutive across lanes.
 //
 // Edges: every global read goes through a buffer resource; masked elements
 // get an out-of-range offset and read as zero, so partial tiles need no
