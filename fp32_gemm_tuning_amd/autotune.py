@@ -4,7 +4,8 @@ The pages tune their kernels by sweeping the block tile, the K slice and the
 per-thread patch, and find that the best choice differs between GPUs ("GEMM
 from scratch", Module 08; "Optimizing Matrix Multiply on CUDA, Part 2",
 "Increasing the Outputs per Thread"). Here those parameters are compile-time
-macros of csrc/mfma.hip, so a sweep builds one copy of the library per
+macros of the matrix-core sources (csrc/mfma_pipe.hip, csrc/mfma_kgroup.hip),
+so a sweep builds one copy of the library per
 configuration and times the kernel the configuration changes:
 
   space "tile" (mfma_128x128): block tile BM x BN, wave tile WM x WN, K
@@ -17,7 +18,7 @@ configuration and times the kernel the configuration changes:
 
 build (on any machine with hipcc; no GPU):
     python -m fp32_gemm_tuning_amd.autotune build --space tile --out DIR [--jobs N]
-  compiles csrc/mfma.hip once per configuration (the other sources are shared
+  compiles the space's source once per configuration (the other sources are shared
   with the in-tree build), links DIR/<config>/libsgemm_f32.so, and writes
   DIR/manifest.json with each configuration's flags, build status and the
   compiler's register / spill report for its kernel. Configurations that fail
@@ -56,6 +57,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SPACES: Dict[str, dict] = {
     "tile": {
         "variant": "mfma_128x128",
+        "source": "mfma_pipe.hip",
         "kernel": "k_mfma_pipeILi{SGEMM_M128_BM}ELi{SGEMM_M128_BN}ELi{SGEMM_M128_WM}ELi{SGEMM_M128_WN}E",
         "params": {
             "SGEMM_M128_BM,SGEMM_M128_BN": [(128, 128), (64, 128), (128, 64), (256, 128),
@@ -68,6 +70,7 @@ SPACES: Dict[str, dict] = {
     },
     "pipe": {
         "variant": "mfma_256x256",
+        "source": "mfma_pipe.hip",
         "kernel": "k_mfma_pipeILi{SGEMM_M256_BM}ELi{SGEMM_M256_BN}ELi{SGEMM_M256_WM}ELi{SGEMM_M256_WN}E",
         "params": {
             "SGEMM_M256_BM,SGEMM_M256_BN": [(256, 256), (256, 128), (128, 256), (128, 128)],
@@ -79,6 +82,7 @@ SPACES: Dict[str, dict] = {
     },
     "kg96": {
         "variant": "mfma_64x96_kg4",
+        "source": "mfma_kgroup.hip",
         "kernel": "k_mfma_kgroup",
         "params": {"SGEMM_KG96_BK": [16, 32]},
     },
@@ -184,13 +188,15 @@ def build(space: str, out: str, jobs: int = 4, limit: Optional[int] = None, log=
     b = _build_module()
     b.build(jobs=jobs)                       # the shared objects, current
     os.makedirs(out, exist_ok=True)
+    source = SPACES[space]["source"]
     shared = [os.path.join(b.BUILD, os.path.splitext(s)[0] + ".o") for s in b.SOURCES
-              if s != "mfma.hip"]
+              if s != source]
+
     def one(c):
         name = config_name(space, c)
         d = os.path.join(out, name)
         os.makedirs(d, exist_ok=True)
-        src, obj, rc, text, cmd = b._compile("mfma.hip", d, tuple(flags(c)))
+        src, obj, rc, text, cmd = b._compile(source, d, tuple(flags(c)))
         entry = {"name": name, "space": space, "config": c, "flags": flags(c), "built": rc == 0}
         if rc != 0:
             entry["error"] = [ln for ln in text.splitlines() if "error" in ln][:3]

@@ -26,7 +26,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsgemm_f32.so")
 ARCH = os.environ.get("SGEMM_F32_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "ladder.hip", "valu_main.hip", "mfma.hip", "peak.hip"]
+SOURCES = ["api.hip", "ladder.hip", "valu_main.hip", "mfma_pipe.hip", "mfma_kgroup.hip",
+           "mfma_small.hip", "peak.hip"]
 
 CXXFLAGS = [
     f"--offload-arch={ARCH}",

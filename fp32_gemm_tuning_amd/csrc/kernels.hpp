@@ -93,7 +93,7 @@ hipError_t launch_scale(const Args& a, hipStream_t s);
 extern Variant kNaive, kCoalesced, kLdsTiled, kReg1d, kReg2d, kVec4TransA;
 // valu_main.hip
 extern Variant kValuMain;
-// mfma.hip
+// mfma_pipe.hip, mfma_kgroup.hip, mfma_small.hip
 extern Variant kMfma128, kMfma64, kMfmaSkinny, kMfmaKsplit, kMfmaDirect, kMfma64x128,
     kMfma256, kMfmaKgroup, kMfmaKgroup96, kMfmaKgroup128, kMfma128Sk, kMfma64x128Sk, kMfma256Sk;
 

@@ -1,0 +1,635 @@
+// The pipelined FP32 matrix-core kernel (k_mfma_pipe, body PipeCore) and its
+// instances: mfma_256x256, mfma_128x128 and mfma_64x128, with their stream-K
+// forms (k_mfma_pipe_sk, summed by k_sk_fixup). Operand layouts and edge
+// handling: mfma_common.hpp.
+#include "mfma_common.hpp"
+
+namespace sgemm {
+
+// ===========================================================================
+// Tile parameters of mfma_128x128 and mfma_64x128, two instances of the
+// pipelined kernel below (k_mfma_pipe), set at compile time so that the
+// autotuner (fp32_gemm_tuning_amd/autotune.py) can sweep them. mfma_128x128
+// is BM = BN = 128 with 8 waves of 64x32 (32 accumulator registers per
+// lane), BK = 32, and an occupancy target of 4 waves per SIMD (2 workgroups
+// per compute unit); mfma_64x128 is 64x128 with 4 waves of 64x32, BK = 32
+// and 3 workgroups per compute unit. The block and wave tiles came from a sweep of the earlier
+// single-buffered tile kernel on MI355X; moved onto the pipelined kernel
+// they gain 3-20% (2048^3 122.6 -> 130.5, 512x4096x4096 108.8 -> 130.5
+// TFLOP/s) and lose 4% only on the 1000x1531x777 odd shape, which the
+// dispatch gives to a K-group kernel.
+// ===========================================================================
+#ifndef SGEMM_M128_BK
+#define SGEMM_M128_BK 32
+#endif
+#ifndef SGEMM_M128_WAVES_PER_EU
+#define SGEMM_M128_WAVES_PER_EU 4
+#endif
+#ifndef SGEMM_M128_BM
+#define SGEMM_M128_BM 128
+#endif
+#ifndef SGEMM_M128_BN
+#define SGEMM_M128_BN 128
+#endif
+#ifndef SGEMM_M128_WM
+#define SGEMM_M128_WM 64
+#endif
+#ifndef SGEMM_M128_WN
+#define SGEMM_M128_WN 32
+#endif
+#ifndef SGEMM_M64x128_WM
+#define SGEMM_M64x128_WM 64
+#endif
+#ifndef SGEMM_M64x128_WN
+#define SGEMM_M64x128_WN 32
+#endif
+#ifndef SGEMM_M64x128_BK
+#define SGEMM_M64x128_BK 32
+#endif
+constexpr int M128_BM = SGEMM_M128_BM, M128_BN = SGEMM_M128_BN, M128_BK = SGEMM_M128_BK;
+constexpr int M128_WM = SGEMM_M128_WM, M128_WN = SGEMM_M128_WN;
+
+// ---------------------------------------------------------------------------
+// Stream-K (SkPlan in common.hpp). A run of slices that covers a whole tile
+// writes C directly; any other run leaves its partial tile in the workspace,
+// and a second kernel on the same stream (k_sk_fixup) sums the pieces of
+// each split tile in K order -- so the result does not depend on which
+// piece finished first -- and writes C. The kernel boundary orders the
+// partial stores before their reads. (The pages let the unit that computes
+// a tile's last piece combine the pieces inside the one kernel. On MI355X
+// that needs a release fence per piece and an acquire per tile at device
+// scope, and each of those writes back or invalidates a whole XCD's L2,
+// which cost 13-37 us per call at 1536^3-3072^3, against a few us for the
+// second launch.)
+//
+// Partial tiles travel as 16-byte vectors: vector q of thread t of a BM x BN
+// tile is at float offset (q * NT + t) * 4 of its slot, so each access of a
+// wave is 1 KiB contiguous, and the fixup kernel, with the same thread
+// layout, reads back exactly the values each of its threads owns.
+// ---------------------------------------------------------------------------
+template <int BI, int BJ, int NT>
+struct PartialIo {
+    static constexpr int Q = BI * BJ * 4;   // 16-byte vectors per lane
+
+    __device__ __forceinline__ static void put(float* slot, int t, const f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
+            *(f32x4*)(slot + ((size_t)q * NT + t) * 4) =
+                f32x4{acc[bi][bj][r0], acc[bi][bj][r0 + 1], acc[bi][bj][r0 + 2], acc[bi][bj][r0 + 3]};
+        }
+    }
+
+    // acc = slot (FIRST) or acc += slot, one 32x32 block at a time (the asm
+    // pin keeps the compiler from loading a whole partial tile at once).
+    template <bool FIRST>
+    __device__ __forceinline__ static void gather(const float* slot, int t, f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int bi = q / (4 * BJ), bj = (q / 4) % BJ, r0 = (q % 4) * 4;
+            const f32x4 v = *(const f32x4*)(slot + ((size_t)q * NT + t) * 4);
+            if (FIRST) {
+                acc[bi][bj][r0] = v.x;
+                acc[bi][bj][r0 + 1] = v.y;
+                acc[bi][bj][r0 + 2] = v.z;
+                acc[bi][bj][r0 + 3] = v.w;
+            } else {
+                acc[bi][bj][r0] += v.x;
+                acc[bi][bj][r0 + 1] += v.y;
+                acc[bi][bj][r0 + 2] += v.z;
+                acc[bi][bj][r0 + 3] += v.w;
+            }
+            if (q % 4 == 3) asm volatile("" : "+v"(acc[bi][bj])::"memory");
+        }
+    }
+};
+
+// Slot of workgroup jj's piece of split tile st: its first run (slot 2jj)
+// if that run starts in the tile, else its last run (slot 2jj+1).
+__device__ __forceinline__ int sk_slot(const SkPlan& p, int jj, int st) {
+    return (jj * p.upw >= st * p.slices) ? 2 * jj : 2 * jj + 1;
+}
+
+// ===========================================================================
+// The same tile with a software-pipelined slice and an LDS ring of STAGES
+// slices. Each BK = 16 slice is split into two halves of four MFMA k-steps,
+// and every wave holds two fragment register sets, so the LDS reads of one
+// half are in flight while the MFMAs of the other half run. The workgroup
+// barrier sits between the two halves of a slice: before it, each wave has
+// finished reading the slice's stage and its own buffer-to-LDS loads of the
+// next slice have landed (loads of later slices may still be in flight);
+// after it, the loads of the slice STAGES ahead are issued into the stage
+// just released, and the first half of the next slice is read while the
+// second half of this one is multiplied. A lone wave on a SIMD then never
+// waits on an LDS round trip between MFMAs, and a global load has STAGES - 1
+// slices of time to land.
+// ===========================================================================
+// The instruction order within one scheduling region of the pipelined slice:
+// a part's MFMAs with the LDS fragment reads of the next part woven in, one
+// read after every two MFMAs, and, with LOADS > 0, that many of the slice's
+// buffer-to-LDS loads spread over the region, each after a group of three
+// reads. Issued in one burst right after the workgroup barrier, the reads of
+// sixteen waves fill the LDS command queue, and the loads' scalar set-up
+// holds every wave of a SIMD at once; woven in, a ready MFMA is always at
+// hand (about 2.5% at 4096^3 and 8192^3, bit-identical results: the MFMA
+// order per accumulator is unchanged). Instructions past the pattern's counts
+// (the transposed and 4-byte-fill instances read and load more) are placed
+// by the scheduler.
+template <int LOADS>
+__device__ __forceinline__ void weave_half() {
+    constexpr int MFMA = 0x008, VMEM_READ = 0x020, DS_READ = 0x100;
+    if constexpr (LOADS == 0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+        }
+    } else {
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(VMEM_READ, 1, 0);
+        }
+    }
+    __builtin_amdgcn_sched_group_barrier(MFMA, 64, 0);   // the rest
+}
+
+template <int BI, int BJ>
+struct PartFrag {
+    f32x4 a[BI];      // A operands of the part's 4 k-steps, per row block
+    float b[BJ][4];   // B operands of the part's 4 k-steps, per column block
+};
+
+// Workgroup barrier of the LDS ring: waits until at most VMCNT of this wave's
+// vector-memory operations (buffer-to-LDS loads of later slices, issued after
+// the ones that must have landed) are outstanding and all of its LDS reads
+// are done, then synchronises the workgroup. A fence would wait for every
+// outstanding load, so the compiler is instead kept from moving memory
+// accesses across the barrier by empty asm statements with a memory clobber.
+// s_waitcnt immediate (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8.
+template <int VMCNT>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(VMCNT >= 0 && VMCNT < 64, "vmcnt field is 6 bits");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VMCNT & 15) | ((VMCNT >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The body of k_mfma_pipe, shared with its stream-K form: the product of
+// slices [s_begin, s_end) of one tile through the LDS ring, and the
+// epilogue. On return every load issued into the ring has landed and every
+// wave has passed the last barrier, so the ring may be refilled.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool VEC, bool FULL, bool TA,
+          bool TB>
+struct PipeCore {
+    static_assert(BK == 16 || BK == 32, "slices of 16 or 32 k");
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0,
+                  "wave tiles are whole 32x32 blocks that divide the block tile");
+    static_assert((BM / WM) * (BN / WN) * 64 <= 1024, "at most 16 waves per workgroup");
+    static constexpr int P = BK / 8;   // parts of 4 MFMA k-steps per slice
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NT = (BM / WM) * WAVES_N * 64;
+    static constexpr int BI = WM / 32, BJ = WN / 32;
+    using Dma = TileFillDma<BM, BN, BK, NT, VEC, TA, TB>;
+    static constexpr int BNP = Dma::BNP, APITCH = BK;
+    // Deeper rings count outstanding loads, which must then be the same on
+    // every wave; with two stages the barrier waits for all of them.
+    static_assert(Dma::EVEN || STAGES == 2, "the ring barrier counts the same loads on every wave");
+    static constexpr int G = Dma::A_INSTR + Dma::B_INSTR;   // loads per wave per slice
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
+    static_assert((STAGES - 2) * G < 64, "outstanding loads exceed vmcnt");
+    // The prologue leaves the later stages' loads in flight only when every
+    // wave issues the same G loads per slice (G is the largest per-wave
+    // count; a wave that issues fewer must wait for all of its own) and the
+    // count fits the 6-bit field.
+    static constexpr int PROLOGUE_VMCNT = (Dma::EVEN && (STAGES - 1) * G < 64) ? (STAGES - 1) * G : 0;
+    static constexpr int LDS_A = BM * APITCH, LDS_B = BK * BNP;
+
+    int m0, n0, rows_valid, cols_valid, t, wm, wn, h, c;
+
+    __device__ __forceinline__ PipeCore(const Args& a, int tm, int tn, int tid = threadIdx.x) {
+        // The tile coordinates are workgroup-uniform; the integer divisions
+        // of the tile mapping leave them in vector registers, and a buffer
+        // resource built from a vector register costs a per-lane loop around
+        // every load, so move them to scalar registers explicitly.
+        m0 = __builtin_amdgcn_readfirstlane(tm * BM);
+        n0 = __builtin_amdgcn_readfirstlane(tn * BN);
+        rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+        cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+        t = tid;
+        const int lane = t & 63, w = t >> 6;
+        wm = w / WAVES_N;
+        wn = w % WAVES_N;
+        h = lane >> 5;
+        c = lane & 31;
+    }
+
+    __device__ __forceinline__ static void zero(f32x16 (&acc)[BI][BJ]) {
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    }
+
+    __device__ __forceinline__ void mainloop(const Args& a, int s_begin, int s_end,
+                                             float* const (&Ast)[4], float* const (&Bst)[4],
+                                             f32x16 (&acc)[BI][BJ]) const {
+        // Lanes 0-31 take k = s and lanes 32-63 take k = BK/2 + s at MFMA step s
+        // of the slice; part v covers steps 4v .. 4v+3, i.e. 16-byte chunk
+        // P*h + v of a k-contiguous row ([row][k], swizzled: A, or B stored
+        // transposed) and rows BK/2*h + 4v .. BK/2*h + 4v + 3 of a row-contiguous
+        // stage ([k][row]: B, or A stored transposed). A chunk address of part v
+        // is xrow + ((xchunk ^ v) << 2), computed per read (one XOR and one
+        // shift-or, hidden under the MFMAs) rather than held in P registers per
+        // block.
+        int arow[BI], achunk[BI], brow[BJ], bchunk[BJ];
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi) {
+            const int row = wm * WM + bi * 32 + c;
+            arow[bi] = TA ? (BK / 2) * h * BM + row : row * APITCH;
+            achunk[bi] = (P * h) ^ swz_chunk<BK>(row);
+        }
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj) {
+            const int col = wn * WN + bj * 32 + c;
+            brow[bj] = TB ? col * BK : (BK / 2) * h * BNP + col;
+            bchunk[bj] = (P * h) ^ swz_chunk<BK>(col);
+        }
+
+        auto read_part = [&](PartFrag<BI, BJ>& f, const float* Ac, const float* Bc, int v) {
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi) {
+                if constexpr (TA) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) f.a[bi][k] = Ac[arow[bi] + (4 * v + k) * BM];
+                } else {
+                    f.a[bi] = *(const f32x4*)&Ac[arow[bi] + ((achunk[bi] ^ v) << 2)];
+                }
+            }
+            if constexpr (TB) {
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj) {
+                    const f32x4 q = *(const f32x4*)&Bc[brow[bj] + ((bchunk[bj] ^ v) << 2)];
+                    f.b[bj][0] = q.x; f.b[bj][1] = q.y; f.b[bj][2] = q.z; f.b[bj][3] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj) f.b[bj][k] = Bc[brow[bj] + (4 * v + k) * BNP];
+            }
+        };
+        auto mma_part = [&](const PartFrag<BI, BJ>& f, int k_begin = 0, int k_end = 4) {
+#pragma unroll
+            for (int k = k_begin; k < k_end; ++k)
+#pragma unroll
+                for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < BJ; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[bi][k], f.b[bj][k],
+                                                                           acc[bi][bj], 0, 0, 0);
+        };
+
+        const Dma dma;
+        PartFrag<BI, BJ> f0, f1;
+        // Prologue: fill every stage (stages past the last slice read zeros),
+        // wait for slice 0, read its first half. Every slice below issues exactly
+        // G loads per wave, whether or not its target slice exists, so the count
+        // of loads issued after any given one is the same on every path.
+#pragma unroll
+        for (int j = 0; j < STAGES; ++j)
+            dma.template issue<FULL>(a, t, m0, n0, (s_begin + j) * BK, rows_valid, cols_valid, Ast[j],
+                                     Bst[j]);
+        ring_barrier<PROLOGUE_VMCNT>();
+        read_part(f0, Ast[0], Bst[0], 0);
+
+        // Slice s lives in stage (Ac, Bc), slice s + 1 in (An, Bn); on entry f0
+        // holds (or is loading) part 0 of slice s; parts alternate between f0
+        // and f1 (P is even, so the last part is in f1). The barrier comes after
+        // the reads of the last part and before its MFMAs; at the barrier the
+        // loads of slices s + 2 .. s + STAGES - 1 may still be in flight.
+        // Each part's MFMAs form one scheduling region with the reads of the
+        // next part (and, after the barrier, the loads of slice s + STAGES),
+        // ordered by weave_half; scheduling fences keep the regions apart (the
+        // scheduler would otherwise hoist the barrier, with its wait on the
+        // reads just issued, above the MFMAs, or pull MFMAs up next to the
+        // reads they depend on).
+        auto slice = [&](int s, float* Ac, float* Bc, const float* An, const float* Bn) {
+#pragma unroll
+            for (int v = 0; v + 1 < P; ++v) {
+                if (v & 1)
+                    read_part(f0, Ac, Bc, v + 1);
+                else
+                    read_part(f1, Ac, Bc, v + 1);
+                if (v & 1)
+                    mma_part(f1);
+                else
+                    mma_part(f0);
+                weave_half<0>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            ring_barrier<(STAGES - 2) * G>();
+            read_part(f0, An, Bn, 0);   // past the last slice: read and unused
+            mma_part(f1);
+            dma.template issue<FULL>(a, t, m0, n0, (s + STAGES) * BK, rows_valid, cols_valid, Ac, Bc);
+            weave_half<2>();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // Whole rounds of STAGES slices, free of conditionals, then the rest.
+        int s0 = s_begin;
+        for (; s0 + STAGES <= s_end; s0 += STAGES) {
+#pragma unroll
+            for (int j = 0; j < STAGES; ++j)
+                slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+        }
+#pragma unroll
+        for (int j = 0; j < STAGES - 1; ++j)
+            if (s0 + j < s_end)
+                slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+        // The zero-filling loads issued for slices past the end must land before
+        // the workgroup's LDS can be handed to another workgroup.
+        ring_barrier<0>();
+
+    }
+
+    __device__ __forceinline__ void store(const Args& a, const f32x16 (&acc)[BI][BJ]) const {
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int j = wn * WN + bj * 32 + c;
+                    if (i < rows_valid && j < cols_valid)
+                        store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+                }
+    }
+};
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
+          bool TA = false, bool TB = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB>;
+    // One LDS object per stage, so that the compiler can tell the stage being
+    // filled from the stages being read (unused stages are dropped).
+    __shared__ __attribute__((aligned(16))) float As0[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs0[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As1[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs1[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? Core::LDS_B : 4];
+    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? Core::LDS_B : 4];
+    float* const Ast[4] = {As0, As1, As2, As3};
+    float* const Bst[4] = {Bs0, Bs1, Bs2, Bs3};
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+    const Core core(a, tm, tn);
+    f32x16 acc[Core::BI][Core::BJ];
+    Core::zero(acc);
+    core.mainloop(a, 0, (a.K + BK - 1) / BK, Ast, Bst, acc);
+    core.store(a, acc);
+}
+
+// Stream-K form of k_mfma_pipe (SkPlan in common.hpp): workgroups below
+// p.dp_tiles compute whole tiles; the others their runs of slices, a run
+// covering a whole tile writing C, the others their partial tiles (summed by
+// k_sk_fixup).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
+          bool TA = false, bool TB = false>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
+    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB>;
+    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
+    __shared__ __attribute__((aligned(16))) float As0[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs0[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As1[Core::LDS_A];
+    __shared__ __attribute__((aligned(16))) float Bs1[Core::LDS_B];
+    __shared__ __attribute__((aligned(16))) float As2[STAGES > 2 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs2[STAGES > 2 ? Core::LDS_B : 4];
+    __shared__ __attribute__((aligned(16))) float As3[STAGES > 3 ? Core::LDS_A : 4];
+    __shared__ __attribute__((aligned(16))) float Bs3[STAGES > 3 ? Core::LDS_B : 4];
+    float* const Ast[4] = {As0, As1, As2, As3};
+    float* const Bst[4] = {Bs0, Bs1, Bs2, Bs3};
+
+    const int b = blockIdx.x;
+    f32x16 acc[Core::BI][Core::BJ];
+    int tm, tn;
+    if (b < p.dp_tiles) {
+        tile_of_first(b, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0, tm, tn);
+        const Core core(a, tm, tn);
+        Core::zero(acc);
+        core.mainloop(a, 0, p.slices, Ast, Bst, acc);
+        core.store(a, acc);
+        return;
+    }
+    const int j = b - p.dp_tiles;
+    const int U = p.sk_tiles * p.slices;
+    int u = j * p.upw;
+    const int u_end = (u + p.upw) < U ? (u + p.upw) : U;
+    while (u < u_end) {
+        const int st = u / p.slices;
+        const int s0 = u - st * p.slices;
+        const int s1 = (s0 + (u_end - u)) < p.slices ? (s0 + (u_end - u)) : p.slices;
+        tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M,
+                      xcd_remap != 0, tm, tn);
+        // The lane's fragment and epilogue offsets derive from its thread
+        // index; hidden from the compiler here, they are recomputed per run
+        // instead of being hoisted out of the loop (and spilled).
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const Core core(a, tm, tn, tid);
+        Core::zero(acc);
+        core.mainloop(a, s0, s1, Ast, Bst, acc);
+        if (s0 == 0 && s1 == p.slices)
+            core.store(a, acc);
+        else
+            Io::put(p.partials + (size_t)sk_slot(p, j, st) * BM * BN, core.t, acc);
+        u += s1 - s0;
+    }
+}
+
+// One workgroup per split tile: the sum of its pieces in K order, then the
+// epilogue. A tile covered by a single run was written by that run.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
+void k_sk_fixup(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
+    using Core = PipeCore<BM, BN, WM, WN, 16, 2, true, false, false, false>;
+    using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
+    const int st = blockIdx.x;
+    const int j0 = st * p.slices / p.upw, j1 = (st * p.slices + p.slices - 1) / p.upw;
+    if (j0 == j1) return;
+    int tm, tn;
+    tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M, xcd_remap != 0,
+                  tm, tn);
+    const Core core(a, tm, tn);
+    f32x16 acc[Core::BI][Core::BJ];
+    constexpr size_t TILE = (size_t)BM * BN;
+    Io::template gather<true>(p.partials + (size_t)sk_slot(p, j0, st) * TILE, core.t, acc);
+    for (int jj = j0 + 1; jj <= j1; ++jj)
+        Io::template gather<false>(p.partials + (size_t)sk_slot(p, jj, st) * TILE, core.t, acc);
+    core.store(a, acc);
+}
+
+bool vec_ok(const Args& a) {
+    const int ca = a.ta ? a.M : a.K, cb = a.tb ? a.K : a.N;
+    return !((ca & 3) || (cb & 3) || (a.lda & 3) || (a.ldb & 3) || !aligned16(a.A) ||
+             !aligned16(a.B));
+}
+
+// mfma_256x256 tile parameters: the pipelined kernel with a 256x256 block
+// tile, 16 waves of 64x64 (four per SIMD, all of one workgroup), one
+// workgroup per compute unit (2 x 32 KiB LDS stages). With every wave of a
+// compute unit in one workgroup there is no staggered finish between
+// workgroups sharing a SIMD, and the A and B panels are read from L2 half as
+// often as with 128x128 tiles.
+#ifndef SGEMM_M256_BM
+#define SGEMM_M256_BM 256
+#endif
+#ifndef SGEMM_M256_BN
+#define SGEMM_M256_BN 256
+#endif
+#ifndef SGEMM_M256_WM
+#define SGEMM_M256_WM 64
+#endif
+#ifndef SGEMM_M256_WN
+#define SGEMM_M256_WN 64
+#endif
+#ifndef SGEMM_M256_WPE
+#define SGEMM_M256_WPE 4
+#endif
+#ifndef SGEMM_M256_STAGES
+#define SGEMM_M256_STAGES 2
+#endif
+#ifndef SGEMM_M256_BK
+#define SGEMM_M256_BK 16
+#endif
+
+// An instance of the pipelined kernel (k_mfma_pipe, and k_mfma_pipe_sk for
+// stream-K): block tile, wave tile, K slice, LDS stages and occupancy
+// target. Per call it picks the FULL form (tile grid and K slices exactly
+// cover the problem: no range masks) or the masked one, and the 16-byte or
+// 4-byte fill (vec_ok). The 4-byte-fill form keeps more loads in flight per
+// lane; it targets 3 waves per SIMD, or as many as one workgroup puts on
+// each SIMD if that is more, since it would spill at 4.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE>
+struct PipeInstance {
+    static constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    static constexpr int kBM = BM, kBN = BN, kBK = BK;
+    static constexpr int WPE4 = NT / 256 > 3 ? NT / 256 : 3;
+
+    static const void* kernel() {
+        return (const void*)k_mfma_pipe<BM, BN, WM, WN, BK, STAGES, WPE, true, false>;
+    }
+    static const void* sk_kernel() {
+        return (const void*)k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, WPE, true, false>;
+    }
+    static int check(const Args& a) {
+        if (!extents_ok(a, BM, BN, BK)) return SGEMM_F32_ERR_TOO_LARGE;
+        const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
+        return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+    }
+    // f(VEC, FULL, TA, TB), each a std::integral_constant<bool>.
+    template <class F>
+    static hipError_t forms(const Args& a, F&& f) {
+        using T = std::true_type;
+        using N = std::false_type;
+        const bool vec = vec_ok(a);
+        const bool full = a.M % BM == 0 && a.N % BN == 0 && a.K % BK == 0;
+        return with_trans(a, [&](auto ta, auto tb) {
+            if (vec && full) return f(T{}, T{}, ta, tb);
+            if (vec) return f(T{}, N{}, ta, tb);
+            return f(N{}, N{}, ta, tb);
+        });
+    }
+    static hipError_t launch(const Args& a, hipStream_t s) {
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
+        return forms(a, [&](auto vec, auto full, auto ta, auto tb) {
+            constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
+            hipLaunchKernelGGL((k_mfma_pipe<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
+                                            decltype(ta)::value, decltype(tb)::value>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+            return hipGetLastError();
+        });
+    }
+
+    // Stream-K: one workgroup per whole tile of the first rounds, then the
+    // stream-K workgroups (sk_split), then k_sk_fixup on the same stream.
+    static SkSplit split(const Args& a, int cus) {
+        return sk_split(cdiv(a.M, BM) * cdiv(a.N, BN), cdiv(a.K, BK), cus);
+    }
+    static size_t ws_size(const Args& a, int cus) { return sk_workspace_bytes(split(a, cus), BM, BN); }
+    static hipError_t launch_ws(const Args& a, void* ws, size_t ws_bytes, int cus, hipStream_t s) {
+        const SkSplit sp = split(a, cus);
+        if (!sp.split()) return launch(a, s);
+        if (ws == nullptr || ws_bytes < sk_workspace_bytes(sp, BM, BN)) return hipErrorInvalidValue;
+        SkPlan p;
+        p.dp_tiles = (int)sp.dp_tiles;
+        p.sk_tiles = (int)sp.sk_tiles;
+        p.sk_wgs = (int)sp.sk_wgs;
+        p.upw = (int)sp.upw;
+        p.slices = (int)sp.slices;
+        p.partials = (float*)ws;
+        const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
+        const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(NT);
+        const hipError_t e = forms(a, [&](auto vec, auto full, auto ta, auto tb) {
+            constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
+            hipLaunchKernelGGL((k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
+                                               decltype(ta)::value, decltype(tb)::value>),
+                               grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
+            return hipGetLastError();
+        });
+        // Runs as long as a tile (upw == slices) cover whole tiles only.
+        if (e != hipSuccess || p.upw == p.slices) return e;
+        hipLaunchKernelGGL((k_sk_fixup<BM, BN, WM, WN>), dim3((unsigned)p.sk_tiles), block, 0, s, a,
+                           tm, tn, xcd_remap_enabled(), p);
+        return hipGetLastError();
+    }
+};
+
+using Pipe256 = PipeInstance<SGEMM_M256_BM, SGEMM_M256_BN, SGEMM_M256_WM, SGEMM_M256_WN,
+                             SGEMM_M256_BK, SGEMM_M256_STAGES, SGEMM_M256_WPE>;
+using Pipe128 = PipeInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK, 2,
+                             SGEMM_M128_WAVES_PER_EU>;
+// Two 24 KiB LDS stages per 4-wave workgroup: three workgroups per compute
+// unit, so three waves per SIMD.
+using Pipe64x128 =
+    PipeInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK, 2, 3>;
+
+Variant kMfma256 = {"mfma_256x256", Pipe256::check, Pipe256::launch, Pipe256::kernel(),
+                    Pipe256::NT, true, nullptr, nullptr, Pipe256::kBM, Pipe256::kBN, Pipe256::kBK};
+Variant kMfma128 = {"mfma_128x128", Pipe128::check, Pipe128::launch, Pipe128::kernel(),
+                    Pipe128::NT, true, nullptr, nullptr, Pipe128::kBM, Pipe128::kBN, Pipe128::kBK};
+// 64x128: twice the tiles of mfma_128x128 for medium shapes (e.g. 3072^3,
+// whose 576 tiles of 128x128 leave the second round of workgroups a third
+// full).
+Variant kMfma64x128 = {"mfma_64x128", Pipe64x128::check, Pipe64x128::launch,
+                       Pipe64x128::kernel(), Pipe64x128::NT, true, nullptr, nullptr,
+                       Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK};
+// Stream-K forms (they need a workspace: sgemm_f32_ws).
+Variant kMfma256Sk = {"mfma_256x256_sk", Pipe256::check, nullptr, Pipe256::sk_kernel(),
+                      Pipe256::NT, true, Pipe256::ws_size, Pipe256::launch_ws,
+                      Pipe256::kBM, Pipe256::kBN, Pipe256::kBK};
+Variant kMfma128Sk = {"mfma_128x128_sk", Pipe128::check, nullptr, Pipe128::sk_kernel(),
+                      Pipe128::NT, true, Pipe128::ws_size, Pipe128::launch_ws,
+                      Pipe128::kBM, Pipe128::kBN, Pipe128::kBK};
+Variant kMfma64x128Sk = {"mfma_64x128_sk", Pipe64x128::check, nullptr, Pipe64x128::sk_kernel(),
+                         Pipe64x128::NT, true, Pipe64x128::ws_size, Pipe64x128::launch_ws,
+                         Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK};
+
+}  // namespace sgemm

@@ -1,0 +1,515 @@
+// FP32 matrix-core kernels for shapes the tiled kernels serve badly:
+// mfma_64x64 (small tiles), mfma_64x64_k4 (in-workgroup K split),
+// mfma_direct (tiny products, no LDS) and mfma_skinny (M <= 32, HBM-bound).
+// Operand layouts and edge handling: mfma_common.hpp.
+#include "mfma_common.hpp"
+
+namespace sgemm {
+
+// ===========================================================================
+// mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2
+// blocks of 16x16 accumulated with v_mfma_f32_16x16x4_f32. Four times as many
+// tiles as mfma_128 for shapes whose 128x128 grid leaves compute units idle.
+// ===========================================================================
+constexpr int M64_BM = 64, M64_BN = 64, M64_BK = 16, M64_GROUP_M = 8;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_mfma64(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    constexpr int BM = M64_BM, BN = M64_BN, BK = M64_BK;
+    using Fill = TileFill<BM, BN, BK, 256, VEC>;
+    constexpr int BNP = Fill::BNP;
+    __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BNP];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, M64_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int g = lane >> 4, c = lane & 15;
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int aoff[2], boff[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int row = wm * 32 + bi * 16 + c;
+        aoff[bi] = row * BK + ((g ^ swz16(row)) << 2);
+    }
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) boff[bj] = (4 * g) * BNP + wn * 32 + bj * 16 + c;
+
+    const int nslices = (a.K + BK - 1) / BK;
+    Fill fill;
+    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
+    fill.store(As[0], Bs[0], t);
+    __syncthreads();
+
+    for (int s = 0; s < nslices; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
+        const float* Ac = As[cur];
+        const float* Bc = Bs[cur];
+        f32x4 af[2];
+        float bf[2][4];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) af[bi] = *(const f32x4*)&Ac[aoff[bi]];
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[bi][k], bf[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+        if (s + 1 < nslices) fill.store(As[cur ^ 1], Bs[cur ^ 1], t);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = wm * 32 + bi * 16 + 4 * g + r;
+                const int j = wn * 32 + bj * 16 + c;
+                if (i < rows_valid && j < cols_valid)
+                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
+            }
+}
+
+static int check_mfma64(const Args& a) {
+    if (!extents_ok(a, M64_BM, M64_BN, M64_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, M64_BM) * cdiv(a.N, M64_BN);
+    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_mfma64(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, M64_BM), tn = (int)cdiv(a.N, M64_BN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
+    if (vec_ok(a))
+        hipLaunchKernelGGL(k_mfma64<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL(k_mfma64<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfma64 = {"mfma_64x64", check_mfma64, launch_mfma64, (const void*)k_mfma64<true>,
+                   256, false, nullptr, nullptr, M64_BM, M64_BN, M64_BK};
+
+// ===========================================================================
+// mfma_64x64_k4: a 64x64 tile whose 4 waves split every 64-deep K slice four
+// ways. Wave w multiplies k = 16w .. 16w+15 of each slice into its own full
+// 64x64 accumulator (2x2 blocks of v_mfma_f32_32x32x2_f32), so each wave
+// issues 32 MFMAs (2048 matrix-core cycles) per barrier -- four times the
+// work of mfma_64x64 -- which hides fill latency with only one or two
+// workgroups per compute unit. This is the pages' split-K idea ("Optimizing
+// Matrix Multiply on CUDA, Part 2", "Selecting Among Three Kernels") moved
+// inside the workgroup: the four partial tiles are summed through LDS in a
+// fixed order (w = 0, 1, 2, 3), so no global workspace is needed and the
+// result is deterministic.
+// ===========================================================================
+constexpr int KS_BM = 64, KS_BN = 64, KS_WAVES = 4, KS_BK = 16 * KS_WAVES, KS_GROUP_M = 8;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_mfma_ksplit(Args a, int tiles_m, int tiles_n,
+                                                     int xcd_remap) {
+    constexpr int BM = KS_BM, BN = KS_BN, BK = KS_BK;
+    using Fill = TileFill<BM, BN, BK, 256, VEC>;
+    constexpr int BNP = Fill::BNP;
+    constexpr int STAGE = BM * BK + BK * BNP;  // floats per LDS stage
+    static_assert(2 * STAGE >= KS_WAVES * 4 * 16 * 64, "reduction buffer must fit in the stages");
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, KS_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Wave w, half h: k = 16w + 8h + s (s = 0..7) of each slice.
+    const int kb = 16 * w + 8 * h;
+    int aoff[2][2], boff[2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+        const int row = bi * 32 + c;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) aoff[bi][v] = row * BK + (((kb / 4 + v) ^ swz_chunk<BK>(row)) << 2);
+    }
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) boff[bj] = kb * BNP + bj * 32 + c;
+
+    const int nslices = (a.K + BK - 1) / BK;
+    Fill fill;
+    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
+    fill.store(smem, smem + BM * BK, t);
+    __syncthreads();
+
+    for (int s = 0; s < nslices; ++s) {
+        const int cur = s & 1;
+        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
+        const float* Ac = smem + cur * STAGE;
+        const float* Bc = Ac + BM * BK;
+        float af[2][8], bf[2][8];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+            const f32x4 lo = *(const f32x4*)&Ac[aoff[bi][0]];
+            const f32x4 hi = *(const f32x4*)&Ac[aoff[bi][1]];
+            af[bi][0] = lo.x; af[bi][1] = lo.y; af[bi][2] = lo.z; af[bi][3] = lo.w;
+            af[bi][4] = hi.x; af[bi][5] = hi.y; af[bi][6] = hi.z; af[bi][7] = hi.w;
+        }
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bi][k], bf[bj][k],
+                                                                       acc[bi][bj], 0, 0, 0);
+        if (s + 1 < nslices) {
+            float* An = smem + (cur ^ 1) * STAGE;
+            fill.store(An, An + BM * BK, t);
+        }
+        __syncthreads();
+    }
+
+    // Fixed-order reduction: every wave parks its 4 blocks in LDS as
+    // red[w][block][r][lane]; wave w then sums block w over the 4 waves.
+    float* red = smem;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[((w * 4 + bi * 2 + bj) * 16 + r) * 64 + lane] = acc[bi][bj][r];
+    __syncthreads();
+    const int bi = w >> 1, bj = w & 1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        float v = red[((0 * 4 + w) * 16 + r) * 64 + lane];
+#pragma unroll
+        for (int ww = 1; ww < KS_WAVES; ++ww) v += red[((ww * 4 + w) * 16 + r) * 64 + lane];
+        const int i = bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int j = bj * 32 + c;
+        if (i < rows_valid && j < cols_valid) store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+    }
+}
+
+static int check_ksplit(const Args& a) {
+    if (!extents_ok(a, KS_BM, KS_BN, KS_BK)) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, KS_BM) * cdiv(a.N, KS_BN);
+    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_ksplit(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, KS_BM), tn = (int)cdiv(a.N, KS_BN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
+    if (vec_ok(a))
+        hipLaunchKernelGGL(k_mfma_ksplit<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL(k_mfma_ksplit<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfmaKsplit = {"mfma_64x64_k4", check_ksplit, launch_ksplit,
+                       (const void*)k_mfma_ksplit<true>, 256};
+
+// ===========================================================================
+// mfma_direct: small and medium shapes. A workgroup of KS waves owns a TM x TN
+// tile of C; wave w takes the 16-deep k steps w, w + KS, w + 2*KS, ... and
+// accumulates the whole tile for them (TM/32 x TN/32 blocks of
+// v_mfma_f32_32x32x2_f32). Operands go straight from global memory (L2) into
+// MFMA registers -- there is no LDS tile and no barrier inside the K loop, so
+// the waves run independently and hide latency with a register double buffer
+// (step j+KS is loaded while step j is multiplied). With the k-permuted
+// operand layout a lane's A values are 8 consecutive floats of one row and its
+// B values are rows of 32 consecutive columns across the half-wave. At the end
+// the KS partial tiles are summed through LDS in the fixed order w = 0..KS-1.
+// Fine tiles (32x32) spread a few-tile shape evenly over the compute
+// units; this is the pages' split-K ("Optimizing Matrix Multiply on CUDA,
+// Part 2", "Selecting Among Three Kernels") kept inside the workgroup.
+// ===========================================================================
+#ifndef SGEMM_DIRECT_TM
+#define SGEMM_DIRECT_TM 32
+#endif
+#ifndef SGEMM_DIRECT_TN
+#define SGEMM_DIRECT_TN 32
+#endif
+#ifndef SGEMM_DIRECT_KS
+#define SGEMM_DIRECT_KS 4
+#endif
+constexpr int DR_TM = SGEMM_DIRECT_TM, DR_TN = SGEMM_DIRECT_TN, DR_KS = SGEMM_DIRECT_KS;
+constexpr int DR_GROUP_M = 8;
+
+template <int TM, int TN, bool VEC>
+struct DirectFrag {
+    static constexpr int BI = TM / 32, BJ = TN / 32;
+    float a[BI][8];
+    float b[BJ][8];
+
+    // Step starting at k0: lane (h, c) reads A[m0 + 32*bi + c][k0 + 8h + 0..7]
+    // and B[k0 + 8h + s][n0 + 32*bj + c]; everything outside the matrix reads 0.
+    __device__ __forceinline__ void load(const Args& a_, int m0, int n0, int k0, int rows_valid,
+                                         int cols_valid, int h, int c) {
+        const int kk = (a_.K - k0) < 16 ? (a_.K - k0) : 16;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            a_.A + (int64_t)m0 * a_.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a_.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+            a_.B + (int64_t)k0 * a_.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a_.ldb + cols_valid) * 4));
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi) {
+            const int row = 32 * bi + c;
+            const bool rok = row < rows_valid;
+            if (VEC) {
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const int kq = 8 * h + 4 * v;
+                    const f32x4 x = buf_load4(rA, rok && kq + 4 <= kk ? (uint32_t)((row * (int)a_.lda + kq) * 4) : OOB);
+                    a[bi][4 * v + 0] = x.x; a[bi][4 * v + 1] = x.y;
+                    a[bi][4 * v + 2] = x.z; a[bi][4 * v + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int kq = 8 * h + s;
+                    a[bi][s] = buf_load1(rA, rok && kq < kk ? (uint32_t)((row * (int)a_.lda + kq) * 4) : OOB);
+                }
+            }
+        }
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj) {
+            const int col = 32 * bj + c;
+            const bool cok = col < cols_valid;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int kr = 8 * h + s;
+                b[bj][s] = buf_load1(rB, cok && kr < kk ? (uint32_t)((kr * (int)a_.ldb + col) * 4) : OOB);
+            }
+        }
+    }
+};
+
+template <int TM, int TN, int KS, bool VEC>
+__global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, int tiles_n,
+                                                         int xcd_remap) {
+    constexpr int BI = TM / 32, BJ = TN / 32, NB = BI * BJ;
+    __shared__ float red[KS * NB * 16 * 64];
+
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, DR_GROUP_M, xcd_remap != 0, tm, tn);
+    const int m0 = tm * TM, n0 = tn * TN;
+    const int rows_valid = (a.M - m0) < TM ? (a.M - m0) : TM;
+    const int cols_valid = (a.N - n0) < TN ? (a.N - n0) : TN;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = lane >> 5, c = lane & 31;
+
+    f32x16 acc[BI][BJ];
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < BJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nsteps = (a.K + 15) / 16;
+    DirectFrag<TM, TN, VEC> cur, nxt;
+    if (w < nsteps) cur.load(a, m0, n0, 16 * w, rows_valid, cols_valid, h, c);
+    for (int j = w; j < nsteps; j += KS) {
+        if (j + KS < nsteps) nxt.load(a, m0, n0, 16 * (j + KS), rows_valid, cols_valid, h, c);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[bi][s], cur.b[bj][s],
+                                                                       acc[bi][bj], 0, 0, 0);
+        cur = nxt;
+    }
+
+    // Fixed-order reduction over the KS waves: red[w][block][r][lane].
+#pragma unroll
+    for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                red[((w * NB + bi * BJ + bj) * 16 + r) * 64 + lane] = acc[bi][bj][r];
+    __syncthreads();
+    for (int blk = w; blk < NB; blk += KS) {
+        const int bi = blk / BJ, bj = blk % BJ;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float v = red[((0 * NB + blk) * 16 + r) * 64 + lane];
+#pragma unroll
+            for (int ww = 1; ww < KS; ++ww) v += red[((ww * NB + blk) * 16 + r) * 64 + lane];
+            const int i = bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int jj = bj * 32 + c;
+            if (i < rows_valid && jj < cols_valid)
+                store_out(a, (int64_t)m0 + i, (int64_t)n0 + jj, v);
+        }
+    }
+}
+
+static int check_direct(const Args& a) {
+    const int64_t ea = ((int64_t)(DR_TM - 1) * a.lda + 16) * 4;
+    const int64_t eb = ((int64_t)15 * a.ldb + DR_TN) * 4;
+    if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, DR_TM) * cdiv(a.N, DR_TN);
+    return tiles <= max_workgroups(64 * DR_KS) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_direct(const Args& a, hipStream_t s) {
+    const int tm = (int)cdiv(a.M, DR_TM), tn = (int)cdiv(a.N, DR_TN);
+    const dim3 grid((unsigned)((int64_t)tm * tn)), block(64 * DR_KS);
+    const bool vec = !((a.K & 3) || (a.lda & 3) || !aligned16(a.A));
+    if (vec)
+        hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, true>), grid, block, 0, s, a, tm, tn,
+                           xcd_remap_enabled());
+    else
+        hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, false>), grid, block, 0, s, a, tm, tn,
+                           xcd_remap_enabled());
+    return hipGetLastError();
+}
+
+Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
+                       (const void*)k_mfma_direct<DR_TM, DR_TN, DR_KS, true>, 64 * DR_KS};
+
+// ===========================================================================
+// mfma_skinny: for few rows (near-GEMV, e.g. 16 x 8192 x 8192, where B is
+// read once and the shape is bound by HBM bandwidth). A workgroup owns a
+// 16x32 tile of C and all of K; its 16 waves each take one contiguous 1/16 of
+// K, so 16 independent streams of B loads are in flight per compute unit.
+// Operands go straight from global memory into MFMA registers (no LDS tile):
+// lane l of a wave reads row k = 4*(l/16) + s of its K run at column l%16 of
+// each 16-column block, 64 contiguous bytes per quarter-wave, and a 16-byte
+// run of 4 consecutive k of row l%16 of A. At the end the 16 partial tiles
+// are summed in a fixed order through LDS (deterministic) and the epilogue
+// writes C.
+// ===========================================================================
+constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KU = 64;  // k per unrolled step
+
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int kchunk) {
+    __shared__ float red[SK_WAVES][2][4][64];
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int m0 = tm * SK_BM, n0 = tn * SK_BN;
+    const int rows_valid = (a.M - m0) < SK_BM ? (a.M - m0) : SK_BM;
+    const int cols_valid = (a.N - n0) < SK_BN ? (a.N - n0) : SK_BN;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = lane >> 4, c = lane & 15;
+    const int kbeg = w * kchunk;
+    const int kend = (a.K - kbeg) < kchunk ? a.K : kbeg + kchunk;
+
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = kbeg; k0 < kend; k0 += SK_KU) {
+        const int kk = (a.K - k0) < SK_KU ? (a.K - k0) : SK_KU;  // rows present in memory
+        const int klim = kend - k0;                              // rows this wave owns
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
+            a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+            a.B + (int64_t)k0 * a.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
+        f32x4 af[SK_KU / 16];
+        float b0[SK_KU / 4], b1[SK_KU / 4];
+#pragma unroll
+        for (int u = 0; u < SK_KU / 16; ++u) {
+            const int kq = 16 * u + 4 * g;  // this lane's 4 consecutive k
+            if (VEC) {
+                const bool ok = c < rows_valid && kq + 4 <= klim;
+                af[u] = buf_load4(rA, ok ? (uint32_t)((c * (int)a.lda + kq) * 4) : OOB);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = c < rows_valid && kq + e < klim;
+                    af[u][e] = buf_load1(rA, ok ? (uint32_t)((c * (int)a.lda + kq + e) * 4) : OOB);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kr = kq + e;
+                const bool okr = kr < klim;
+                const uint32_t base = (uint32_t)(kr * (int)a.ldb) * 4;
+                b0[4 * u + e] = buf_load1(rB, okr && c < cols_valid ? base + c * 4 : OOB);
+                b1[4 * u + e] = buf_load1(rB, okr && c + 16 < cols_valid ? base + (c + 16) * 4 : OOB);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SK_KU / 16; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b0[4 * u + e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b1[4 * u + e], acc1, 0, 0, 0);
+            }
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        red[w][0][r][lane] = acc0[r];
+        red[w][1][r][lane] = acc1[r];
+    }
+    __syncthreads();
+    if (threadIdx.x < SK_BM * SK_BN) {
+        const int i = threadIdx.x / SK_BN, j = threadIdx.x % SK_BN;
+        const int bj = j >> 4, src = (i >> 2) * 16 + (j & 15), r = i & 3;
+        float v = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < SK_WAVES; ++ww) v += red[ww][bj][r][src];
+        if (i < rows_valid && j < cols_valid) store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+    }
+}
+
+static int skinny_kchunk(const Args& a) {
+    // Equal K runs per wave, each a multiple of 16.
+    const int64_t per = cdiv(a.K, SK_WAVES);
+    return (int)(cdiv(per, 16) * 16);
+}
+
+static int check_skinny(const Args& a) {
+    const int64_t ea = ((int64_t)(SK_BM - 1) * a.lda + SK_KU) * 4;
+    const int64_t eb = ((int64_t)(SK_KU - 1) * a.ldb + SK_BN) * 4;
+    if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
+    const int64_t tiles = cdiv(a.M, SK_BM) * cdiv(a.N, SK_BN);
+    return tiles <= max_workgroups(1024) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
+}
+
+static hipError_t launch_skinny(const Args& a, hipStream_t s) {
+    const int tn = (int)cdiv(a.N, SK_BN);
+    const dim3 grid((unsigned)(cdiv(a.M, SK_BM) * tn)), block(1024);
+    const bool vec = !((a.K & 3) || (a.lda & 3) || !aligned16(a.A));
+    if (vec)
+        hipLaunchKernelGGL(k_mfma_skinny<true>, grid, block, 0, s, a, tn, skinny_kchunk(a));
+    else
+        hipLaunchKernelGGL(k_mfma_skinny<false>, grid, block, 0, s, a, tn, skinny_kchunk(a));
+    return hipGetLastError();
+}
+
+Variant kMfmaSkinny = {"mfma_skinny", check_skinny, launch_skinny,
+                             (const void*)k_mfma_skinny<true>, 1024};
+
+}  // namespace sgemm

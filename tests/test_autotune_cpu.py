@@ -19,7 +19,14 @@ def _autotune():
 
 
 at = _autotune()
-MFMA_SRC = open(os.path.join(ROOT, "fp32_gemm_tuning_amd", "csrc", "mfma.hip")).read()
+CSRC = os.path.join(ROOT, "fp32_gemm_tuning_amd", "csrc")
+
+
+def _space_source(space):
+    # The space's source file and the header every matrix-core source
+    # includes (where the macros a space sets are defined).
+    return (open(os.path.join(CSRC, at.SPACES[space]["source"])).read() +
+            open(os.path.join(CSRC, "mfma_common.hpp")).read())
 
 
 @pytest.mark.parametrize("space", sorted(at.SPACES))
@@ -27,8 +34,9 @@ def test_first_configuration_is_the_in_tree_build(space):
     # Every macro a space sets exists in the kernel source with the first
     # value of its list as the default, so configuration 0 is the control.
     c = at.configs(space)[0]
+    src = _space_source(space)
     for macro, value in c.items():
-        assert f"#define {macro} {value}\n" in MFMA_SRC, macro
+        assert f"#define {macro} {value}\n" in src, macro
 
 
 @pytest.mark.parametrize("space", sorted(at.SPACES))
