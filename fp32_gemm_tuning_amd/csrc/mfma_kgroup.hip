@@ -2,7 +2,7 @@
 // mfma_64x96_kg4 and mfma_128x128_kg4, one tile per workgroup of four groups
 // of waves that split the K slices and sum their partial tiles in a fixed
 // order. Operand layouts and edge handling: mfma_common.hpp.
-#include "mfma_common.hpp"
+#include "mfma_pipecore.hpp"
 
 namespace sgemm {
 
@@ -128,35 +128,52 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // This group's part of a stage starts at g * BM * BK (A) and
-    // g * BK * BNP (B).
-    const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, g * BM * BK, g * BK * BNP);
-    auto compute = [&](const float* Ac, const float* Bc) { mma(Ac, Bc, acc); };
-
-    // Step i: group g multiplies slice i*KG + g from the current stage while
-    // its loads of slice (i+1)*KG + g fill the other one; one workgroup
-    // barrier per step (it also waits for each wave's loads).
+    // g * BK * BNP (B). With 16-byte fills each group runs the pipelined main
+    // loop (PipeCore) over its slices g, g + KG, g + 2 KG, ...; the ring's
+    // barriers are the workgroup's, so every group takes the same number of
+    // steps, and a group's slices past the end of K load as zeros. With
+    // 4-byte fills (several times as many loads per slice, and more
+    // registers in flight) the plain double-buffered loop below is faster:
+    // the pipelined one measured 2-5% slower there, and it spilled in the
+    // 64x64-wave groups.
     const int nslices = (a.K + BK - 1) / BK;
-    const int nsteps = (nslices + KG - 1) / KG;
-    const Dma dma;
-    auto step = [&](int i, float* Acur, float* Bcur, float* Anext, float* Bnext) {
-        const int s = i * KG + g;
-        if (s + KG < nslices)
-            dma.issue(a, tl, m0, n0, (s + KG) * BK, rows_valid, cols_valid, Anext + g * BM * BK,
-                      Bnext + g * BK * BNP);
-        if (s < nslices) compute(Acur, Bcur);
+    if constexpr (VEC) {
+        using Core = PipeCore<BM, BN, WM, WN, BK, 2, true, false, TA, TB>;
+        static_assert(Core::NT == GT && Core::LDS_A == BM * BK && Core::LDS_B == BK * BNP,
+                      "the group's pipeline works in the group's part of each stage");
+        const Core core(a, tm, tn, tl);
+        float* const Ast[4] = {As0 + g * BM * BK, As1 + g * BM * BK, nullptr, nullptr};
+        float* const Bst[4] = {Bs0 + g * BK * BNP, Bs1 + g * BK * BNP, nullptr, nullptr};
+        core.template mainloop<KG>(a, 0, (nslices + KG - 1) / KG, Ast, Bst, acc, g);
+    } else {
+        const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, g * BM * BK, g * BK * BNP);
+        auto compute = [&](const float* Ac, const float* Bc) { mma(Ac, Bc, acc); };
+
+        // Step i: group g multiplies slice i*KG + g from the current stage while
+        // its loads of slice (i+1)*KG + g fill the other one; one workgroup
+        // barrier per step (it also waits for each wave's loads).
+        const int nsteps = (nslices + KG - 1) / KG;
+        const Dma dma;
+        auto step = [&](int i, float* Acur, float* Bcur, float* Anext, float* Bnext) {
+            const int s = i * KG + g;
+            if (s + KG < nslices)
+                dma.issue(a, tl, m0, n0, (s + KG) * BK, rows_valid, cols_valid, Anext + g * BM * BK,
+                          Bnext + g * BK * BNP);
+            if (s < nslices) compute(Acur, Bcur);
+            __syncthreads();
+        };
+        if (g < nslices)
+            dma.issue(a, tl, m0, n0, g * BK, rows_valid, cols_valid, As0 + g * BM * BK,
+                      Bs0 + g * BK * BNP);
         __syncthreads();
-    };
-    if (g < nslices)
-        dma.issue(a, tl, m0, n0, g * BK, rows_valid, cols_valid, As0 + g * BM * BK,
-                  Bs0 + g * BK * BNP);
-    __syncthreads();
-    for (int i = 0; i < nsteps; i += 2) {
-        step(i, As0, Bs0, As1, Bs1);
-        if (i + 1 < nsteps) step(i + 1, As1, Bs1, As0, Bs0);
+        for (int i = 0; i < nsteps; i += 2) {
+            step(i, As0, Bs0, As1, Bs1);
+            if (i + 1 < nsteps) step(i + 1, As1, Bs1, As0, Bs0);
+        }
     }
 
-    // Fixed-order reduction of the four partial tiles (the last step's
-    // barrier has retired every read of the stages).
+    // Fixed-order reduction of the four partial tiles (the main loop's last
+    // barrier has retired every read of the stages and every load into them).
     // Two-level tree in a fixed order, (p0 + p2) + (p1 + p3), through the
     // stages: each wave holds at most one partial tile besides its own. The
     // accumulators of a lane travel as 16-byte vectors; vector q of thread tl
