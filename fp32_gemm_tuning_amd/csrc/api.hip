@@ -72,8 +72,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // four were fitted per kernel to interleaved timings of every candidate on
 // 30 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
 // (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
-// the fastest whole-tile kernel on 26 of them, with one the fastest of all
-// on 24, in both cases one within 8% on the rest (0.3% and 0.7% lost on
+// the fastest whole-tile kernel on 28 of them, with one the fastest of all
+// on 23, in both cases one within 8% on the rest (0.1% and 0.6% lost on
 // average).
 // ---------------------------------------------------------------------------
 struct Candidate {
@@ -108,16 +108,16 @@ struct Model {
 // Built-in model, listed in order of preference when predictions tie.
 static const Model kDefaultModel = {10,
                                     {
-                                        {SGEMM_F32_MFMA_128, 0.0, {0.919, 0.947, 0.963, 0.963}, 0.82, 6.0},
-                                        {SGEMM_F32_MFMA_256, 0.0, {0.996, 0.950, 0.974, 0.974}, 0.86, 12.0},
-                                        {SGEMM_F32_MFMA_64x128, 1.5, {0.761, 0.857, 0.903, 0.923}, 0.70, 2.5},
-                                        {SGEMM_F32_MFMA_64, 4.0, {0.451, 0.627, 0.703, 0.819}, 0.86, 1.0},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 2.5, {0.787, 0.787, 0.825, 0.835}, 0.86, 5.0},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 4.5, {0.756, 0.755, 0.775, 0.798}, 0.86, 4.5},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 2.0, {0.892, 0.883, 0.892, 0.890}, 0.86, 8.5},
-                                        {SGEMM_F32_MFMA_128_SK, 11.5, {0.810, 0.954, 0.957, 0.925}, 0.78, 4.5},
-                                        {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.733, 0.892, 1.000, 0.943}, 0.70, 2.5},
-                                        {SGEMM_F32_MFMA_256_SK, 10.5, {0.938, 0.930, 0.972, 0.972}, 0.78, 20.0},
+                                        {SGEMM_F32_MFMA_128, 0.0, {0.903, 0.919, 0.952, 0.920}, 0.84, 6.0},
+                                        {SGEMM_F32_MFMA_256, 0.0, {0.996, 0.953, 0.962, 0.962}, 0.86, 12.0},
+                                        {SGEMM_F32_MFMA_64x128, 0.5, {0.754, 0.866, 0.884, 0.909}, 0.70, 3.0},
+                                        {SGEMM_F32_MFMA_64, 3.5, {0.450, 0.627, 0.682, 0.785}, 0.86, 1.0},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 0.5, {0.786, 0.817, 0.833, 0.861}, 0.82, 5.5},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 3.0, {0.742, 0.771, 0.771, 0.806}, 0.84, 5.0},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 0.0, {0.911, 0.908, 0.941, 0.916}, 0.84, 10.5},
+                                        {SGEMM_F32_MFMA_128_SK, 11.5, {0.801, 0.941, 0.959, 0.907}, 0.80, 4.5},
+                                        {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.713, 0.869, 1.000, 0.903}, 0.70, 2.5},
+                                        {SGEMM_F32_MFMA_256_SK, 9.5, {0.919, 0.917, 0.970, 0.970}, 0.78, 20.0},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a
