@@ -123,6 +123,14 @@ SMALL = [
     # one K slice only, and exactly two (the pipelined kernel's LDS ring)
     (260, 270, 16, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
     (257, 300, 32, 1.0, 0.5, "uniform", (0, 4, 0), (0, 0, 0)),
+    # whole tiles (the unmasked instances) with one and two slices of 16 and
+    # one of 32
+    (256, 256, 16, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
+    (256, 256, 32, 1.0, 0.5, "uniform", (0, 0, 0), (0, 0, 0)),
+    # 16-byte fills with K below one slice: all but the first K-group see
+    # only slices past the end
+    (130, 132, 4, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
+    (96, 128, 20, 1.0, 0.25, "uniform", (0, 0, 0), (0, 0, 0)),
 ]
 
 
