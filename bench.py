@@ -42,6 +42,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["fp32_gemm_tuning_amd/csrc/mfma_pipe.hip", "fp32_gemm_tuning_amd/csrc/mfma_kgroup.hip",
                   "fp32_gemm_tuning_amd/csrc/mfma_small.hip", "fp32_gemm_tuning_amd/csrc/mfma_common.hpp",
+                  "fp32_gemm_tuning_amd/csrc/mfma_pipecore.hpp",
                   "fp32_gemm_tuning_amd/csrc/valu_main.hip",
                   "fp32_gemm_tuning_amd/csrc/common.hpp", "fp32_gemm_tuning_amd/csrc/ladder.hip"]
 

@@ -60,7 +60,7 @@ VARIANTS = ("naive", "coalesced", "lds_tiled", "reg1d", "reg2d", "vec4_transa", 
             "mfma_128x128", "mfma_64x64", "mfma_skinny", "mfma_64x64_k4", "mfma_direct",
             "mfma_64x128", "mfma_256x256", "mfma_64x128_kg4",
             "mfma_64x96_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
-            "mfma_256x256_sk")
+            "mfma_256x256_sk", "mfma_96x64_kg4")
 
 
 class SgemmError(RuntimeError):

@@ -17,7 +17,7 @@ static const Variant* const kTable[SGEMM_F32_NUM_VARIANTS] = {
     &kNaive, &kCoalesced, &kLdsTiled, &kReg1d, &kReg2d, &kVec4TransA,
     &kValuMain, &kMfma128, &kMfma64, &kMfmaSkinny, &kMfmaKsplit, &kMfmaDirect, &kMfma64x128,
     &kMfma256, &kMfmaKgroup, &kMfmaKgroup96, &kMfmaKgroup128, &kMfma128Sk, &kMfma64x128Sk,
-    &kMfma256Sk,
+    &kMfma256Sk, &kMfmaKgroup96x64,
 };
 
 static bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
@@ -90,7 +90,7 @@ struct Candidate {
 static const int kModelVariants[] = {
     SGEMM_F32_MFMA_128,      SGEMM_F32_MFMA_256,       SGEMM_F32_MFMA_64x128,
     SGEMM_F32_MFMA_64,       SGEMM_F32_MFMA_64x128_KG4, SGEMM_F32_MFMA_64x96_KG4,
-    SGEMM_F32_MFMA_128x128_KG4, SGEMM_F32_MFMA_128_SK, SGEMM_F32_MFMA_64x128_SK,
+    SGEMM_F32_MFMA_96x64_KG4, SGEMM_F32_MFMA_128x128_KG4, SGEMM_F32_MFMA_128_SK, SGEMM_F32_MFMA_64x128_SK,
     SGEMM_F32_MFMA_256_SK,
 };
 static bool model_variant(int variant) {
@@ -106,7 +106,7 @@ struct Model {
 };
 
 // Built-in model, listed in order of preference when predictions tie.
-static const Model kDefaultModel = {10,
+static const Model kDefaultModel = {11,
                                     {
                                         {SGEMM_F32_MFMA_128, 0.0, {0.903, 0.919, 0.952, 0.920}, 0.84, 6.0},
                                         {SGEMM_F32_MFMA_256, 0.0, {0.996, 0.953, 0.962, 0.962}, 0.86, 12.0},
@@ -114,6 +114,7 @@ static const Model kDefaultModel = {10,
                                         {SGEMM_F32_MFMA_64, 3.5, {0.450, 0.627, 0.682, 0.785}, 0.86, 1.0},
                                         {SGEMM_F32_MFMA_64x128_KG4, 0.5, {0.786, 0.817, 0.833, 0.861}, 0.82, 5.5},
                                         {SGEMM_F32_MFMA_64x96_KG4, 3.0, {0.742, 0.771, 0.771, 0.806}, 0.84, 5.0},
+                                        {SGEMM_F32_MFMA_96x64_KG4, 3.0, {0.742, 0.771, 0.771, 0.806}, 0.84, 5.0},
                                         {SGEMM_F32_MFMA_128x128_KG4, 0.0, {0.911, 0.908, 0.941, 0.916}, 0.84, 10.5},
                                         {SGEMM_F32_MFMA_128_SK, 11.5, {0.801, 0.941, 0.959, 0.907}, 0.80, 4.5},
                                         {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.713, 0.869, 1.000, 0.903}, 0.70, 2.5},

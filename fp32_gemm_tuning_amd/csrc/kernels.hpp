@@ -95,7 +95,7 @@ extern Variant kNaive, kCoalesced, kLdsTiled, kReg1d, kReg2d, kVec4TransA;
 extern Variant kValuMain;
 // mfma_pipe.hip, mfma_kgroup.hip, mfma_small.hip
 extern Variant kMfma128, kMfma64, kMfmaSkinny, kMfmaKsplit, kMfmaDirect, kMfma64x128,
-    kMfma256, kMfmaKgroup, kMfmaKgroup96, kMfmaKgroup128, kMfma128Sk, kMfma64x128Sk, kMfma256Sk;
+    kMfma256, kMfmaKgroup, kMfmaKgroup96, kMfmaKgroup96x64, kMfmaKgroup128, kMfma128Sk, kMfma64x128Sk, kMfma256Sk;
 
 // Common host checks.
 bool aligned16(const void* p);

@@ -1,5 +1,5 @@
 // K-group FP32 matrix-core kernels (k_mfma_kgroup): mfma_64x128_kg4,
-// mfma_64x96_kg4 and mfma_128x128_kg4, one tile per workgroup of four groups
+// mfma_64x96_kg4, mfma_96x64_kg4 and mfma_128x128_kg4, one tile per workgroup of four groups
 // of waves that split the K slices and sum their partial tiles in a fixed
 // order. Operand layouts and edge handling: mfma_common.hpp.
 #include "mfma_pipecore.hpp"
@@ -281,6 +281,17 @@ Variant kMfmaKgroup = {"mfma_64x128_kg4", Kg128::check, Kg128::launch, Kg128::ke
 using Kg96 = KgroupInstance<64, 96, 64, 32, SGEMM_KG96_BK>;
 Variant kMfmaKgroup96 = {"mfma_64x96_kg4", Kg96::check, Kg96::launch, Kg96::kernel(), Kg96::NT,
                          true, nullptr, nullptr, Kg96::kBM, Kg96::kBN, Kg96::kBK};
+// 96x64 tile, 4 groups of 3 waves of 32x64 (12 waves, 80 KB LDS): the
+// 64x96 tile stood on end, for outputs with the odd shape's sides swapped
+// (1531x1000 is exactly 256 such tiles).
+#ifndef SGEMM_KG96x64_WM
+#define SGEMM_KG96x64_WM 32
+#define SGEMM_KG96x64_WN 64
+#endif
+using Kg96x64 = KgroupInstance<96, 64, SGEMM_KG96x64_WM, SGEMM_KG96x64_WN>;
+Variant kMfmaKgroup96x64 = {"mfma_96x64_kg4", Kg96x64::check, Kg96x64::launch, Kg96x64::kernel(),
+                            Kg96x64::NT, true, nullptr, nullptr, Kg96x64::kBM, Kg96x64::kBN,
+                            Kg96x64::kBK};
 // 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
 // tile per compute unit with four waves per SIMD, for shapes with at most
 // about one 128x128 tile per compute unit and long K.

@@ -40,6 +40,7 @@ TILE: Dict[str, Tuple[int, int]] = {
     "mfma_64x64": (64, 64),
     "mfma_64x128_kg4": (64, 128),
     "mfma_64x96_kg4": (64, 96),
+    "mfma_96x64_kg4": (96, 64),
     "mfma_128x128_kg4": (128, 128),
     "mfma_128x128_sk": (128, 128),
     "mfma_64x128_sk": (64, 128),

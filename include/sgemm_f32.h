@@ -148,7 +148,11 @@ enum sgemm_f32_variant_id {
     /* the same for MFMA_256 (one workgroup per compute unit, so whole tiles
        come in rounds of one tile per unit) */
     SGEMM_F32_MFMA_256_SK = 19,
-    SGEMM_F32_NUM_VARIANTS = 20
+    /* MFMA_64x96_KG4's tile stood on end: 96x64, 12 waves (4 groups of 3
+       waves of 32x64); a 1531x1000 output (the column-major 1000x1531 call
+       after the swap) is exactly 256 such tiles */
+    SGEMM_F32_MFMA_96x64_KG4 = 20,
+    SGEMM_F32_NUM_VARIANTS = 21
 };
 
 /* Storage order and operand transposition of the _ex entry points (the
@@ -327,7 +331,7 @@ SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int *bm, int *bn, int *bk)
 #define SGEMM_F32_MODEL_MAX 16
 typedef struct {
     int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,
-                           MFMA_64x128_KG4, MFMA_64x96_KG4, MFMA_128x128_KG4,
+                           MFMA_64x128_KG4, MFMA_64x96_KG4, MFMA_96x64_KG4, MFMA_128x128_KG4,
                            MFMA_128_SK, MFMA_64x128_SK or MFMA_256_SK */
     double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
     double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */

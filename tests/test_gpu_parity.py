@@ -242,7 +242,7 @@ def test_main_kernels_at_2048(dev, variant):
 
 @pytest.mark.parametrize("integer", [False, True], ids=["random", "integer"])
 @pytest.mark.parametrize("variant", ["mfma_256x256", "mfma_128x128", "mfma_64x128_kg4",
-                                     "mfma_64x96_kg4", "mfma_128x128_kg4"])
+                                     "mfma_64x96_kg4", "mfma_96x64_kg4", "mfma_128x128_kg4"])
 def test_large_tiles_on_odd_shape(dev, variant, integer):
     # 1000 x 1531 x 777: ragged in every dimension and not 16-byte aligned,
     # so the 4-byte fill runs; every output checked.

@@ -24,7 +24,7 @@ ROW, COL = sg.ROW_MAJOR, sg.COL_MAJOR
 NT, T = sg.NO_TRANS, sg.TRANS
 COMBOS = list(itertools.product((ROW, COL), (NT, T), (NT, T)))
 TRANS_KERNELS = ["mfma_128x128", "mfma_256x256", "mfma_64x128", "mfma_64x128_kg4",
-                 "mfma_64x96_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
+                 "mfma_64x96_kg4", "mfma_96x64_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
                  "mfma_256x256_sk"]
 
 
