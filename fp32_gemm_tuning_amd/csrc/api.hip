@@ -158,8 +158,8 @@ static int choose(const Args& a, int num_cus, size_t ws_bytes) {
     if (num_cus < 1) num_cus = 1;
     const int64_t M = a.M, N = a.N, K = a.K;
     const bool trans = a.ta || a.tb;
-    if (!trans && M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
-    if (!trans && (double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
+    if (M <= kSkinnyMaxM) return SGEMM_F32_MFMA_SKINNY;
+    if ((double)M * N * K < kTinyMacs) return SGEMM_F32_MFMA_DIRECT;
     const Model* m = g_model.load(std::memory_order_acquire);
     const bool vec = vec_ok(a);
     int best = SGEMM_F32_MFMA_128;

@@ -267,7 +267,7 @@ Variant kMfmaKsplit = {"mfma_64x64_k4", check_ksplit, launch_ksplit,
 constexpr int DR_TM = SGEMM_DIRECT_TM, DR_TN = SGEMM_DIRECT_TN, DR_KS = SGEMM_DIRECT_KS;
 constexpr int DR_GROUP_M = 8;
 
-template <int TM, int TN, bool VEC>
+template <int TM, int TN, bool VEC, bool TA, bool TB>
 struct DirectFrag {
     static constexpr int BI = TM / 32, BJ = TN / 32;
     float a[BI][8];
@@ -275,18 +275,27 @@ struct DirectFrag {
 
     // Step starting at k0: lane (h, c) reads A[m0 + 32*bi + c][k0 + 8h + 0..7]
     // and B[k0 + 8h + s][n0 + 32*bj + c]; everything outside the matrix reads 0.
+    // Element (m, k) of A sits at m*lda + k, or at k*lda + m when A is stored
+    // transposed (TA); element (k, n) of B at k*ldb + n, or at n*ldb + k (TB).
+    // VEC: the k-contiguous operands (A unless TA, B if TB) take 16-byte loads.
     __device__ __forceinline__ void load(const Args& a_, int m0, int n0, int k0, int rows_valid,
                                          int cols_valid, int h, int c) {
         const int kk = (a_.K - k0) < 16 ? (a_.K - k0) : 16;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-            a_.A + (int64_t)m0 * a_.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a_.lda + kk) * 4));
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
-            a_.B + (int64_t)k0 * a_.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a_.ldb + cols_valid) * 4));
+        const __amdgpu_buffer_rsrc_t rA =
+            TA ? make_rsrc(a_.A + (int64_t)k0 * a_.lda + m0,
+                           (uint32_t)(((int64_t)(kk - 1) * a_.lda + rows_valid) * 4))
+               : make_rsrc(a_.A + (int64_t)m0 * a_.lda + k0,
+                           (uint32_t)(((int64_t)(rows_valid - 1) * a_.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB =
+            TB ? make_rsrc(a_.B + (int64_t)n0 * a_.ldb + k0,
+                           (uint32_t)(((int64_t)(cols_valid - 1) * a_.ldb + kk) * 4))
+               : make_rsrc(a_.B + (int64_t)k0 * a_.ldb + n0,
+                           (uint32_t)(((int64_t)(kk - 1) * a_.ldb + cols_valid) * 4));
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi) {
             const int row = 32 * bi + c;
             const bool rok = row < rows_valid;
-            if (VEC) {
+            if (VEC && !TA) {
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
                     const int kq = 8 * h + 4 * v;
@@ -298,7 +307,8 @@ struct DirectFrag {
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const int kq = 8 * h + s;
-                    a[bi][s] = buf_load1(rA, rok && kq < kk ? (uint32_t)((row * (int)a_.lda + kq) * 4) : OOB);
+                    const int off = TA ? kq * (int)a_.lda + row : row * (int)a_.lda + kq;
+                    a[bi][s] = buf_load1(rA, rok && kq < kk ? (uint32_t)(off * 4) : OOB);
                 }
             }
         }
@@ -306,16 +316,27 @@ struct DirectFrag {
         for (int bj = 0; bj < BJ; ++bj) {
             const int col = 32 * bj + c;
             const bool cok = col < cols_valid;
+            if (VEC && TB) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int kr = 8 * h + s;
-                b[bj][s] = buf_load1(rB, cok && kr < kk ? (uint32_t)((kr * (int)a_.ldb + col) * 4) : OOB);
+                for (int v = 0; v < 2; ++v) {
+                    const int kq = 8 * h + 4 * v;
+                    const f32x4 x = buf_load4(rB, cok && kq + 4 <= kk ? (uint32_t)((col * (int)a_.ldb + kq) * 4) : OOB);
+                    b[bj][4 * v + 0] = x.x; b[bj][4 * v + 1] = x.y;
+                    b[bj][4 * v + 2] = x.z; b[bj][4 * v + 3] = x.w;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int kr = 8 * h + s;
+                    const int off = TB ? col * (int)a_.ldb + kr : kr * (int)a_.ldb + col;
+                    b[bj][s] = buf_load1(rB, cok && kr < kk ? (uint32_t)(off * 4) : OOB);
+                }
             }
         }
     }
 };
 
-template <int TM, int TN, int KS, bool VEC>
+template <int TM, int TN, int KS, bool VEC, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, int tiles_n,
                                                          int xcd_remap) {
     constexpr int BI = TM / 32, BJ = TN / 32, NB = BI * BJ;
@@ -338,7 +359,7 @@ __global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, in
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nsteps = (a.K + 15) / 16;
-    DirectFrag<TM, TN, VEC> cur, nxt;
+    DirectFrag<TM, TN, VEC, TA, TB> cur, nxt;
     if (w < nsteps) cur.load(a, m0, n0, 16 * w, rows_valid, cols_valid, h, c);
     for (int j = w; j < nsteps; j += KS) {
         if (j + KS < nsteps) nxt.load(a, m0, n0, 16 * (j + KS), rows_valid, cols_valid, h, c);
@@ -377,9 +398,27 @@ __global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, in
     }
 }
 
+// The 16-byte loads need every k-contiguous operand (A unless transposed, B
+// if transposed) 16-byte aligned with a row pitch and K that are multiples of 4.
+static bool small_vec_ok(const Args& a) {
+    if (a.K & 3) return false;
+    if (!a.ta && ((a.lda & 3) || !aligned16(a.A))) return false;
+    if (a.tb && ((a.ldb & 3) || !aligned16(a.B))) return false;
+    return true;
+}
+
+// Largest byte extent one buffer resource of an operand spans: `rows` x
+// `depth` of A (M rows by K) or B (K by N columns) in its storage order.
+static int64_t extent_a(const Args& a, int rows, int depth) {
+    return (a.ta ? (int64_t)(depth - 1) * a.lda + rows : (int64_t)(rows - 1) * a.lda + depth) * 4;
+}
+static int64_t extent_b(const Args& a, int depth, int cols) {
+    return (a.tb ? (int64_t)(cols - 1) * a.ldb + depth : (int64_t)(depth - 1) * a.ldb + cols) * 4;
+}
+
 static int check_direct(const Args& a) {
-    const int64_t ea = ((int64_t)(DR_TM - 1) * a.lda + 16) * 4;
-    const int64_t eb = ((int64_t)15 * a.ldb + DR_TN) * 4;
+    const int64_t ea = extent_a(a, DR_TM, 16);
+    const int64_t eb = extent_b(a, 16, DR_TN);
     if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
     const int64_t tiles = cdiv(a.M, DR_TM) * cdiv(a.N, DR_TN);
     return tiles <= max_workgroups(64 * DR_KS) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
@@ -388,18 +427,21 @@ static int check_direct(const Args& a) {
 static hipError_t launch_direct(const Args& a, hipStream_t s) {
     const int tm = (int)cdiv(a.M, DR_TM), tn = (int)cdiv(a.N, DR_TN);
     const dim3 grid((unsigned)((int64_t)tm * tn)), block(64 * DR_KS);
-    const bool vec = !((a.K & 3) || (a.lda & 3) || !aligned16(a.A));
-    if (vec)
-        hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, true>), grid, block, 0, s, a, tm, tn,
-                           xcd_remap_enabled());
-    else
-        hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, false>), grid, block, 0, s, a, tm, tn,
-                           xcd_remap_enabled());
-    return hipGetLastError();
+    const bool vec = small_vec_ok(a);
+    return with_trans(a, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (vec)
+            hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, true, TA, TB>), grid, block, 0, s,
+                               a, tm, tn, xcd_remap_enabled());
+        else
+            hipLaunchKernelGGL((k_mfma_direct<DR_TM, DR_TN, DR_KS, false, TA, TB>), grid, block, 0, s,
+                               a, tm, tn, xcd_remap_enabled());
+        return hipGetLastError();
+    });
 }
 
 Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
-                       (const void*)k_mfma_direct<DR_TM, DR_TN, DR_KS, true>, 64 * DR_KS};
+                       (const void*)k_mfma_direct<DR_TM, DR_TN, DR_KS, true>, 64 * DR_KS, true};
 
 // ===========================================================================
 // mfma_skinny: for few rows (near-GEMV, e.g. 16 x 8192 x 8192, where B is
@@ -415,7 +457,7 @@ Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
 // ===========================================================================
 constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KU = 64;  // k per unrolled step
 
-template <bool VEC>
+template <bool VEC, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int kchunk) {
     __shared__ float red[SK_WAVES][2][4][64];
     const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
@@ -427,40 +469,66 @@ __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int k
     const int kbeg = w * kchunk;
     const int kend = (a.K - kbeg) < kchunk ? a.K : kbeg + kchunk;
 
+    // With both operands transposed and 4-byte loads, a 64-deep step's
+    // addresses and values exceed the 128 registers of a 1024-lane
+    // workgroup: such calls step 32 deep.
+    constexpr int KU = (!VEC && TA && TB) ? SK_KU / 2 : SK_KU;
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = kbeg; k0 < kend; k0 += SK_KU) {
-        const int kk = (a.K - k0) < SK_KU ? (a.K - k0) : SK_KU;  // rows present in memory
+    for (int k0 = kbeg; k0 < kend; k0 += KU) {
+        const int kk = (a.K - k0) < KU ? (a.K - k0) : KU;  // rows present in memory
         const int klim = kend - k0;                              // rows this wave owns
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(
-            a.A + (int64_t)m0 * a.lda + k0, (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(
-            a.B + (int64_t)k0 * a.ldb + n0, (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
-        f32x4 af[SK_KU / 16];
-        float b0[SK_KU / 4], b1[SK_KU / 4];
+        const __amdgpu_buffer_rsrc_t rA =
+            TA ? make_rsrc(a.A + (int64_t)k0 * a.lda + m0,
+                           (uint32_t)(((int64_t)(kk - 1) * a.lda + rows_valid) * 4))
+               : make_rsrc(a.A + (int64_t)m0 * a.lda + k0,
+                           (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+        const __amdgpu_buffer_rsrc_t rB =
+            TB ? make_rsrc(a.B + (int64_t)n0 * a.ldb + k0,
+                           (uint32_t)(((int64_t)(cols_valid - 1) * a.ldb + kk) * 4))
+               : make_rsrc(a.B + (int64_t)k0 * a.ldb + n0,
+                           (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
+        f32x4 af[KU / 16];
+        float b0[KU / 4], b1[KU / 4];
 #pragma unroll
-        for (int u = 0; u < SK_KU / 16; ++u) {
+        for (int u = 0; u < KU / 16; ++u) {
             const int kq = 16 * u + 4 * g;  // this lane's 4 consecutive k
-            if (VEC) {
+            if (VEC && !TA) {
                 const bool ok = c < rows_valid && kq + 4 <= klim;
                 af[u] = buf_load4(rA, ok ? (uint32_t)((c * (int)a.lda + kq) * 4) : OOB);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const bool ok = c < rows_valid && kq + e < klim;
-                    af[u][e] = buf_load1(rA, ok ? (uint32_t)((c * (int)a.lda + kq + e) * 4) : OOB);
+                    const int off = TA ? (kq + e) * (int)a.lda + c : c * (int)a.lda + kq + e;
+                    af[u][e] = buf_load1(rA, ok ? (uint32_t)(off * 4) : OOB);
                 }
             }
+            if (VEC && TB) {
+                // Columns c and c + 16 of B are rows of the stored matrix:
+                // 4 consecutive k in one 16-byte load each.
+                const bool ok = kq + 4 <= klim;
+                const f32x4 x0 = buf_load4(rB, ok && c < cols_valid ? (uint32_t)((c * (int)a.ldb + kq) * 4) : OOB);
+                const f32x4 x1 = buf_load4(rB, ok && c + 16 < cols_valid
+                                                   ? (uint32_t)(((c + 16) * (int)a.ldb + kq) * 4) : OOB);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kr = kq + e;
-                const bool okr = kr < klim;
-                const uint32_t base = (uint32_t)(kr * (int)a.ldb) * 4;
-                b0[4 * u + e] = buf_load1(rB, okr && c < cols_valid ? base + c * 4 : OOB);
-                b1[4 * u + e] = buf_load1(rB, okr && c + 16 < cols_valid ? base + (c + 16) * 4 : OOB);
+                for (int e = 0; e < 4; ++e) {
+                    b0[4 * u + e] = x0[e];
+                    b1[4 * u + e] = x1[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kr = kq + e;
+                    const bool okr = kr < klim;
+                    const int o0 = TB ? c * (int)a.ldb + kr : kr * (int)a.ldb + c;
+                    const int o1 = TB ? (c + 16) * (int)a.ldb + kr : kr * (int)a.ldb + c + 16;
+                    b0[4 * u + e] = buf_load1(rB, okr && c < cols_valid ? (uint32_t)(o0 * 4) : OOB);
+                    b1[4 * u + e] = buf_load1(rB, okr && c + 16 < cols_valid ? (uint32_t)(o1 * 4) : OOB);
+                }
             }
         }
 #pragma unroll
-        for (int u = 0; u < SK_KU / 16; ++u)
+        for (int u = 0; u < KU / 16; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b0[4 * u + e], acc0, 0, 0, 0);
@@ -491,8 +559,8 @@ static int skinny_kchunk(const Args& a) {
 }
 
 static int check_skinny(const Args& a) {
-    const int64_t ea = ((int64_t)(SK_BM - 1) * a.lda + SK_KU) * 4;
-    const int64_t eb = ((int64_t)(SK_KU - 1) * a.ldb + SK_BN) * 4;
+    const int64_t ea = extent_a(a, SK_BM, SK_KU);
+    const int64_t eb = extent_b(a, SK_KU, SK_BN);
     if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
     const int64_t tiles = cdiv(a.M, SK_BM) * cdiv(a.N, SK_BN);
     return tiles <= max_workgroups(1024) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
@@ -501,15 +569,19 @@ static int check_skinny(const Args& a) {
 static hipError_t launch_skinny(const Args& a, hipStream_t s) {
     const int tn = (int)cdiv(a.N, SK_BN);
     const dim3 grid((unsigned)(cdiv(a.M, SK_BM) * tn)), block(1024);
-    const bool vec = !((a.K & 3) || (a.lda & 3) || !aligned16(a.A));
-    if (vec)
-        hipLaunchKernelGGL(k_mfma_skinny<true>, grid, block, 0, s, a, tn, skinny_kchunk(a));
-    else
-        hipLaunchKernelGGL(k_mfma_skinny<false>, grid, block, 0, s, a, tn, skinny_kchunk(a));
-    return hipGetLastError();
+    const bool vec = small_vec_ok(a);
+    const int kchunk = skinny_kchunk(a);
+    return with_trans(a, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (vec)
+            hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB>), grid, block, 0, s, a, tn, kchunk);
+        else
+            hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB>), grid, block, 0, s, a, tn, kchunk);
+        return hipGetLastError();
+    });
 }
 
 Variant kMfmaSkinny = {"mfma_skinny", check_skinny, launch_skinny,
-                             (const void*)k_mfma_skinny<true>, 1024};
+                       (const void*)k_mfma_skinny<true>, 1024, true};
 
 }  // namespace sgemm

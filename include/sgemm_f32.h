@@ -208,8 +208,9 @@ SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, c
  * After the swap an operand may be stored transposed (A as K x M or B as
  * N x K, row-major); the matrix-core tile kernels read such operands
  * directly (the buffer-to-LDS fill stores them in the LDS layout the
- * fragment reads need; see sgemm_f32_variant_trans_ok), and the automatic
- * choice then takes one of them. */
+ * fragment reads need; see sgemm_f32_variant_trans_ok), as do mfma_skinny
+ * and mfma_direct (whose lanes load their k-runs straight from memory), and
+ * the automatic choice then takes one of them. */
 SGEMM_F32_API int sgemm_f32_ex(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
                                float alpha, const float *A, int64_t lda, const float *B,
                                int64_t ldb, float beta, float *C, int64_t ldc, void *stream);
@@ -323,11 +324,10 @@ SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int *bm, int *bn, int *bk)
  * (a fraction of a tile), with b taken for ceil(n); stream-K entries are
  * considered only by sgemm_f32_ws, on shapes they split, and when the
  * workspace suffices; if no entry applies, mfma_128x128 runs. M <= 32 and
- * tiny products
- * bypass the model (mfma_skinny, mfma_direct). A call with a transposed
- * operand (after the column-major swap) uses the model for every shape,
- * restricted to the entries that read transposed operands (mfma_128x128 if
- * there are none). */
+ * tiny products bypass the model (mfma_skinny, mfma_direct; both read
+ * transposed operands). Otherwise a call with a transposed operand (after
+ * the column-major swap) is restricted to the model's entries that read
+ * transposed operands (mfma_128x128 if there are none). */
 #define SGEMM_F32_MODEL_MAX 16
 typedef struct {
     int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,

@@ -25,7 +25,7 @@ NT, T = sg.NO_TRANS, sg.TRANS
 COMBOS = list(itertools.product((ROW, COL), (NT, T), (NT, T)))
 TRANS_KERNELS = ["mfma_128x128", "mfma_256x256", "mfma_64x128", "mfma_64x128_kg4",
                  "mfma_64x96_kg4", "mfma_96x64_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
-                 "mfma_256x256_sk"]
+                 "mfma_256x256_sk", "mfma_skinny", "mfma_direct"]
 
 
 def combo_id(c):
@@ -142,6 +142,34 @@ def test_transposed_small(dev, combo, variant, case):
     A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, dist, 500 + M + N + K, beta, pads)
     rc, out = run_ex(variant, layout, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets,
                      tag="trans-small")
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    rep = check(out, C, opA, opB, M, N, K, alpha, beta, exact=(dist == "integer"))
+    assert rep.ok, f"{variant} {combo_id(combo)} {case}: {rep}"
+
+
+# Few rows and long K for the kernels that load their k-runs straight from
+# memory: K spread over all 16 waves of mfma_skinny with a ragged last run,
+# 16-byte k-runs where the stored rows allow them, 4-byte ones on odd pitches
+# and misaligned bases.
+SMALL_M = [
+    (16, 520, 4100, 1.0, 0.0, "uniform", (0, 0, 0), (0, 0, 0)),
+    (32, 64, 4096, 1.0, 0.5, "integer", (0, 0, 0), (0, 0, 0)),
+    (7, 333, 1029, 2.0, -1.0, "integer", (1, 3, 2), (1, 0, 3)),
+    (20, 96, 52, 1.0, 0.0, "integer", (4, 0, 0), (0, 2, 0)),
+]
+
+
+@pytest.mark.parametrize("combo", COMBOS, ids=combo_id)
+@pytest.mark.parametrize("variant", ["mfma_skinny", "mfma_direct"])
+@pytest.mark.parametrize("case", SMALL_M, ids=lambda c: "x".join(map(str, c[:3])) + f"-{c[5]}")
+def test_transposed_few_rows(dev, combo, variant, case):
+    layout, ta, tb = combo
+    M, N, K, alpha, beta, dist, pads, offsets = case
+    if layout == COL:
+        M, N = N, M   # few columns: few rows after the column-major swap
+    A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, dist, 700 + M + N + K, beta, pads)
+    rc, out = run_ex(variant, layout, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets,
+                     tag="trans-few-rows")
     assert rc == 0, sg.sgemm_f32_strerror(rc)
     rep = check(out, C, opA, opB, M, N, K, alpha, beta, exact=(dist == "integer"))
     assert rep.ok, f"{variant} {combo_id(combo)} {case}: {rep}"

@@ -15,7 +15,7 @@ ROW, COL = sg.ROW_MAJOR, sg.COL_MAJOR
 NT, T = sg.NO_TRANS, sg.TRANS
 TRANS_KERNELS = {"mfma_128x128", "mfma_256x256", "mfma_64x128", "mfma_64x128_kg4",
                  "mfma_64x96_kg4", "mfma_96x64_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
-                 "mfma_256x256_sk"}
+                 "mfma_256x256_sk", "mfma_skinny", "mfma_direct"}
 
 
 def min_lds(layout, ta, tb, M, N, K):
@@ -102,6 +102,18 @@ def test_transposed_plan_follows_the_model():
                                     ldc, 256)
         assert sg.sgemm_f32_variant_name(v) == sg.sgemm_f32_variant_name(
             sg.sgemm_f32_plan(1000, 1531, 777, 1.0, P, 777, P, 1531, 0.0, P, 1531, 256)[1])
+
+
+@pytest.mark.parametrize("layout,ta,tb", [c for c in COMBOS if c not in ((ROW, NT, NT), (COL, NT, NT))])
+def test_transposed_few_rows_and_tiny_calls_take_the_small_kernels(layout, ta, tb):
+    # M <= 32 rows (N <= 32 columns for column-major: rows after the swap)
+    # take the skinny kernel and tiny products the direct one, transposed or not.
+    for (M, N, K), want in (((16, 8192, 8192), "mfma_skinny"), ((256, 256, 256), "mfma_direct")):
+        if layout == COL:
+            M, N = N, M
+        lda, ldb, ldc = min_lds(layout, ta, tb, M, N, K)
+        rc, v = sg.sgemm_f32_plan_ex(layout, ta, tb, M, N, K, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
+        assert rc == 0 and sg.sgemm_f32_variant_name(v) == want, (M, N, K)
 
 
 def test_trans_ok_flags():
