@@ -71,10 +71,11 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // fixed cost per tile on that unit (a tile's first fill and epilogue). All
 // four were fitted per kernel to interleaved timings of every candidate on
 // 30 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
-// (fp32_gemm_tuning_amd/tune.py): without a workspace the fitted model picks
-// the fastest whole-tile kernel on 28 of them, with one the fastest of all
-// on 23, in both cases one within 8% on the rest (0.1% and 0.6% lost on
-// average).
+// (fp32_gemm_tuning_amd/tune.py); mfma_96x64_kg4's row comes from a later
+// fit of the same kind. On a later, independent timing of the 30 shapes the
+// model picks the fastest whole-tile kernel on 26 of them without a
+// workspace and the fastest of all on 22 with one, in both cases one within
+// 5% on the rest (0.3% and 0.5% lost on average).
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
@@ -114,7 +115,7 @@ static const Model kDefaultModel = {11,
                                         {SGEMM_F32_MFMA_64, 3.5, {0.450, 0.627, 0.682, 0.785}, 0.86, 1.0},
                                         {SGEMM_F32_MFMA_64x128_KG4, 0.5, {0.786, 0.817, 0.833, 0.861}, 0.82, 5.5},
                                         {SGEMM_F32_MFMA_64x96_KG4, 3.0, {0.742, 0.771, 0.771, 0.806}, 0.84, 5.0},
-                                        {SGEMM_F32_MFMA_96x64_KG4, 3.0, {0.742, 0.771, 0.771, 0.806}, 0.84, 5.0},
+                                        {SGEMM_F32_MFMA_96x64_KG4, 1.0, {0.730, 0.788, 0.811, 0.815}, 0.82, 5.5},
                                         {SGEMM_F32_MFMA_128x128_KG4, 0.0, {0.911, 0.908, 0.941, 0.916}, 0.84, 10.5},
                                         {SGEMM_F32_MFMA_128_SK, 11.5, {0.801, 0.941, 0.959, 0.907}, 0.80, 4.5},
                                         {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.713, 0.869, 1.000, 0.903}, 0.70, 2.5},

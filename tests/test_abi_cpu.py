@@ -122,8 +122,10 @@ def test_plan_busiest_cu_rule():
     assert _plan(4096, 2048, 4096, cus=256) == "mfma_128x128"
     # 1024x1536: 96 tiles of 128^2 keep 160 CUs idle; 256 tiles of 64x96 do not.
     assert _plan(1024, 1536, 768, cus=256) == "mfma_64x96_kg4"
-    # 1000^3: 256 tiles of 64^2 (with 16 of them ragged) on 256 CUs.
-    assert _plan(1000, 1000, 1000, cus=256) == "mfma_64x64"
+    # 1000^3: one tile per CU, either 256 tiles of 64^2 or 176 twelve-wave
+    # K-group tiles of 96x64 or 64x96 (measured within 0.5% of each other:
+    # 35.4-35.6 us), never a kernel that leaves whole rounds of CUs idle.
+    assert _plan(1000, 1000, 1000, cus=256) in ("mfma_64x64", "mfma_96x64_kg4", "mfma_64x96_kg4")
     # 8192^2: four rounds of 256^2 tiles.
     assert _plan(8192, 8192, 8192, cus=256) == "mfma_256x256"
     # a single CU: the largest tile always wins.
