@@ -245,7 +245,36 @@ static Args make_args(int layout, int transa, int transb, int64_t M, int64_t N, 
     a.beta = beta;
     a.ta = col ? transb : transa;
     a.tb = col ? transa : transb;
+    a.tc = 0;
     return a;
+}
+
+// A column-major call with few rows and more columns would become, after the
+// swap, a product with few columns, which no kernel serves well. The skinny
+// kernel takes it unswapped instead: column-major storage of A and B is
+// row-major storage of their transposes, so it reads them with the
+// transposition flags flipped, and it writes C column-major (Args::tc).
+// Returns the variant for the automatic choice, with `a` replaced by the
+// unswapped arguments when that applies.
+static int plan_args(const Args& a, int num_cus, size_t ws_bytes);
+static int plan_call(int layout, int transa, int transb, Args& a, int num_cus, size_t ws_bytes) {
+    if (layout == SGEMM_F32_COL_MAJOR && a.N <= kSkinnyMaxM && a.M > kSkinnyMaxM) {
+        Args u = a;
+        u.A = a.B;
+        u.B = a.A;
+        u.lda = a.ldb;
+        u.ldb = a.lda;
+        u.M = a.N;
+        u.N = a.M;
+        u.ta = !transa;
+        u.tb = !transb;
+        u.tc = 1;
+        if (kTable[SGEMM_F32_MFMA_SKINNY]->check(u) == 0) {
+            a = u;
+            return SGEMM_F32_MFMA_SKINNY;
+        }
+    }
+    return plan_args(a, num_cus, ws_bytes);
 }
 
 // The variant the automatic choice launches for a (valid, non-quick-return)
@@ -275,7 +304,7 @@ static int run(int forced, int layout, int transa, int transb, int64_t M, int64_
     if (M == 0 || N == 0) return 0;
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     if (K == 0 || alpha == 0.0f) {
         const hipError_t e = launch_scale(a, s);
         return e == hipSuccess ? 0 : (int)e;
@@ -285,7 +314,7 @@ static int run(int forced, int layout, int transa, int transb, int64_t M, int64_
         rc = device_cus(&cus);
         if (rc) return rc;
     }
-    if (v < 0) v = plan_args(a, cus, ws_bytes);
+    if (v < 0) v = plan_call(layout, transa, transb, a, cus, ws_bytes);
     const Variant& var = *kTable[v];
     if ((a.ta || a.tb) && !var.trans_ok) return SGEMM_F32_ERR_UNSUPPORTED;
     rc = var.check(a);
@@ -311,9 +340,9 @@ static int plan(int layout, int transa, int transb, int64_t M, int64_t N, int64_
         return 0;
     }
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
-    const Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta,
-                             const_cast<float*>(C), ldc);
-    *variant = plan_args(a, num_cus, ws_bytes);
+    Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta,
+                       const_cast<float*>(C), ldc);
+    *variant = plan_call(layout, transa, transb, a, num_cus, ws_bytes);
     return 0;
 }
 

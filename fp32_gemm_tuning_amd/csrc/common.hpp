@@ -22,6 +22,9 @@ struct Args {
     // these): ta -> A is stored K x M, A(i,k) = A[k*lda + i]; tb -> B is
     // stored N x K, B(k,j) = B[j*ldb + k].
     int32_t ta, tb;
+    // C stored column-major, C(i,j) = C[j*ldc + i] (only mfma_skinny, which
+    // takes column-major calls with few rows unswapped, writes it this way).
+    int32_t tc;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -31,6 +34,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // when beta != 0 (so an uninitialised C cannot leak NaN into the result).
 __device__ __forceinline__ void store_out(const Args& a, int64_t i, int64_t j, float acc) {
     float* p = a.C + i * a.ldc + j;
+    float v = a.alpha * acc;
+    if (a.beta != 0.0f) v = __builtin_fmaf(a.beta, *p, v);
+    *p = v;
+}
+// The same for a column-major C (Args::tc).
+__device__ __forceinline__ void store_out_col(const Args& a, int64_t i, int64_t j, float acc) {
+    float* p = a.C + j * a.ldc + i;
     float v = a.alpha * acc;
     if (a.beta != 0.0f) v = __builtin_fmaf(a.beta, *p, v);
     *p = v;

@@ -457,7 +457,7 @@ Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
 // ===========================================================================
 constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KU = 64;  // k per unrolled step
 
-template <bool VEC, bool TA = false, bool TB = false>
+template <bool VEC, bool TA = false, bool TB = false, bool TC = false>
 __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int kchunk) {
     __shared__ float red[SK_WAVES][2][4][64];
     const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
@@ -543,12 +543,20 @@ __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int k
     }
     __syncthreads();
     if (threadIdx.x < SK_BM * SK_BN) {
-        const int i = threadIdx.x / SK_BN, j = threadIdx.x % SK_BN;
+        // Consecutive threads take consecutive columns of a row-major C, or
+        // consecutive rows of a column-major one (TC).
+        const int i = TC ? threadIdx.x % SK_BM : threadIdx.x / SK_BN;
+        const int j = TC ? threadIdx.x / SK_BM : threadIdx.x % SK_BN;
         const int bj = j >> 4, src = (i >> 2) * 16 + (j & 15), r = i & 3;
         float v = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < SK_WAVES; ++ww) v += red[ww][bj][r][src];
-        if (i < rows_valid && j < cols_valid) store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+        if (i < rows_valid && j < cols_valid) {
+            if (TC)
+                store_out_col(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+            else
+                store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+        }
     }
 }
 
@@ -573,10 +581,16 @@ static hipError_t launch_skinny(const Args& a, hipStream_t s) {
     const int kchunk = skinny_kchunk(a);
     return with_trans(a, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-        if (vec)
+        if (a.tc) {
+            if (vec)
+                hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB, true>), grid, block, 0, s, a, tn, kchunk);
+            else
+                hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB, true>), grid, block, 0, s, a, tn, kchunk);
+        } else if (vec) {
             hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB>), grid, block, 0, s, a, tn, kchunk);
-        else
+        } else {
             hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB>), grid, block, 0, s, a, tn, kchunk);
+        }
         return hipGetLastError();
     });
 }

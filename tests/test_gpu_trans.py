@@ -175,6 +175,23 @@ def test_transposed_few_rows(dev, combo, variant, case):
     assert rep.ok, f"{variant} {combo_id(combo)} {case}: {rep}"
 
 
+@pytest.mark.parametrize("ta,tb", [(NT, NT), (T, NT), (NT, T), (T, T)], ids=["NN", "TN", "NT", "TT"])
+@pytest.mark.parametrize("case", SMALL_M, ids=lambda c: "x".join(map(str, c[:3])) + f"-{c[5]}")
+def test_column_major_few_rows_auto(dev, ta, tb, case):
+    # Few rows, column-major: the automatic choice runs the skinny kernel
+    # unswapped, reading both operands as transposes and writing C by columns.
+    M, N, K, alpha, beta, dist, pads, offsets = case
+    rc, v = sg.sgemm_f32_plan_ex(COL, ta, tb, M, N, K, alpha, 1 << 20, K + 4 if ta else M + 4,
+                                 1 << 20, N + 4 if tb else K + 4, beta, 1 << 20, M + 4, 256)
+    assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_skinny"
+    A, B, C, opA, opB = make_case(COL, ta, tb, M, N, K, dist, 800 + M + N + K, beta, pads)
+    rc, out = run_ex(None, COL, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets,
+                     tag="col-few-rows")
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    rep = check(out, C, opA, opB, M, N, K, alpha, beta, exact=(dist == "integer"))
+    assert rep.ok, f"col {ta}{tb} {case}: {rep}"
+
+
 @pytest.mark.parametrize("variant", sg.VARIANTS)
 def test_column_major_plain_runs_every_variant(dev, variant):
     # Column-major with nothing transposed is the swapped row-major product

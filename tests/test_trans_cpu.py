@@ -73,9 +73,14 @@ def test_column_major_plain_call_is_the_swapped_row_major_call(M, N, K):
     # C (M x N, col-major) = A B is C^T = B^T A^T row-major: an N x M product
     # with the operands swapped and nothing transposed, so every kernel,
     # including the skinny one (for small N), is available.
+    # The exception: few rows and more columns, which the skinny kernel takes
+    # unswapped (after the swap it would be a product with few columns).
     rc, v = sg.sgemm_f32_plan_ex(COL, NT, NT, M, N, K, 1.0, P, M, P, K, 0.0, P, M, 256)
     assert rc == 0
-    assert (rc, v) == sg.sgemm_f32_plan(N, M, K, 1.0, P, K, P, M, 0.0, P, M, 256)
+    if M <= 32 < N:
+        assert sg.sgemm_f32_variant_name(v) == "mfma_skinny"
+    else:
+        assert (rc, v) == sg.sgemm_f32_plan(N, M, K, 1.0, P, K, P, M, 0.0, P, M, 256)
 
 
 @pytest.mark.parametrize("layout,ta,tb", [c for c in COMBOS if c not in ((ROW, NT, NT), (COL, NT, NT))])
@@ -114,6 +119,20 @@ def test_transposed_few_rows_and_tiny_calls_take_the_small_kernels(layout, ta, t
         lda, ldb, ldc = min_lds(layout, ta, tb, M, N, K)
         rc, v = sg.sgemm_f32_plan_ex(layout, ta, tb, M, N, K, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
         assert rc == 0 and sg.sgemm_f32_variant_name(v) == want, (M, N, K)
+
+
+@pytest.mark.parametrize("ta,tb", [(NT, NT), (T, NT), (NT, T), (T, T)])
+def test_column_major_few_rows_take_the_skinny_kernel(ta, tb):
+    # 16 rows, 8192 columns, column-major: the skinny kernel, unswapped; with
+    # few columns as well the swapped call is itself a few-row product.
+    for (M, N, K) in ((16, 8192, 8192), (32, 33, 100), (7, 4096, 1029), (16, 16, 4096)):
+        lda, ldb, ldc = min_lds(COL, ta, tb, M, N, K)
+        rc, v = sg.sgemm_f32_plan_ex(COL, ta, tb, M, N, K, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
+        assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_skinny", (M, N, K)
+    # 33 rows are not few
+    lda, ldb, ldc = min_lds(COL, ta, tb, 33, 8192, 8192)
+    rc, v = sg.sgemm_f32_plan_ex(COL, ta, tb, 33, 8192, 8192, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
+    assert rc == 0 and sg.sgemm_f32_variant_name(v) != "mfma_skinny"
 
 
 def test_trans_ok_flags():
