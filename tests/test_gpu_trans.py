@@ -242,6 +242,27 @@ def test_transposed_headline_size(dev, combo):
         assert rep.ok, f"{combo_id(combo)}: {rep}"
 
 
+@pytest.mark.parametrize("combo", [(COL, NT, NT), (COL, T, T), (ROW, T, NT), (ROW, NT, T)],
+                         ids=combo_id)
+def test_few_rows_full_size(dev, combo):
+    # 16 x 8192 x 8192 (the near-GEMV workload) through the automatic choice:
+    # column-major runs the skinny kernel unswapped, row-major with a
+    # transposed operand reads it in place; every row, sampled columns.
+    layout, ta, tb = combo
+    w = WORKLOADS["R_skinny"]
+    M, N, K = w.M, w.N, w.K
+    A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, "uniform", 1600, 0.0, (0, 0, 0))
+    rc, out = run_ex(None, layout, ta, tb, M, N, K, 1.0, 0.0, A, B, C, dev, tag="few-rows-R_skinny")
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    got = C.read_logical(out)
+    rng = np.random.default_rng(7)
+    cols = np.unique(np.concatenate([[0, 1, 31, 32, N - 1], rng.integers(0, N, 40)]))
+    Cc, bc = oracle.sgemm_ref_cols(opA, opB, None, 1.0, 0.0, cols, M=M, N=N, K=K)
+    rep = check_bound(got[:, cols], Cc, bc, K, cols=cols)
+    print(f"[gpu] R_skinny {combo_id(combo)}: {rep}", flush=True)
+    assert rep.ok, f"{combo_id(combo)}: {rep}"
+
+
 def test_gemm_helper_takes_transposed_views(dev):
     M, N, K = 300, 200, 100
     g = np.random.default_rng(5)
