@@ -249,16 +249,17 @@ static Args make_args(int layout, int transa, int transb, int64_t M, int64_t N, 
     return a;
 }
 
-// A column-major call with few rows and more columns would become, after the
-// swap, a product with few columns, which no kernel serves well. The skinny
-// kernel takes it unswapped instead: column-major storage of A and B is
-// row-major storage of their transposes, so it reads them with the
-// transposition flags flipped, and it writes C column-major (Args::tc).
+// A product with few columns and more rows (a row-major call with N <= 32,
+// or a column-major call with M <= 32, which the swap turns into one) is one
+// no kernel serves well as it stands. Its transpose has few rows:
+// C^T = op(B)^T op(A)^T, where op(B)^T is read through B with its
+// transposition flag flipped, op(A)^T through A likewise, and C^T is C
+// written column-major (Args::tc). The skinny kernel computes that.
 // Returns the variant for the automatic choice, with `a` replaced by the
-// unswapped arguments when that applies.
+// transposed problem when that applies.
 static int plan_args(const Args& a, int num_cus, size_t ws_bytes);
-static int plan_call(int layout, int transa, int transb, Args& a, int num_cus, size_t ws_bytes) {
-    if (layout == SGEMM_F32_COL_MAJOR && a.N <= kSkinnyMaxM && a.M > kSkinnyMaxM) {
+static int plan_call(Args& a, int num_cus, size_t ws_bytes) {
+    if (a.N <= kSkinnyMaxM && a.M > kSkinnyMaxM) {
         Args u = a;
         u.A = a.B;
         u.B = a.A;
@@ -266,8 +267,8 @@ static int plan_call(int layout, int transa, int transb, Args& a, int num_cus, s
         u.ldb = a.lda;
         u.M = a.N;
         u.N = a.M;
-        u.ta = !transa;
-        u.tb = !transb;
+        u.ta = !a.tb;
+        u.tb = !a.ta;
         u.tc = 1;
         if (kTable[SGEMM_F32_MFMA_SKINNY]->check(u) == 0) {
             a = u;
@@ -314,7 +315,7 @@ static int run(int forced, int layout, int transa, int transb, int64_t M, int64_
         rc = device_cus(&cus);
         if (rc) return rc;
     }
-    if (v < 0) v = plan_call(layout, transa, transb, a, cus, ws_bytes);
+    if (v < 0) v = plan_call(a, cus, ws_bytes);
     const Variant& var = *kTable[v];
     if ((a.ta || a.tb) && !var.trans_ok) return SGEMM_F32_ERR_UNSUPPORTED;
     rc = var.check(a);
@@ -342,7 +343,7 @@ static int plan(int layout, int transa, int transb, int64_t M, int64_t N, int64_
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return SGEMM_F32_ERR_TOO_LARGE;
     Args a = make_args(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta,
                        const_cast<float*>(C), ldc);
-    *variant = plan_call(layout, transa, transb, a, num_cus, ws_bytes);
+    *variant = plan_call(a, num_cus, ws_bytes);
     return 0;
 }
 

@@ -210,10 +210,11 @@ SGEMM_F32_API int sgemm_f32_plan(int64_t M, int64_t N, int64_t K, float alpha, c
  * directly (the buffer-to-LDS fill stores them in the LDS layout the
  * fragment reads need; see sgemm_f32_variant_trans_ok), as do mfma_skinny
  * and mfma_direct (whose lanes load their k-runs straight from memory), and
- * the automatic choice then takes one of them. One exception to the swap:
- * the automatic choice runs a column-major call with M <= 32 < N unswapped
- * on mfma_skinny (after the swap it would be a product with few columns),
- * reading A and B as transposes and writing C column-major. */
+ * the automatic choice then takes one of them. A product with few columns
+ * (row-major N <= 32 < M, or column-major M <= 32 < N, which the swap makes
+ * one) runs instead as its transpose, which has few rows, on mfma_skinny:
+ * A and B are read with their transposition flags flipped and C is written
+ * transposed. */
 SGEMM_F32_API int sgemm_f32_ex(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
                                float alpha, const float *A, int64_t lda, const float *B,
                                int64_t ldb, float beta, float *C, int64_t ldc, void *stream);

@@ -175,21 +175,26 @@ def test_transposed_few_rows(dev, combo, variant, case):
     assert rep.ok, f"{variant} {combo_id(combo)} {case}: {rep}"
 
 
+@pytest.mark.parametrize("layout", [COL, ROW], ids=["col", "row"])
 @pytest.mark.parametrize("ta,tb", [(NT, NT), (T, NT), (NT, T), (T, T)], ids=["NN", "TN", "NT", "TT"])
 @pytest.mark.parametrize("case", SMALL_M, ids=lambda c: "x".join(map(str, c[:3])) + f"-{c[5]}")
-def test_column_major_few_rows_auto(dev, ta, tb, case):
-    # Few rows, column-major: the automatic choice runs the skinny kernel
-    # unswapped, reading both operands as transposes and writing C by columns.
+def test_few_rows_or_columns_auto(dev, layout, ta, tb, case):
+    # Few rows in column-major storage, or few columns in row-major storage:
+    # the automatic choice runs the skinny kernel on the transposed problem
+    # (few rows), reading both operands as transposes and writing C^T
+    # column-major.
     M, N, K, alpha, beta, dist, pads, offsets = case
-    rc, v = sg.sgemm_f32_plan_ex(COL, ta, tb, M, N, K, alpha, 1 << 20, K + 4 if ta else M + 4,
-                                 1 << 20, N + 4 if tb else K + 4, beta, 1 << 20, M + 4, 256)
+    if layout == ROW:
+        M, N = N, M
+    A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, dist, 800 + M + N + K, beta, pads)
+    rc, v = sg.sgemm_f32_plan_ex(layout, ta, tb, M, N, K, alpha, 1 << 20, A.ld, 1 << 20, B.ld, beta,
+                                 1 << 20, C.ld, 256)
     assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_skinny"
-    A, B, C, opA, opB = make_case(COL, ta, tb, M, N, K, dist, 800 + M + N + K, beta, pads)
-    rc, out = run_ex(None, COL, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets,
-                     tag="col-few-rows")
+    rc, out = run_ex(None, layout, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets,
+                     tag="few-rows-or-columns")
     assert rc == 0, sg.sgemm_f32_strerror(rc)
     rep = check(out, C, opA, opB, M, N, K, alpha, beta, exact=(dist == "integer"))
-    assert rep.ok, f"col {ta}{tb} {case}: {rep}"
+    assert rep.ok, f"{combo_id((layout, ta, tb))} {case}: {rep}"
 
 
 @pytest.mark.parametrize("variant", sg.VARIANTS)
@@ -261,6 +266,24 @@ def test_few_rows_full_size(dev, combo):
     rep = check_bound(got[:, cols], Cc, bc, K, cols=cols)
     print(f"[gpu] R_skinny {combo_id(combo)}: {rep}", flush=True)
     assert rep.ok, f"{combo_id(combo)}: {rep}"
+
+
+@pytest.mark.parametrize("ta,tb", [(NT, NT), (T, T)], ids=["NN", "TT"])
+def test_few_columns_full_size(dev, ta, tb):
+    # 8192 x 16 x 8192 row-major (the near-GEMV workload transposed): the
+    # skinny kernel on C^T = B^T A^T; sampled rows of C.
+    w = WORKLOADS["R_skinny"]
+    M, N, K = w.N, w.M, w.K
+    A, B, C, opA, opB = make_case(ROW, ta, tb, M, N, K, "uniform", 1700, 0.0, (0, 0, 0))
+    rc, out = run_ex(None, ROW, ta, tb, M, N, K, 1.0, 0.0, A, B, C, dev, tag="few-columns-full")
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    got = C.read_logical(out)
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, M - 1], rng.integers(0, M, 40)]))
+    Cr, br = oracle.sgemm_ref_rows(opA, opB, None, 1.0, 0.0, rows, M=M, N=N, K=K)
+    rep = check_bound(got[rows, :], Cr, br, K, rows=rows)
+    print(f"[gpu] R_skinny transposed row {ta}{tb}: {rep}", flush=True)
+    assert rep.ok, rep
 
 
 def test_gemm_helper_takes_transposed_views(dev):

@@ -136,6 +136,11 @@ def test_column_major_few_rows_take_the_skinny_kernel(ta, tb):
         rc, v = sg.sgemm_f32_plan_ex(COL, NT, NT, 16, 8192, 8192, 1.0, P, 1 << 24, P, 8192, 0.0, P,
                                      16, 256)
         assert rc == 0 and sg.sgemm_f32_variant_name(v) != "mfma_skinny"
+    # Row-major with few columns is the same transposed problem.
+    for (M, N, K) in ((8192, 16, 8192), (4096, 8, 4096), (33, 32, 100)):
+        lda, ldb, ldc = min_lds(ROW, ta, tb, M, N, K)
+        rc, v = sg.sgemm_f32_plan_ex(ROW, ta, tb, M, N, K, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
+        assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_skinny", (M, N, K)
     # 33 rows are not few
     lda, ldb, ldc = min_lds(COL, ta, tb, 33, 8192, 8192)
     rc, v = sg.sgemm_f32_plan_ex(COL, ta, tb, 33, 8192, 8192, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
