@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import json
 import math
+import random
 import sys
 from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
@@ -257,16 +258,19 @@ def _middle(x) -> float:
     return xs[len(xs) // 2]
 
 
-def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int) -> List[dict]:
+def check(model: Sequence[dict], samples: Sequence[dict], num_cus: int,
+          workspace: bool = True) -> List[dict]:
     """Per shape: the kernel the model picks, the fastest measured one, and
-    the time lost (fraction)."""
+    the time lost (fraction). Without `workspace` the stream-K kernels are
+    left out of both."""
     by_shape: Dict[Tuple[int, int, int], Dict[str, float]] = {}
     for s in samples:
-        by_shape.setdefault((s["M"], s["N"], s["K"]), {})[s["variant"]] = s["ms"]
+        if workspace or s["variant"] not in SK_BK:
+            by_shape.setdefault((s["M"], s["N"], s["K"]), {})[s["variant"]] = s["ms"]
     res = []
     for (M, N, K), d in by_shape.items():
         sub = [e for e in model if e["variant"] in d]
-        pick = choose(sub, M, N, K, num_cus, workspace=True, vec=packed_vec(M, N, K))
+        pick = choose(sub, M, N, K, num_cus, workspace=workspace, vec=packed_vec(M, N, K))
         fastest = min(d, key=d.get)
         res.append({"shape": [M, N, K], "picked": pick, "fastest": fastest,
                     "loss": round(d[pick] / d[fastest] - 1.0, 4)})
@@ -298,6 +302,12 @@ def main(argv=None) -> int:
     ap.add_argument("--quick", action="store_true", help="6 shapes instead of 30")
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--calls", type=int, default=4)
+    ap.add_argument("--random", type=int, default=0, metavar="N",
+                    help="N seeded random shapes (sides log-uniform in [300, 6000]) instead")
+    ap.add_argument("--seed", type=int, default=2026)
+    ap.add_argument("--check-installed", action="store_true",
+                    help="measure the shapes and report how the installed model (built-in, or "
+                         "--load) picks, without fitting: a held-out check")
     args = ap.parse_args(argv)
     import torch
     if not torch.cuda.is_available():
@@ -305,7 +315,15 @@ def main(argv=None) -> int:
         return 1
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     shapes = QUICK_SHAPES if args.quick else DEFAULT_SHAPES
-    if args.load:
+    if args.random:
+        rng = random.Random(args.seed)
+        shapes = [tuple(int(round(math.exp(rng.uniform(math.log(300), math.log(6000)))))
+                        for _ in range(3)) for _ in range(args.random)]
+    if args.load and args.check_installed:
+        rc = install(load(args.load))
+        if rc:
+            return 1
+    elif args.load:
         model = load(args.load)
         rc = install(model)
         print(json.dumps({"installed": args.load, "rc": rc}))
@@ -320,6 +338,24 @@ def main(argv=None) -> int:
         return 0 if rc == 0 else 1
     samples = measure(shapes, rounds=args.rounds, calls=args.calls,
                       log=lambda m: print(m, file=sys.stderr, flush=True))
+    if args.check_installed:
+        model = sg.sgemm_f32_get_model()
+        out = {"num_cus": cus, "samples": samples}
+        for ws in (False, True):
+            report = check(model, samples, cus, workspace=ws)
+            for r in report:
+                print(json.dumps({"workspace": ws, **r}))
+            summary = {"workspace": ws, "shapes": len(report),
+                       "picked_fastest": sum(r["loss"] == 0.0 for r in report),
+                       "worst_loss": max(r["loss"] for r in report),
+                       "mean_loss": round(sum(r["loss"] for r in report) / len(report), 4)}
+            print(json.dumps(summary))
+            out["check_workspace" if ws else "check"] = report
+            out["summary_workspace" if ws else "summary"] = summary
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump(out, f)
+        return 0
     model = fit(samples, cus)
     report = check(model, samples, cus)
     for e in model:
