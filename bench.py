@@ -2,7 +2,8 @@
 
 One step is one sgemm_f32 call (the whole hot path) on the 4096^3 workload
 (alpha = 1, beta = 0, A and B uniform in [-1, 1), seeded), inputs already in
-HBM. W untimed warm-up steps, then K timed steps between a device
+HBM. An untimed clock warm-up (0.5 s of calls by default, stated in the
+output), W untimed warm-up steps, then K timed steps between a device
 synchronisation on each side; per-step kernel durations come from HIP events
 recorded on the launch stream. Prints ONE JSON line.
 
@@ -14,6 +15,9 @@ Extra objects on that line:
                  current kernel source (else null).
   cpu_baseline - the FP64 CPU oracle timed on this host's cores over a bounded
                  sample of the same workload (whole output rows).
+  clock        - the shader clock read on the device right before and right
+                 after the timed steps (library clock probe), and rocm-smi's
+                 clock and power before the warm-up and after the timed steps.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload S4096]
                   [--variant auto|mfma_128x128|...] [--no-cpu-baseline]
@@ -117,6 +121,37 @@ def measured_peaks(dev, stream, cus: int) -> dict:
             best = max(best, flops / (a.elapsed_time(b) * 1e-3) / 1e12)
         res[name] = round(best, 2)
     return res
+
+
+def clock_probe_enqueue(dev, stream, cus: int):
+    """Enqueue the library's clock probe on `stream` (no host wait): 4 waves
+    of FP32 MFMAs per SIMD, like the GEMM, each workgroup reporting its
+    shader-clock and constant-rate counter differences. Called right after
+    the timed steps, it runs on the clock they left."""
+    import torch
+
+    import fp32_gemm_tuning_amd as sg
+    wgs = cus * 4
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    rc, _ = sg.sgemm_f32_peak_probe(3, wgs, 1024, out, stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"clock probe failed: {rc}")
+    return out
+
+
+def clock_probe_read(out) -> dict:
+    """Median, min and max over workgroups of the probe's clock, in MHz: the
+    ratio of the two counter differences times the constant counter rate."""
+    import numpy as np
+
+    import fp32_gemm_tuning_amd as sg
+    rc, wall_khz, max_khz = sg.sgemm_f32_clock_rates()
+    if rc != 0:
+        raise RuntimeError(f"sgemm_f32_clock_rates failed: {rc}")
+    v = out.view(-1, 256)[:, :2].cpu().numpy().astype(np.float64)
+    mhz = v[:, 0] / v[:, 1] * wall_khz / 1e3
+    return {"median": round(float(np.median(mhz)), 1), "min": round(float(mhz.min()), 1),
+            "max": round(float(mhz.max()), 1), "max_sclk_mhz": round(max_khz / 1e3, 1)}
 
 
 def time_calls(call, steps: int, warmup: int, stream):
@@ -412,6 +447,9 @@ def main() -> int:
     # 100 untimed steps (about 0.1 s at 4096^3) let the clock ramp up; with 5
     # the timed steps still see the ramp (about 3% lower).
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--clock-warmup-s", type=float, default=0.5,
+                    help="untimed seconds of back-to-back calls before the warm-up steps "
+                         "(0 to skip); reported in the output line")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -498,12 +536,22 @@ def main() -> int:
                                             w.beta, dC, w.N, sp)
     vname = sg.sgemm_f32_variant_name(vid)
 
+    smi_before = smi_snapshot()
+    # Untimed clock warm-up (stated in the output): a fixed stretch of calls
+    # brings the shader clock up from idle, so the timed steps do not depend
+    # on how many warm-up steps the caller asked for.
+    if args.clock_warmup_s > 0:
+        rc = call()
+        if rc != 0:
+            print(f"sgemm_f32 failed: {rc} {sg.sgemm_f32_strerror(rc)}", file=sys.stderr)
+            return 1
+        clock_warmup(call, args.clock_warmup_s)
     for _ in range(args.warmup):
         rc = call()
         if rc != 0:
             print(f"sgemm_f32 failed: {rc} {sg.sgemm_f32_strerror(rc)}", file=sys.stderr)
             return 1
-    torch.cuda.synchronize()
+    clk_before = clock_probe_read(clock_probe_enqueue(dev, stream, cus))
 
     K = args.steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -517,8 +565,11 @@ def main() -> int:
         if rc != 0:
             print(f"sgemm_f32 failed: {rc}", file=sys.stderr)
             return 1
+    clk_out = clock_probe_enqueue(dev, stream, cus)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall = time.perf_counter() - t0      # includes the clock probe's run (under 1 ms)
+    clk_after = clock_probe_read(clk_out)
+    smi_after = smi_snapshot()
     durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
     region_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = region_ms / K
@@ -558,6 +609,9 @@ def main() -> int:
                      "kernel_ms_min": round(float(durs.min()), 4),
                      "flops_per_launch": int(flops)},
         "wall_s_timed_region": round(wall, 3),
+        "clock": {"warmup_untimed_s": args.clock_warmup_s,
+                  "sclk_mhz_device_before": clk_before, "sclk_mhz_device_after": clk_after,
+                  "smi_before": smi_before, "smi_after": smi_after},
     }
     peaks = measured_peaks(dev, stream, cus)
     mpk = peaks["valu_fma_f32"] if is_valu else peaks["mfma_f32_32x32x2"]

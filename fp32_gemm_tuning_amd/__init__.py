@@ -27,6 +27,8 @@ or raw device addresses as ints; they return the C status code):
     sgemm_f32_ws_size(variant, layout, transa, transb, M, N, K, num_cus) -> (code, bytes)
     sgemm_f32_num_variants(), sgemm_f32_variant_name(v), sgemm_f32_variant_by_name(s),
     sgemm_f32_strerror(code), sgemm_f32_kernel_info(v) -> dict
+    sgemm_f32_peak_probe(kind, workgroups, iters, out, stream=None) -> (code, flops),
+    sgemm_f32_clock_rates() -> (code, wall_khz, max_sclk_khz)   (include/sgemm_f32_probe.h)
     sgemm_f32_set_model(entries) -> code, sgemm_f32_get_model() -> list of dicts
 
 Tensor helper:
@@ -138,6 +140,8 @@ def _load() -> ctypes.CDLL:
     lib.sgemm_f32_kernel_info.restype = c_int
     lib.sgemm_f32_peak_probe.argtypes = [c_int, c_int, c_int, vp, vp, ctypes.POINTER(ctypes.c_double)]
     lib.sgemm_f32_peak_probe.restype = c_int
+    lib.sgemm_f32_clock_rates.argtypes = [ip, ip]
+    lib.sgemm_f32_clock_rates.restype = c_int
     lib.sgemm_f32_set_model.argtypes = [ctypes.POINTER(ModelEntry), c_int]
     lib.sgemm_f32_set_model.restype = c_int
     lib.sgemm_f32_get_model.argtypes = [ctypes.POINTER(ModelEntry), c_int]
@@ -292,6 +296,13 @@ def sgemm_f32_peak_probe(kind: int, workgroups: int, iters: int, out, stream=Non
     rc = _lib.sgemm_f32_peak_probe(int(kind), int(workgroups), int(iters), _ptr(out),
                                    _stream(stream, out), ctypes.byref(fl))
     return int(rc), float(fl.value)
+
+
+def sgemm_f32_clock_rates() -> Tuple[int, int, int]:
+    """(code, constant counter rate kHz, peak shader clock kHz) of the current device."""
+    w, m = ctypes.c_int(0), ctypes.c_int(0)
+    rc = _lib.sgemm_f32_clock_rates(ctypes.byref(w), ctypes.byref(m))
+    return int(rc), int(w.value), int(m.value)
 
 
 def sgemm_f32_set_model(entries) -> int:

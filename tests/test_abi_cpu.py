@@ -44,7 +44,7 @@ def test_variant_enum_matches_names():
 
 
 @pytest.mark.parametrize("code", [0, -1, -2, -3, -5, -6, -7, -8, -10, -11, -12, -100, -101,
-                                  -102, -103, -999])
+                                  -102, -103, -104, -999])
 def test_strerror_is_static_text(code):
     s = sg.sgemm_f32_strerror(code)
     assert isinstance(s, str) and len(s) > 3

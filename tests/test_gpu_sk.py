@@ -157,7 +157,7 @@ def test_stream_k_needs_its_workspace(dev, cus):
 
 def test_auto_with_workspace_on_a_split_shape(dev, cus):
     # 3072^3 through sgemm_f32_ws: whatever it picks must match the oracle
-    # (sampled rows and columns).
+    # on every element.
     M = N = K = 3072
     A, B, C0, _, _ = operands(M, N, K, "uniform", 9, 0.0)
     rc, C, wsb = call_sk(None, M, N, K, 1.0, 0.0, A, B, C0, dev, cus, tag="sk-auto")
@@ -165,11 +165,8 @@ def test_auto_with_workspace_on_a_split_shape(dev, cus):
     _, v = sg.sgemm_f32_plan_ws(ROW, 0, 0, M, N, K, 1.0, 0x1000, K, 0x1000, N, 0.0, 0x1000, N,
                                 wsb, cus)
     print(f"[gpu] 3072^3 with workspace -> {sg.sgemm_f32_variant_name(v)}", flush=True)
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 127, 128, 2047, 2048, M - 1], rng.integers(0, M, 24)]))
-    cols = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.integers(0, N, 24)]))
-    Cr, br = oracle.sgemm_ref_rows(A, B, None, 1.0, 0.0, rows)
-    Cc, bc = oracle.sgemm_ref_cols(A, B, None, 1.0, 0.0, cols)
-    for rep in (check_bound(C[rows, :], Cr, br, K, rows=rows),
-                check_bound(C[:, cols], Cc, bc, K, cols=cols)):
-        assert rep.ok, rep
+    Cref, babs = oracle.sgemm_ref(A, B, None, 1.0, 0.0)
+    rep = check_bound(C, Cref, babs, K)
+    print(f"[gpu] 3072^3 with workspace: {rep}", flush=True)
+    assert rep.n == M * N
+    assert rep.ok, rep

@@ -228,23 +228,17 @@ def test_transposed_auto(dev, combo, shape):
                          ids=combo_id)
 def test_transposed_headline_size(dev, combo):
     # 4096^3 through the automatic choice (the 256x256 kernel's full-tile
-    # instance), checked on sampled rows and columns.
+    # instance), every element checked.
     layout, ta, tb = combo
     w = WORKLOADS["S4096"]
     M, N, K = w.M, w.N, w.K
     A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, "uniform", 4096, 0.0, (0, 0, 0))
     rc, out = run_ex(None, layout, ta, tb, M, N, K, 1.0, 0.0, A, B, C, dev, tag="trans-S4096")
     assert rc == 0, sg.sgemm_f32_strerror(rc)
-    got = C.read_logical(out)
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 1], rng.integers(0, M, 24)]))
-    cols = np.unique(np.concatenate([[0, 1, 255, 256, N - 1], rng.integers(0, N, 24)]))
-    Cr, br = oracle.sgemm_ref_rows(opA, opB, None, 1.0, 0.0, rows, M=M, N=N, K=K)
-    Cc, bc = oracle.sgemm_ref_cols(opA, opB, None, 1.0, 0.0, cols, M=M, N=N, K=K)
-    for rep in (check_bound(got[rows, :], Cr, br, K, rows=rows),
-                check_bound(got[:, cols], Cc, bc, K, cols=cols)):
-        print(f"[gpu] S4096 {combo_id(combo)}: {rep}", flush=True)
-        assert rep.ok, f"{combo_id(combo)}: {rep}"
+    rep = check(out, C, opA, opB, M, N, K, 1.0, 0.0, exact=False)
+    print(f"[gpu] S4096 {combo_id(combo)}: {rep}", flush=True)
+    assert rep.n == M * N
+    assert rep.ok, f"{combo_id(combo)}: {rep}"
 
 
 @pytest.mark.parametrize("combo", [(COL, NT, NT), (COL, T, T), (ROW, T, NT), (ROW, NT, T)],
@@ -252,37 +246,31 @@ def test_transposed_headline_size(dev, combo):
 def test_few_rows_full_size(dev, combo):
     # 16 x 8192 x 8192 (the near-GEMV workload) through the automatic choice:
     # column-major runs the skinny kernel unswapped, row-major with a
-    # transposed operand reads it in place; every row, sampled columns.
+    # transposed operand reads it in place; every element checked.
     layout, ta, tb = combo
     w = WORKLOADS["R_skinny"]
     M, N, K = w.M, w.N, w.K
     A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, "uniform", 1600, 0.0, (0, 0, 0))
     rc, out = run_ex(None, layout, ta, tb, M, N, K, 1.0, 0.0, A, B, C, dev, tag="few-rows-R_skinny")
     assert rc == 0, sg.sgemm_f32_strerror(rc)
-    got = C.read_logical(out)
-    rng = np.random.default_rng(7)
-    cols = np.unique(np.concatenate([[0, 1, 31, 32, N - 1], rng.integers(0, N, 40)]))
-    Cc, bc = oracle.sgemm_ref_cols(opA, opB, None, 1.0, 0.0, cols, M=M, N=N, K=K)
-    rep = check_bound(got[:, cols], Cc, bc, K, cols=cols)
+    rep = check(out, C, opA, opB, M, N, K, 1.0, 0.0, exact=False)
     print(f"[gpu] R_skinny {combo_id(combo)}: {rep}", flush=True)
+    assert rep.n == M * N
     assert rep.ok, f"{combo_id(combo)}: {rep}"
 
 
 @pytest.mark.parametrize("ta,tb", [(NT, NT), (T, T)], ids=["NN", "TT"])
 def test_few_columns_full_size(dev, ta, tb):
     # 8192 x 16 x 8192 row-major (the near-GEMV workload transposed): the
-    # skinny kernel on C^T = B^T A^T; sampled rows of C.
+    # skinny kernel on C^T = B^T A^T; every element checked.
     w = WORKLOADS["R_skinny"]
     M, N, K = w.N, w.M, w.K
     A, B, C, opA, opB = make_case(ROW, ta, tb, M, N, K, "uniform", 1700, 0.0, (0, 0, 0))
     rc, out = run_ex(None, ROW, ta, tb, M, N, K, 1.0, 0.0, A, B, C, dev, tag="few-columns-full")
     assert rc == 0, sg.sgemm_f32_strerror(rc)
-    got = C.read_logical(out)
-    rng = np.random.default_rng(8)
-    rows = np.unique(np.concatenate([[0, 1, 15, 16, M - 1], rng.integers(0, M, 40)]))
-    Cr, br = oracle.sgemm_ref_rows(opA, opB, None, 1.0, 0.0, rows, M=M, N=N, K=K)
-    rep = check_bound(got[rows, :], Cr, br, K, rows=rows)
+    rep = check(out, C, opA, opB, M, N, K, 1.0, 0.0, exact=False)
     print(f"[gpu] R_skinny transposed row {ta}{tb}: {rep}", flush=True)
+    assert rep.n == M * N
     assert rep.ok, rep
 
 
