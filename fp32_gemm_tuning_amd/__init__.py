@@ -25,6 +25,9 @@ or raw device addresses as ints; they return the C status code):
     sgemm_f32_plan_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                       workspace_bytes, num_cus) -> (code, variant)
     sgemm_f32_ws_size(variant, layout, transa, transb, M, N, K, num_cus) -> (code, bytes)
+    sgemm_f32_ws_static(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb,
+                        beta, C, ldc, stream=None)   (variant -1: automatic; no workspace
+                        argument: the library's fixed SCRATCH_BYTES device scratch)
     sgemm_f32_num_variants(), sgemm_f32_variant_name(v), sgemm_f32_variant_by_name(s),
     sgemm_f32_strerror(code), sgemm_f32_kernel_info(v) -> dict
     sgemm_f32_peak_probe(kind, workgroups, iters, out, stream=None) -> (code, flops),
@@ -54,6 +57,9 @@ ERR_UNSUPPORTED = -101
 ERR_TOO_LARGE = -102
 ERR_DEVICE = -103
 ERR_WORKSPACE = -104
+ERR_SCRATCH = -105
+# SGEMM_F32_SCRATCH_BYTES: the fixed device scratch of sgemm_f32_ws_static
+SCRATCH_BYTES = 32 * 1024 * 1024
 
 ROW_MAJOR, COL_MAJOR = 0, 1
 NO_TRANS, TRANS = 0, 1
@@ -119,6 +125,8 @@ def _load() -> ctypes.CDLL:
     lib.sgemm_f32_variant_ws.restype = c_int
     lib.sgemm_f32_plan_ws.argtypes = [c_int, c_int, c_int] + gemm_args + [sz, c_int, ctypes.POINTER(c_int)]
     lib.sgemm_f32_plan_ws.restype = c_int
+    lib.sgemm_f32_ws_static.argtypes = [c_int, c_int, c_int, c_int] + gemm_args + [vp]
+    lib.sgemm_f32_ws_static.restype = c_int
     lib.sgemm_f32_ws_size.argtypes = [c_int, c_int, c_int, c_int, i64, i64, i64, c_int,
                                       ctypes.POINTER(sz)]
     lib.sgemm_f32_ws_size.restype = c_int
@@ -234,6 +242,14 @@ def sgemm_f32_variant_ws(variant, layout, transa, transb, M, N, K, alpha, A, lda
                                          _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
                                          _ptr(workspace), int(workspace_bytes),
                                          _stream(stream, C, A, B)))
+
+
+def sgemm_f32_ws_static(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                        ldc, stream=None) -> int:
+    return int(_lib.sgemm_f32_ws_static(int(variant), int(layout), int(transa), int(transb),
+                                        int(M), int(N), int(K), float(alpha), _ptr(A), int(lda),
+                                        _ptr(B), int(ldb), float(beta), _ptr(C), int(ldc),
+                                        _stream(stream, C, A, B)))
 
 
 def sgemm_f32_plan_ws(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

@@ -294,9 +294,12 @@ static int validate_ws(const void* ws, size_t ws_bytes) {
     return (ws_bytes > 0 && (ws == nullptr || misaligned16(ws))) ? -16 : 0;
 }
 
+// `ws_short` is the code returned when a forced stream-K variant needs more
+// workspace than `ws_bytes`.
 static int run(int forced, int layout, int transa, int transb, int64_t M, int64_t N, int64_t K,
                float alpha, const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
-               float* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+               float* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream,
+               int ws_short = SGEMM_F32_ERR_WORKSPACE) {
     if (forced >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
     int rc = validate(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc) return rc;
@@ -322,12 +325,41 @@ static int run(int forced, int layout, int transa, int transb, int64_t M, int64_
     if (rc) return rc;
     hipError_t e;
     if (var.launch_ws != nullptr) {
-        if (var.ws_size(a, cus) > ws_bytes) return SGEMM_F32_ERR_WORKSPACE;
+        if (var.ws_size(a, cus) > ws_bytes) return ws_short;
         e = var.launch_ws(a, ws, ws_bytes, cus, s);
     } else {
         e = var.launch(a, s);
     }
     return e == hipSuccess ? 0 : (int)e;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch for sgemm_f32_ws_static: the stream-K partial tiles of
+// callers that cannot allocate. Each device the library runs on holds its own
+// copy from the code object's load until the process ends. In host code the
+// name `scratch` is only a stand-in for the symbol, never a device address:
+// kernels get the address hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------
+static constexpr size_t kScratchBytes = SGEMM_F32_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current) and kept. Concurrent first calls may both look it up;
+// they get the same address.
+static int scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return SGEMM_F32_ERR_DEVICE;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (p == nullptr) return SGEMM_F32_ERR_DEVICE;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return 0;
 }
 
 static int plan(int layout, int transa, int transb, int64_t M, int64_t N, int64_t K, float alpha,
@@ -447,6 +479,22 @@ SGEMM_F32_API int sgemm_f32_variant_ws(int variant, int layout, int transa, int 
                workspace, workspace_bytes, stream);
 }
 
+SGEMM_F32_API int sgemm_f32_ws_static(int variant, int layout, int transa, int transb, int64_t M,
+                                      int64_t N, int64_t K, float alpha, const float* A,
+                                      int64_t lda, const float* B, int64_t ldb, float beta,
+                                      float* C, int64_t ldc, void* stream) {
+    if (variant < -1 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
+    // Argument errors and the empty product are reported before any HIP call.
+    int rc = validate(layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return 0;
+    void* ws = nullptr;
+    rc = scratch_ptr(&ws);
+    if (rc) return rc;
+    return run(variant, layout, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws,
+               kScratchBytes, stream, SGEMM_F32_ERR_SCRATCH);
+}
+
 SGEMM_F32_API int sgemm_f32_plan_ws(int layout, int transa, int transb, int64_t M, int64_t N,
                                     int64_t K, float alpha, const float* A, int64_t lda,
                                     const float* B, int64_t ldb, float beta, const float* C,
@@ -511,6 +559,8 @@ SGEMM_F32_API const char* sgemm_f32_strerror(int code) {
         case -15: return "transb is neither SGEMM_F32_NO_TRANS nor SGEMM_F32_TRANS";
         case -16: return "workspace is NULL with a nonzero size, or not 16-byte aligned";
         case SGEMM_F32_ERR_WORKSPACE: return "the stream-K variant needs a larger workspace (sgemm_f32_ws_size)";
+        case SGEMM_F32_ERR_SCRATCH: return "the stream-K variant needs more workspace than the "
+                                           "library's fixed scratch holds (SGEMM_F32_SCRATCH_BYTES)";
         case SGEMM_F32_ERR_VARIANT: return "variant id out of range";
         case SGEMM_F32_ERR_UNSUPPORTED: return "variant cannot run this shape, alignment or transposition";
         case SGEMM_F32_ERR_TOO_LARGE: return "a size exceeds what the kernel can index";

@@ -51,9 +51,13 @@
  *                               workspace than sgemm_f32_ws_size reports
  *    -16                    (the _ws entry points) the workspace pointer is
  *                           NULL with a nonzero size, or not 16-byte aligned
+ *    SGEMM_F32_ERR_SCRATCH  (sgemm_f32_ws_static) the forced stream-K variant
+ *                           needs more than the fixed scratch holds
  *   > 0                     a hipError_t reported by the HIP runtime at launch
  *
- * Thread safety: all entry points are reentrant.
+ * Thread safety: all entry points are reentrant, except that calls of
+ * sgemm_f32_ws_static whose executions overlap on one GPU share its scratch
+ * (see there).
  */
 #ifndef SGEMM_F32_H
 #define SGEMM_F32_H
@@ -77,6 +81,10 @@ extern "C" {
 #define SGEMM_F32_ERR_TOO_LARGE (-102)
 #define SGEMM_F32_ERR_DEVICE (-103)
 #define SGEMM_F32_ERR_WORKSPACE (-104)
+#define SGEMM_F32_ERR_SCRATCH (-105)
+
+/* Size of the fixed device scratch behind sgemm_f32_ws_static (32 MiB). */
+#define SGEMM_F32_SCRATCH_BYTES (32u * 1024u * 1024u)
 
 /* Kernel variants. The first six are the rungs of the pages' optimisation
  * ladder, rebuilt for wave64; the rest are the gfx950 kernels the automatic
@@ -273,6 +281,33 @@ SGEMM_F32_API int sgemm_f32_variant_ws(int variant, int layout, int transa, int 
                                        int64_t lda, const float *B, int64_t ldb, float beta,
                                        float *C, int64_t ldc, void *workspace,
                                        size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * stream-K entry points with the library's own fixed scratch as the
+ * workspace, so that nothing is allocated, on the call path or before it.
+ * variant == -1 is sgemm_f32_ws with workspace_bytes =
+ * SGEMM_F32_SCRATCH_BYTES: the automatic choice, whose stream-K candidates
+ * are only those whose workspace fits the scratch. variant >= 0 is
+ * sgemm_f32_variant_ws with that workspace; a stream-K variant that would
+ * need more than SGEMM_F32_SCRATCH_BYTES on this problem returns
+ * SGEMM_F32_ERR_SCRATCH before anything is launched. Arguments, ownership of
+ * A, B and C, asynchrony and the other return codes are those of
+ * sgemm_f32_ws / sgemm_f32_variant_ws; SGEMM_F32_ERR_VARIANT for variant < -1.
+ *
+ * The scratch is one file-scope device array per GPU, held from the library's
+ * first use on that GPU until the process ends; its address is looked up
+ * once per device (hipGetSymbolAddress, no allocation) on the first call with
+ * that device current. Every call on one GPU shares it and it keeps the last
+ * call's contents (the kernels never read what they have not written in the
+ * same call, so nothing is cleared). Calls on one GPU whose executions can
+ * overlap -- different streams without an ordering between them -- race on
+ * the scratch and may return wrong results: order them, or use sgemm_f32_ws
+ * with one workspace per stream. Calls on the same stream are ordered. */
+SGEMM_F32_API int sgemm_f32_ws_static(int variant, int layout, int transa, int transb, int64_t M,
+                                      int64_t N, int64_t K, float alpha, const float *A,
+                                      int64_t lda, const float *B, int64_t ldb, float beta,
+                                      float *C, int64_t ldc, void *stream);
 
 /* The variant sgemm_f32_ws would launch with `workspace_bytes` of workspace,
  * as sgemm_f32_plan (host-only). */

@@ -44,7 +44,7 @@ def test_variant_enum_matches_names():
 
 
 @pytest.mark.parametrize("code", [0, -1, -2, -3, -5, -6, -7, -8, -10, -11, -12, -100, -101,
-                                  -102, -103, -104, -999])
+                                  -102, -103, -104, -105, -999])
 def test_strerror_is_static_text(code):
     s = sg.sgemm_f32_strerror(code)
     assert isinstance(s, str) and len(s) > 3
@@ -73,6 +73,39 @@ def test_argument_errors(args, code):
     assert sg.sgemm_f32(*args, stream=0) == code
     assert sg.sgemm_f32_variant(0, *args, stream=0) == code
     assert sg.sgemm_f32_plan(*args, 256)[0] == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4), -1),
+    ((4, 4, 4, 1.0, 0, 4, P, 4, 0.0, P, 4), -5),
+    ((4, 4, 8, 1.0, P, 7, P, 4, 0.0, P, 4), -6),
+    ((4, 4, 4, 1.0, P, 4, P, 4, 0.0, P + 1, 4), -10),
+])
+def test_ws_static_argument_errors_before_any_hip_call(args, code):
+    # The fixed-scratch entry point checks its arguments before it looks up
+    # the scratch on a device, so these need no GPU.
+    for v in (-1, 7):
+        assert sg.sgemm_f32_ws_static(v, sg.ROW_MAJOR, 0, 0, *args, stream=0) == code
+    assert sg.sgemm_f32_ws_static(-1, 2, 0, 0, *args, stream=0) == -13
+    assert sg.sgemm_f32_ws_static(-1, 0, 2, 0, *args, stream=0) == -14
+
+
+def test_ws_static_variant_range_and_empty_product():
+    args = (4, 4, 4, 1.0, P, 4, P, 4, 0.0, P, 4)
+    assert sg.sgemm_f32_ws_static(-2, 0, 0, 0, *args, stream=0) == sg.ERR_VARIANT
+    assert sg.sgemm_f32_ws_static(len(sg.VARIANTS), 0, 0, 0, *args, stream=0) == sg.ERR_VARIANT
+    # M == 0 or N == 0: nothing touched, no device needed
+    assert sg.sgemm_f32_ws_static(-1, 0, 0, 0, 0, 4, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, stream=0) == 0
+    assert sg.sgemm_f32_ws_static(-1, 1, 0, 0, 4, 0, 4, 1.0, 0, 4, 0, 4, 0.0, 0, 4, stream=0) == 0
+
+
+def test_scratch_size_matches_header():
+    m = re.search(r"#define\s+SGEMM_F32_SCRATCH_BYTES\s+\((\d+)u \* (\d+)u \* (\d+)u\)",
+                  _header_text())
+    assert m is not None
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == sg.SCRATCH_BYTES
+    m = re.search(r"#define\s+SGEMM_F32_ERR_SCRATCH\s+\((-\d+)\)", _header_text())
+    assert int(m.group(1)) == sg.ERR_SCRATCH
 
 
 def test_unread_operands_may_be_null():
