@@ -551,11 +551,14 @@ def main() -> int:
         if rc != 0:
             print(f"sgemm_f32 failed: {rc} {sg.sgemm_f32_strerror(rc)}", file=sys.stderr)
             return 1
-    clk_before = clock_probe_read(clock_probe_enqueue(dev, stream, cus))
-
+    # Both clock probes are read only after the timed steps: a host stall of
+    # 10 ms or more between the warm-up and the timed steps (a read-back, say)
+    # is followed by about 40 calls that run up to 20% slower while the shader
+    # clock reads unchanged, so nothing but a synchronisation separates them.
     K = args.steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    clk_before_out = clock_probe_enqueue(dev, stream, cus)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -568,6 +571,7 @@ def main() -> int:
     clk_out = clock_probe_enqueue(dev, stream, cus)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0      # includes the clock probe's run (under 1 ms)
+    clk_before = clock_probe_read(clk_before_out)
     clk_after = clock_probe_read(clk_out)
     smi_after = smi_snapshot()
     durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
