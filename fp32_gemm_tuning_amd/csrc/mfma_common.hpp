@@ -212,6 +212,156 @@ struct OperandFill {
     }
 };
 
+// One operand's part of a K slice, filled through registers with 16-byte
+// loads from addresses that need only be 4-byte aligned (gfx950 serves
+// unaligned vector loads from global memory): for rows that are not whole
+// 16-byte chunks (a leading dimension, contiguous extent or base address
+// that is not a multiple of 4 floats), where the buffer-to-LDS fill would
+// need one 4-byte load per element. The LDS layout and the lane of each
+// chunk are those of OperandFill's 16-byte form (the lane inverts the A
+// swizzle, so a wave's LDS writes are 1 KiB contiguous).
+//
+// No 16-byte load reaches past the operand's valid elements. A chunk whose
+// four elements are all valid loads them directly. A chunk that straddles
+// the end of the valid range along its contiguous dimension (the K tail for a
+// k-contiguous operand, the edge of M or N for a row-contiguous one), with
+// v < 4 valid elements, loads the last four valid elements instead, starting
+// 4 - v elements earlier, and its lanes shift them down in registers and zero
+// the rest. Chunks with no valid element read as zero: through the
+// out-of-range offset, or, for the k rows of a row-contiguous operand past
+// the K tail, because the slice's resource ends before them.
+//
+// Per-lane offsets are fixed for a tile (init): a whole slice of a
+// k-contiguous operand only moves the resource base by the slice's k0, and
+// every slice of a row-contiguous one moves it by k0 rows. Only the K-tail
+// slice of a k-contiguous operand computes its offsets per lane. The host
+// keeps the contiguous extent of the whole operand (K, or M/N) at least 4, so
+// a shifted start never precedes the row, and (rows - 1) * ld + extent below
+// 2^31 bytes.
+template <int ROWS, int BK, int NT, bool KCONTIG>
+struct OperandFillU {
+    static constexpr int W = NT / 64;
+    static constexpr int TOTAL = ROWS * BK / 256;       // pieces of 64 chunks
+    static_assert(TOTAL * 256 == ROWS * BK, "tile/instruction mismatch");
+    static constexpr int INSTR = (TOTAL + W - 1) / W;   // per wave per slice, at most
+    static constexpr bool EVEN = TOTAL % W == 0;
+    static constexpr int CPR = BK / 4;                  // 16-byte chunks per k-contiguous row
+    static constexpr int CPK = ROWS / 4;                // chunks per k row of a row-contiguous one
+    static_assert(ROWS % 4 == 0, "whole chunks per k row");
+
+    f32x4 v[INSTR];
+    uint32_t off[INSTR];   // byte offsets of a whole slice from its resource base (OOB: zero)
+    int sh[INSTR];         // (row-contiguous) shift of a straddling chunk, else 0
+    int kk;                // valid k of the slice in flight
+    int edge;              // (row-contiguous) some chunk straddles the edge of M or N
+
+    // Offsets from the resource base of a slice: row `line` of the tile at
+    // k0 (k-contiguous), or k row `line` of the slice at column 0
+    // (row-contiguous).
+    __device__ __forceinline__ void init(int64_t ld, int r0, int rows_valid, int t) {
+        const int ldi = (int)ld;
+        const int w = t >> 6, lane = t & 63;
+        edge = KCONTIG ? 0 : (rows_valid & 3);
+#pragma unroll
+        for (int p = 0; p < INSTR; ++p) {
+            const int slot = (w + W * p) * 64 + lane;
+            if (KCONTIG) {
+                const int line = slot / CPR, q = (slot % CPR) ^ swz_chunk<BK>(line);
+                off[p] = line < rows_valid ? (uint32_t)((line * ldi + 4 * q) * 4) : OOB;
+                sh[p] = 0;
+            } else {
+                const int line = slot / CPK, c = r0 + 4 * (slot % CPK), cend = r0 + rows_valid;
+                const bool straddle = c < cend && c + 4 > cend;
+                off[p] = c < cend ? (uint32_t)((line * ldi + (straddle ? cend - 4 : c)) * 4) : OOB;
+                sh[p] = straddle ? c + 4 - cend : 0;
+            }
+        }
+    }
+
+    // Global -> registers for the slice starting at k0 of rows r0 .. r0 +
+    // rows_valid - 1 (X as stored: element (row, k) at X[row*ld + k] when
+    // k-contiguous, else X[k*ld + row]).
+    __device__ __forceinline__ void load(const float* X, int64_t ld, int r0, int k0, int K,
+                                         int rows_valid, int t) {
+        const int kr = K - k0;
+        kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < BK ? kr : BK));
+        const int w = t >> 6, lane = t & 63;
+        if (KCONTIG && kk > 0 && kk < BK) {
+            // The K tail: per-lane range checks and shifted starts, from a
+            // resource at column 0 of the tile's first row.
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(
+                X + (int64_t)r0 * ld, (uint32_t)(((int64_t)(rows_valid - 1) * ld + k0 + kk) * 4));
+            const int ldi = (int)ld, cend = k0 + kk;
+#pragma unroll
+            for (int p = 0; p < INSTR; ++p) {
+                const int piece = w + W * p;
+                if (!EVEN && piece >= TOTAL) break;
+                const int slot = piece * 64 + lane;
+                const int line = slot / CPR, c0 = k0 + 4 * ((slot % CPR) ^ swz_chunk<BK>(line));
+                const bool ok = line < rows_valid && c0 < cend;
+                const int cs = c0 + 4 <= cend ? c0 : cend - 4;
+                v[p] = buf_load4(r, ok ? (uint32_t)((line * ldi + cs) * 4) : OOB);
+            }
+            return;
+        }
+        __amdgpu_buffer_rsrc_t r;
+        if (KCONTIG)
+            r = make_rsrc(X + (int64_t)r0 * ld + k0,
+                          kk > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * ld + BK) * 4) : 0u);
+        else
+            r = make_rsrc(X + (int64_t)k0 * ld,
+                          kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * ld + r0 + rows_valid) * 4) : 0u);
+#pragma unroll
+        for (int p = 0; p < INSTR; ++p) {
+            if (!EVEN && w + W * p >= TOTAL) break;
+            v[p] = buf_load4(r, off[p]);
+        }
+    }
+
+    // Registers -> LDS at dst_base (the operand's part of the stage), for the
+    // slice `load` last fetched (k0 as given there).
+    __device__ __forceinline__ void store(float* dst_base, int k0, int t) const {
+        const int w = t >> 6, lane = t & 63;
+#pragma unroll
+        for (int p = 0; p < INSTR; ++p) {
+            const int piece = w + W * p;
+            if (!EVEN && piece >= TOTAL) break;
+            const int slot = piece * 64 + lane;
+            f32x4 x = v[p];
+            int s = 0;
+            if (KCONTIG) {
+                if (kk & 3) {   // the K tail with a straddling chunk
+                    const int c0 = k0 + 4 * ((slot % CPR) ^ swz_chunk<BK>(slot / CPR)), cend = k0 + kk;
+                    s = (c0 < cend && c0 + 4 > cend) ? c0 + 4 - cend : 0;
+                }
+            } else if (edge) {
+                s = sh[p];
+            }
+            if ((KCONTIG && (kk & 3)) || (!KCONTIG && edge)) {
+                // Lanes of a straddling chunk hold the elements from its
+                // shifted start; move element e + s to e and zero the rest.
+                const float e0 = s == 0 ? x.x : s == 1 ? x.y : s == 2 ? x.z : x.w;
+                const float e1 = s == 0 ? x.y : s == 1 ? x.z : s == 2 ? x.w : 0.0f;
+                const float e2 = s == 0 ? x.z : s == 1 ? x.w : 0.0f;
+                const float e3 = s == 0 ? x.w : 0.0f;
+                x = f32x4{e0, e1, e2, e3};
+            }
+            *(f32x4*)(dst_base + slot * 4) = x;
+        }
+    }
+};
+
+// Host side of OperandFillU: the contiguous extent of each operand (K of A,
+// N of B; M of a transposed A, K of a transposed B) is at least 4, and every
+// offset of a slice's resource stays below 2^31 bytes.
+static inline bool fillu_ok(const Args& a, int BM, int BN, int BK) {
+    const int64_t ca = a.ta ? a.M : a.K, cb = a.tb ? a.K : a.N;
+    if (ca < 4 || cb < 4) return false;
+    const int64_t ea = a.ta ? ((int64_t)(BK - 1) * a.lda + a.M) * 4 : ((int64_t)(BM - 1) * a.lda + a.K) * 4;
+    const int64_t eb = a.tb ? ((int64_t)(BN - 1) * a.ldb + a.K) * 4 : ((int64_t)(BK - 1) * a.ldb + a.N) * 4;
+    return ea < (int64_t)OOB && eb < (int64_t)OOB;
+}
+
 // Both operands of a slice. TA / TB: the operand is stored transposed (A as
 // K x M, B as N x K, row-major), which makes A row-contiguous and B
 // k-contiguous.

@@ -89,10 +89,17 @@ struct SubstepMma {
 // the result does not depend on timing. One workgroup per compute unit
 // (96 KB of LDS).
 // ===========================================================================
-template <int BM, int BN, int WM, int WN, int BK, bool VEC, bool TA = false, bool TB = false>
+// How the K-group kernels fill a slice: buffer-to-LDS loads of 16 bytes
+// (every operand row a whole number of 16-byte chunks), 16-byte loads
+// through registers from 4-byte aligned rows (OperandFillU), or
+// buffer-to-LDS loads of 4 bytes (any rows).
+enum KgFill { KG_DMA4 = 0, KG_U16 = 1, KG_DMA16 = 2 };
+
+template <int BM, int BN, int WM, int WN, int BK, int FILL, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(4 * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN), (BM / WM) * (BN / WN))))
 void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
+    constexpr bool VEC = FILL == KG_DMA16;
     constexpr int KG = 4;
     constexpr int GT = (BM / WM) * (BN / WN) * 64;  // threads per K-group
     constexpr int WAVES_N = BN / WN;
@@ -128,23 +135,30 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // This group's part of a stage starts at g * BM * BK (A) and
-    // g * BK * BNP (B). With 16-byte fills each group runs the pipelined main
-    // loop (PipeCore) over its slices g, g + KG, g + 2 KG, ...; the ring's
-    // barriers are the workgroup's, so every group takes the same number of
-    // steps, and a group's slices past the end of K load as zeros. With
-    // 4-byte fills (several times as many loads per slice, and more
-    // registers in flight) the plain double-buffered loop below is faster:
-    // the pipelined one measured 2-5% slower there, and it spilled in the
-    // 64x64-wave groups.
+    // g * BK * BNP (B). With 16-byte fills, buffer-to-LDS or through
+    // registers (U16), each group runs the pipelined main loop (PipeCore)
+    // over its slices g, g + KG, g + 2 KG, ...; the ring's barriers are the
+    // workgroup's, so every group takes the same number of steps, and a
+    // group's slices past the end of K load as zeros. With 4-byte fills
+    // (several times as many loads per slice, and more registers in flight)
+    // the plain double-buffered loop below is faster: the pipelined one
+    // measured 2-5% slower there, and it spilled in the 64x64-wave groups.
     const int nslices = (a.K + BK - 1) / BK;
-    if constexpr (VEC) {
-        using Core = PipeCore<BM, BN, WM, WN, BK, 2, true, false, TA, TB>;
+    if constexpr (FILL == KG_DMA16 || FILL == KG_U16) {
+        using Core = PipeCore<BM, BN, WM, WN, BK, 2, VEC, false, TA, TB, FILL == KG_U16>;
         static_assert(Core::NT == GT && Core::LDS_A == BM * BK && Core::LDS_B == BK * BNP,
                       "the group's pipeline works in the group's part of each stage");
         const Core core(a, tm, tn, tl);
         float* const Ast[4] = {As0 + g * BM * BK, As1 + g * BM * BK, nullptr, nullptr};
         float* const Bst[4] = {Bs0 + g * BK * BNP, Bs1 + g * BK * BNP, nullptr, nullptr};
-        core.template mainloop<KG>(a, 0, (nslices + KG - 1) / KG, Ast, Bst, acc, g);
+        // Group g has (nslices - g + KG - 1) / KG slices, one fewer than the
+        // first groups' when KG does not divide nslices; its last step then
+        // multiplies nothing. (The 64x64-wave groups, with 64 accumulators
+        // per lane, have no registers to spare for the split-off last step
+        // and multiply the zeros.)
+        constexpr bool GUARD = PER_LANE <= 32;
+        core.template mainloop<KG, GUARD>(a, 0, (nslices + KG - 1) / KG, Ast, Bst, acc, g,
+                                          (nslices - g + KG - 1) / KG);
     } else {
         const SubstepMma<BM, BNP, WM, WN, BK, TA, TB> mma(wm, wn, h, c, g * BM * BK, g * BK * BNP);
         auto compute = [&](const float* Ac, const float* Bc) { mma(Ac, Bc, acc); };
@@ -242,7 +256,13 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
             }
 }
 
-template <int BM, int BN, int WM, int WN, int BK = 16>
+// U16: whether calls with rows that are not whole 16-byte chunks take the
+// register-staged 16-byte fill (its 16 staging registers must fit the
+// occupancy target) rather than 4-byte buffer-to-LDS loads.
+#ifndef SGEMM_KG_U16
+#define SGEMM_KG_U16 1
+#endif
+template <int BM, int BN, int WM, int WN, int BK = 16, bool U16 = SGEMM_KG_U16 != 0>
 struct KgroupInstance {
     static constexpr int NT = 4 * (BM / WM) * (BN / WN) * 64;
     static constexpr int kBM = BM, kBN = BN, kBK = BK;
@@ -251,22 +271,32 @@ struct KgroupInstance {
         const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
         return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
     }
+    // The fill a call takes: 16-byte buffer-to-LDS loads when every row is
+    // whole 16-byte chunks, else 16-byte loads through registers when the
+    // extents allow them (U16), else 4-byte buffer-to-LDS loads.
+    static int fill(const Args& a) {
+        if (vec_ok(a)) return KG_DMA16;
+        return (U16 && fillu_ok(a, BM, BN, BK)) ? KG_U16 : KG_DMA4;
+    }
     static hipError_t launch(const Args& a, hipStream_t s) {
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
-        const bool vec = vec_ok(a);
+        const int f = fill(a);
         return with_trans(a, [&](auto ta, auto tb) {
             constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-            if (vec)
-                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, true, TA, TB>), grid, block, 0, s,
-                                   a, tm, tn, xcd_remap_enabled());
+            if (f == KG_DMA16)
+                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, KG_DMA16, TA, TB>), grid, block,
+                                   0, s, a, tm, tn, xcd_remap_enabled());
+            else if (f == KG_U16)
+                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, U16 ? KG_U16 : KG_DMA4, TA, TB>),
+                                   grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
             else
-                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, false, TA, TB>), grid, block, 0,
-                                   s, a, tm, tn, xcd_remap_enabled());
+                hipLaunchKernelGGL((k_mfma_kgroup<BM, BN, WM, WN, BK, KG_DMA4, TA, TB>), grid, block,
+                                   0, s, a, tm, tn, xcd_remap_enabled());
             return hipGetLastError();
         });
     }
-    static const void* kernel() { return (const void*)k_mfma_kgroup<BM, BN, WM, WN, BK, true>; }
+    static const void* kernel() { return (const void*)k_mfma_kgroup<BM, BN, WM, WN, BK, KG_DMA16>; }
 };
 
 // 64x128 tile, 4 groups of 4 waves of 32x64 (16 waves, 96 KB LDS).
@@ -295,7 +325,9 @@ Variant kMfmaKgroup96x64 = {"mfma_96x64_kg4", Kg96x64::check, Kg96x64::launch, K
 // 128x128 tile, 4 groups of 4 waves of 64x64 (16 waves, 128 KB LDS): one
 // tile per compute unit with four waves per SIMD, for shapes with at most
 // about one 128x128 tile per compute unit and long K.
-using Kg128x128 = KgroupInstance<128, 128, 64, 64>;
+// Its 64x64 waves leave no room for the register stage at four waves per
+// SIMD (it spills), so unaligned rows take the 4-byte fill.
+using Kg128x128 = KgroupInstance<128, 128, 64, 64, 16, false>;
 Variant kMfmaKgroup128 = {"mfma_128x128_kg4", Kg128x128::check, Kg128x128::launch,
                           Kg128x128::kernel(), Kg128x128::NT, true, nullptr, nullptr,
                           Kg128x128::kBM, Kg128x128::kBN, Kg128x128::kBK};

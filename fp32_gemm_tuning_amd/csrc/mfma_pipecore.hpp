@@ -86,9 +86,18 @@ __device__ __forceinline__ void ring_barrier() {
 // slices [s_begin, s_end) of one tile through the LDS ring, and the
 // epilogue. On return every load issued into the ring has landed and every
 // wave has passed the last barrier, so the ring may be refilled.
+//
+// U16 (with VEC false and two stages): operands whose rows are not whole
+// 16-byte chunks, filled with 16-byte loads into registers (OperandFillU).
+// The prologue loads both stages' slices at once (two register sets); in the
+// loop, the loads of slice s + 2, issued after slice s's barrier, are
+// written into the stage slice s released just before slice s + 1's
+// barrier: the same time for the loads to land as the buffer-to-LDS ring
+// gives, with a quarter of the load instructions of the 4-byte fill.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, bool VEC, bool FULL, bool TA,
-          bool TB>
+          bool TB, bool U16 = false>
 struct PipeCore {
+    static_assert(!U16 || (!VEC && !FULL && STAGES == 2), "the register fill serves a two-stage ring");
     static_assert(BK == 16 || BK == 32, "slices of 16 or 32 k");
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0,
                   "wave tiles are whole 32x32 blocks that divide the block tile");
@@ -143,10 +152,15 @@ struct PipeCore {
     // Steps s_begin .. s_end - 1; step s multiplies K slice s * KSTRIDE + koff
     // (a K-group kernel gives each group every KSTRIDE-th slice). Slices at or
     // past the end of K load as zeros.
-    template <int KSTRIDE = 1>
+    // GUARD: s_math_end is s_end or s_end - 1 (a K-group whose slices ended
+    // one step before the other groups'); the last step is then split off
+    // and its fragment reads and MFMAs, which would multiply zeros, are
+    // skipped when s_math_end < s_end.
+    template <int KSTRIDE = 1, bool GUARD = false>
     __device__ __forceinline__ void mainloop(const Args& a, int s_begin, int s_end,
                                              float* const (&Ast)[4], float* const (&Bst)[4],
-                                             f32x16 (&acc)[BI][BJ], int koff = 0) const {
+                                             f32x16 (&acc)[BI][BJ], int koff = 0,
+                                             int s_math_end = 0) const {
         // Lanes 0-31 take k = s and lanes 32-63 take k = BK/2 + s at MFMA step s
         // of the slice; part v covers steps 4v .. 4v+3, i.e. 16-byte chunk
         // P*h + v of a k-contiguous row ([row][k], swizzled: A, or B stored
@@ -204,15 +218,37 @@ struct PipeCore {
         };
 
         const Dma dma;
+        OperandFillU<BM, BK, NT, !TA> ua;
+        OperandFillU<BN, BK, NT, TB> ub;
+        if constexpr (U16) {
+            ua.init(a.lda, m0, rows_valid, t);
+            ub.init(a.ldb, n0, cols_valid, t);
+        }
+        bool pending = false;   // (U16) registers hold a slice to be written
         PartFrag<BI, BJ> f0, f1;
         // Prologue: fill every stage (stages past the last slice read zeros),
         // wait for slice 0, read its first half. Every slice below issues exactly
         // G loads per wave, whether or not its target slice exists, so the count
         // of loads issued after any given one is the same on every path.
+        if constexpr (U16) {
+            // Both prologue slices through registers, in flight together.
+            OperandFillU<BM, BK, NT, !TA> ua1 = ua;
+            OperandFillU<BN, BK, NT, TB> ub1 = ub;
+            const int k0 = (s_begin * KSTRIDE + koff) * BK, k1 = ((s_begin + 1) * KSTRIDE + koff) * BK;
+            ua.load(a.A, a.lda, m0, k0, a.K, rows_valid, t);
+            ub.load(a.B, a.ldb, n0, k0, a.K, cols_valid, t);
+            ua1.load(a.A, a.lda, m0, k1, a.K, rows_valid, t);
+            ub1.load(a.B, a.ldb, n0, k1, a.K, cols_valid, t);
+            ua.store(Ast[0], k0, t);
+            ub.store(Bst[0], k0, t);
+            ua1.store(Ast[1], k1, t);
+            ub1.store(Bst[1], k1, t);
+        } else {
 #pragma unroll
-        for (int j = 0; j < STAGES; ++j)
-            dma.template issue<FULL>(a, t, m0, n0, ((s_begin + j) * KSTRIDE + koff) * BK, rows_valid,
-                                     cols_valid, Ast[j], Bst[j]);
+            for (int j = 0; j < STAGES; ++j)
+                dma.template issue<FULL>(a, t, m0, n0, ((s_begin + j) * KSTRIDE + koff) * BK, rows_valid,
+                                         cols_valid, Ast[j], Bst[j]);
+        }
         ring_barrier<PROLOGUE_VMCNT>();
         read_part(f0, Ast[0], Bst[0], 0);
 
@@ -227,7 +263,9 @@ struct PipeCore {
         // scheduler would otherwise hoist the barrier, with its wait on the
         // reads just issued, above the MFMAs, or pull MFMAs up next to the
         // reads they depend on).
-        auto slice = [&](int s, float* Ac, float* Bc, const float* An, const float* Bn) {
+        // The MFMAs of parts 0 .. P-2 of a slice from the current stage, with
+        // the reads of parts 1 .. P-1 woven in.
+        auto parts = [&](const float* Ac, const float* Bc) {
 #pragma unroll
             for (int v = 0; v + 1 < P; ++v) {
                 if (v & 1)
@@ -241,25 +279,62 @@ struct PipeCore {
                 weave_half<0>();
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        auto slice = [&](int s, float* Ac, float* Bc, float* An, float* Bn) {
+            parts(Ac, Bc);
+            if constexpr (U16) {
+                // Slice s + 1 into the stage slice s - 1 released (An).
+                if (pending) {
+                    const int k1 = ((s + 1) * KSTRIDE + koff) * BK;
+                    ua.store(An, k1, t);
+                    ub.store(Bn, k1, t);
+                }
+            }
             ring_barrier<(STAGES - 2) * G>();
+            const int k2 = ((s + STAGES) * KSTRIDE + koff) * BK;
+            auto issue = [&]() {
+                if constexpr (U16) {
+                    ua.load(a.A, a.lda, m0, k2, a.K, rows_valid, t);
+                    ub.load(a.B, a.ldb, n0, k2, a.K, cols_valid, t);
+                    pending = true;
+                } else {
+                    dma.template issue<FULL>(a, t, m0, n0, k2, rows_valid, cols_valid, Ac, Bc);
+                }
+            };
             read_part(f0, An, Bn, 0);   // past the last slice: read and unused
             mma_part(f1);
-            dma.template issue<FULL>(a, t, m0, n0, ((s + STAGES) * KSTRIDE + koff) * BK, rows_valid,
-                                     cols_valid, Ac, Bc);
-            weave_half<2>();
+            issue();
+            weave_half<U16 ? 0 : 2>();
             __builtin_amdgcn_sched_barrier(0);
         };
-        // Whole rounds of STAGES slices, free of conditionals, then the rest.
+        // GUARD: the last step, whose slice exists only for groups with
+        // s_math_end == s_end; it loads nothing more.
+        auto last_slice = [&](int s, const float* Ac, const float* Bc) {
+            const bool cur = s < s_math_end;
+            if (cur) parts(Ac, Bc);
+            ring_barrier<(STAGES - 2) * G>();
+            if (cur) mma_part(f1);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // Whole rounds of STAGES slices, free of conditionals, then the rest
+        // (with GUARD, up to the last step, which follows on its own).
+        const int s_stop = GUARD ? s_end - 1 : s_end;
         int s0 = s_begin;
-        for (; s0 + STAGES <= s_end; s0 += STAGES) {
+        for (; s0 + STAGES <= s_stop; s0 += STAGES) {
 #pragma unroll
             for (int j = 0; j < STAGES; ++j)
                 slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
         }
 #pragma unroll
         for (int j = 0; j < STAGES - 1; ++j)
-            if (s0 + j < s_end)
+            if (s0 + j < s_stop)
                 slice(s0 + j, Ast[j], Bst[j], Ast[(j + 1) % STAGES], Bst[(j + 1) % STAGES]);
+        if constexpr (GUARD) {
+            if (s_end > s_begin) {
+                const int j = (s_end - 1 - s_begin) % STAGES;
+                last_slice(s_end - 1, Ast[j], Bst[j]);
+            }
+        }
         // The zero-filling loads issued for slices past the end must land before
         // the workgroup's LDS can be handed to another workgroup.
         ring_barrier<0>();
