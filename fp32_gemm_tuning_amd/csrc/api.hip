@@ -151,10 +151,12 @@ static double busiest_tiles(const Variant& v, int64_t M, int64_t N, int64_t K, i
 }
 
 // `trans`: an operand is stored transposed (after the column-major swap);
-// only the kernels that read transposed operands are then candidates. The
-// stream-K kernels are candidates only when they split this shape and
-// `ws_bytes` covers the workspace they need. If no entry of the model
-// applies, mfma_128x128 (which takes any shape, transposed or not) runs.
+// only the kernels that read transposed operands are then candidates. A
+// kernel whose instance for this call spills registers (Variant::auto_ok)
+// is no candidate. The stream-K kernels are candidates only when they split
+// this shape and `ws_bytes` covers the workspace they need. If no entry of
+// the model applies, mfma_128x128 (which takes any shape, transposed or not,
+// without spilling) runs.
 static int choose(const Args& a, int num_cus, size_t ws_bytes) {
     if (num_cus < 1) num_cus = 1;
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -170,6 +172,7 @@ static int choose(const Args& a, int num_cus, size_t ws_bytes) {
         const Candidate& c = m->c[i];
         const Variant& v = *kTable[c.variant];
         if (trans && !v.trans_ok) continue;
+        if (v.auto_ok != nullptr && !v.auto_ok(a)) continue;   // its instance would spill
         if (v.ws_size != nullptr && (ws_bytes == 0 || v.ws_size(a, num_cus) > ws_bytes)) continue;
         const double n = busiest_tiles(v, M, N, K, num_cus);
         if (n <= 0.0) continue;

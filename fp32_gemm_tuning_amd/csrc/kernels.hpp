@@ -33,6 +33,12 @@ struct Variant {
     // tile of one workgroup and the K slice of one pipeline step (the unit
     // of a stream-K split). 0 for the other variants.
     int bm = 0, bn = 0, bk = 0;
+    // Whether the automatic choice may launch this variant for the call:
+    // false when the kernel instance the call would take (its fill, whole
+    // tiles or not, transpositions) spills registers to scratch memory, as
+    // the compiler's resource remarks show. Null: every instance qualifies.
+    // A CPU test checks every spilling instance of the build against these.
+    bool (*auto_ok)(const Args&) = nullptr;
 };
 
 // ---------------------------------------------------------------------------
@@ -45,6 +51,8 @@ struct Variant {
 // "Distributing the Partially Filled Wave": two to four pieces; sixteen
 // lost). Workgroups left without slices by the rounding are not launched.
 // R == 0, or more slices than 32-bit indexing allows, gives no split.
+// Since G >= R, a run holds at most `slices` slices (upw <= slices), so it
+// touches at most two tiles, which the kernel relies on.
 // ---------------------------------------------------------------------------
 struct SkSplit {
     int64_t tiles = 0, slices = 0;

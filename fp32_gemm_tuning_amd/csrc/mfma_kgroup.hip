@@ -328,8 +328,11 @@ Variant kMfmaKgroup96x64 = {"mfma_96x64_kg4", Kg96x64::check, Kg96x64::launch, K
 // Its 64x64 waves leave no room for the register stage at four waves per
 // SIMD (it spills), so unaligned rows take the 4-byte fill.
 using Kg128x128 = KgroupInstance<128, 128, 64, 64, 16, false>;
+// Its 16-byte-fill instances with B transposed spill (the automatic choice
+// leaves them out).
+static bool auto_kg128(const Args& a) { return !(vec_ok(a) && a.tb); }
 Variant kMfmaKgroup128 = {"mfma_128x128_kg4", Kg128x128::check, Kg128x128::launch,
                           Kg128x128::kernel(), Kg128x128::NT, true, nullptr, nullptr,
-                          Kg128x128::kBM, Kg128x128::kBN, Kg128x128::kBK};
+                          Kg128x128::kBM, Kg128x128::kBN, Kg128x128::kBK, auto_kg128};
 
 }  // namespace sgemm

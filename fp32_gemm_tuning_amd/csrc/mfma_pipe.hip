@@ -173,19 +173,19 @@ void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
     }
     const int j = b - p.dp_tiles;
     const int U = p.sk_tiles * p.slices;
-    int u = j * p.upw;
-    const int u_end = (u + p.upw) < U ? (u + p.upw) : U;
-    while (u < u_end) {
+    const int u0 = j * p.upw;
+    const int u_end = (u0 + p.upw) < U ? (u0 + p.upw) : U;
+    // A run holds at most one tile's worth of slices (upw <= slices, see
+    // sk_split), so it touches at most two tiles: the rest of the tile it
+    // starts in, then the start of the next. Each piece is a straight-line
+    // block of its own (as a loop, the compiler kept per-lane values of one
+    // iteration live into the next and spilled them).
+    auto piece = [&](int u, int tid) {
         const int st = u / p.slices;
         const int s0 = u - st * p.slices;
         const int s1 = (s0 + (u_end - u)) < p.slices ? (s0 + (u_end - u)) : p.slices;
         tile_of_first(p.dp_tiles + st, p.dp_tiles, tiles_m, tiles_n, M128_GROUP_M,
                       xcd_remap != 0, tm, tn);
-        // The lane's fragment and epilogue offsets derive from its thread
-        // index; hidden from the compiler here, they are recomputed per run
-        // instead of being hoisted out of the loop (and spilled).
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
         const Core core(a, tm, tn, tid);
         Core::zero(acc);
         core.mainloop(a, s0, s1, Ast, Bst, acc);
@@ -193,8 +193,17 @@ void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
             core.store(a, acc);
         else
             Io::put(p.partials + (size_t)sk_slot(p, j, st) * BM * BN, core.t, acc);
-        u += s1 - s0;
-    }
+        return u + (s1 - s0);
+    };
+    if (u0 >= u_end) return;
+    const int u1 = piece(u0, threadIdx.x);
+    if (u1 >= u_end) return;
+    // The second piece's per-lane offsets derive from the thread index;
+    // hidden from the compiler here, they are recomputed rather than kept
+    // live (and spilled) across the first piece.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    piece(u1, tid);
 }
 
 // One workgroup per split tile: the sum of its pieces in K order, then the
@@ -258,8 +267,10 @@ bool vec_ok(const Args& a) {
 // target. Per call it picks the FULL form (tile grid and K slices exactly
 // cover the problem: no range masks) or the masked one, and the 16-byte or
 // 4-byte fill (vec_ok). The 4-byte-fill form keeps more loads in flight per
-// lane; it targets 3 waves per SIMD, or as many as one workgroup puts on
-// each SIMD if that is more, since it would spill at 4.
+// lane; it targets 3 waves per SIMD (at 4 it would spill), or as many as one
+// workgroup puts on each SIMD if that is more: the 256x256 tile's 16 waves
+// need 4, so its 4-byte forms spill and the automatic choice leaves them out
+// (auto_vec below).
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE>
 struct PipeInstance {
     static constexpr int NT = (BM / WM) * (BN / WN) * 64;
@@ -345,8 +356,21 @@ using Pipe128 = PipeInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK, 2,
 using Pipe64x128 =
     PipeInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK, 2, 3>;
 
+// Instances the automatic choice may launch: the spill-free ones. At four
+// waves per SIMD (128 registers) the 256x256 tile's 4-byte fills spill, and
+// so do its stream-K form's 4-byte fills and masked 16-byte fills (except
+// with only B transposed); the 64x128 stream-K kernel's 4-byte fills spill
+// when A is read untransposed.
+static bool auto_vec(const Args& a) { return vec_ok(a); }
+static bool auto_256_sk(const Args& a) {
+    const bool full = a.M % 256 == 0 && a.N % 256 == 0 && a.K % SGEMM_M256_BK == 0;
+    return vec_ok(a) && (full || (a.tb && !a.ta));
+}
+static bool auto_64x128_sk(const Args& a) { return vec_ok(a) || a.ta; }
+
 Variant kMfma256 = {"mfma_256x256", Pipe256::check, Pipe256::launch, Pipe256::kernel(),
-                    Pipe256::NT, true, nullptr, nullptr, Pipe256::kBM, Pipe256::kBN, Pipe256::kBK};
+                    Pipe256::NT, true, nullptr, nullptr, Pipe256::kBM, Pipe256::kBN, Pipe256::kBK,
+                    auto_vec};
 Variant kMfma128 = {"mfma_128x128", Pipe128::check, Pipe128::launch, Pipe128::kernel(),
                     Pipe128::NT, true, nullptr, nullptr, Pipe128::kBM, Pipe128::kBN, Pipe128::kBK};
 // 64x128: twice the tiles of mfma_128x128 for medium shapes (e.g. 3072^3,
@@ -358,12 +382,12 @@ Variant kMfma64x128 = {"mfma_64x128", Pipe64x128::check, Pipe64x128::launch,
 // Stream-K forms (they need a workspace: sgemm_f32_ws).
 Variant kMfma256Sk = {"mfma_256x256_sk", Pipe256::check, nullptr, Pipe256::sk_kernel(),
                       Pipe256::NT, true, Pipe256::ws_size, Pipe256::launch_ws,
-                      Pipe256::kBM, Pipe256::kBN, Pipe256::kBK};
+                      Pipe256::kBM, Pipe256::kBN, Pipe256::kBK, auto_256_sk};
 Variant kMfma128Sk = {"mfma_128x128_sk", Pipe128::check, nullptr, Pipe128::sk_kernel(),
                       Pipe128::NT, true, Pipe128::ws_size, Pipe128::launch_ws,
                       Pipe128::kBM, Pipe128::kBN, Pipe128::kBK};
 Variant kMfma64x128Sk = {"mfma_64x128_sk", Pipe64x128::check, nullptr, Pipe64x128::sk_kernel(),
                          Pipe64x128::NT, true, Pipe64x128::ws_size, Pipe64x128::launch_ws,
-                         Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK};
+                         Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK, auto_64x128_sk};
 
 }  // namespace sgemm

@@ -342,14 +342,21 @@ struct PipeCore {
     }
 
     __device__ __forceinline__ void store(const Args& a, const f32x16 (&acc)[BI][BJ]) const {
+        // The lane's output coordinates, recomputed from an opaque copy of
+        // the thread index: derived before the main loop, the compiler kept
+        // them live across it at four waves per SIMD and spilled them.
+        int tt = t;
+        asm volatile("" : "+v"(tt));
+        const int lane = tt & 63, w = tt >> 6;
+        const int wm_ = w / WAVES_N, wn_ = w % WAVES_N, h_ = lane >> 5, c_ = lane & 31;
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
             for (int bj = 0; bj < BJ; ++bj)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int i = wm * WM + bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int j = wn * WN + bj * 32 + c;
+                    const int i = wm_ * WM + bi * 32 + 8 * (r >> 2) + 4 * h_ + (r & 3);
+                    const int j = wn_ * WN + bj * 32 + c_;
                     if (i < rows_valid && j < cols_valid)
                         store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
                 }

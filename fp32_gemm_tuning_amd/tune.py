@@ -125,14 +125,31 @@ def predict_us(entry: dict, M: int, N: int, K: int, num_cus: int, vec: bool = Tr
             1e6 * n * 2.0 * bm * bn * K / (peak_per_cu * eff))
 
 
+def auto_ok(variant: str, M: int, N: int, K: int, vec: bool = True) -> bool:
+    """Whether the library's automatic choice may launch `variant` for a
+    packed row-major call: not when the kernel instance it would take spills
+    registers (4-byte fills of the 256x256 tile, masked or 4-byte fills of
+    its stream-K form, 4-byte fills of the 64x128 stream-K kernel)."""
+    if variant == "mfma_256x256":
+        return vec
+    if variant == "mfma_256x256_sk":
+        return vec and M % 256 == 0 and N % 256 == 0 and K % SK_BK[variant] == 0
+    if variant == "mfma_64x128_sk":
+        return vec
+    return True
+
+
 def choose(model: Sequence[dict], M: int, N: int, K: int, num_cus: int,
            workspace: bool = False, vec: bool = True) -> str:
     """The entry with the smallest prediction (earlier entries win ties);
-    stream-K entries only with a workspace and on shapes they split;
-    mfma_128x128 when no entry applies."""
+    stream-K entries only with a workspace and on shapes they split; no entry
+    whose instance for the call would spill (auto_ok); mfma_128x128 when no
+    entry applies."""
     best, best_us = None, 0.0
     for e in model:
         if e["variant"] in SK_BK and not workspace:
+            continue
+        if not auto_ok(e["variant"], M, N, K, vec):
             continue
         us = predict_us(e, M, N, K, num_cus, vec)
         if us == math.inf:

@@ -118,6 +118,29 @@ def test_sk_split_matches_the_library(tiles, slices, cus):
     assert max(pieces) <= -(-wgs // R) + 1                # about four pieces at most
 
 
+def test_sk_run_touches_at_most_two_tiles():
+    # The stream-K kernel computes a run as at most two straight-line pieces
+    # (the rest of the tile it starts in, then the start of the next), which
+    # holds because a run never has more slices than a tile (upw <= slices,
+    # as G >= R). Checked over many splits, with 256 and other unit counts.
+    import random
+    rng = random.Random(7)
+    cases = [(rng.randint(1, 5000), rng.randint(1, 600), rng.choice([80, 104, 256, 304]))
+             for _ in range(3000)]
+    cases += [(t, s, 256) for t in range(1, 600, 7) for s in (1, 2, 3, 16, 49, 100)]
+    for tiles, slices, cus in cases:
+        sp = tune.sk_split(tiles, slices, cus)
+        if sp is None:
+            continue
+        _, R, wgs, upw = sp
+        assert upw <= slices, (tiles, slices, cus, sp)
+        U = R * slices
+        for j in range(wgs):
+            u0, u1 = j * upw, min((j + 1) * upw, U)
+            assert u0 < u1
+            assert (u1 - 1) // slices - u0 // slices <= 1, (tiles, slices, cus, j)
+
+
 def test_stream_k_is_planned_only_with_a_workspace():
     # 3072^3: 576 tiles of 128x128 on 256 units -> 2 whole tiles each + 64
     # split four ways; without a workspace the stream-K kernels are no
