@@ -1,6 +1,6 @@
 // The pipelined FP32 matrix-core kernel (k_mfma_pipe, body PipeCore) and its
-// instances: mfma_256x256, mfma_128x128 and mfma_64x128, with their stream-K
-// forms (k_mfma_pipe_sk, summed by k_sk_fixup). Operand layouts and edge
+// instances: mfma_256x256, mfma_128x128, mfma_64x128 and mfma_64x64, with the
+// stream-K forms of the first three (k_mfma_pipe_sk, summed by k_sk_fixup). Operand layouts and edge
 // handling: mfma_common.hpp.
 #include "mfma_pipecore.hpp"
 
@@ -347,6 +347,17 @@ struct PipeInstance {
     }
 };
 
+// mfma_64x64 tile parameters: a 64x64 block tile of 4 waves of 32x32 (one
+// 32x32 MFMA block each), 32-deep K slices, two 16 KiB LDS stages, so five
+// workgroups share a compute unit: four times the tiles of mfma_128x128 for
+// shapes whose 128x128 grid leaves compute units idle.
+#ifndef SGEMM_M64_BK
+#define SGEMM_M64_BK 32
+#endif
+#ifndef SGEMM_M64_WPE
+#define SGEMM_M64_WPE 5
+#endif
+
 using Pipe256 = PipeInstance<SGEMM_M256_BM, SGEMM_M256_BN, SGEMM_M256_WM, SGEMM_M256_WN,
                              SGEMM_M256_BK, SGEMM_M256_STAGES, SGEMM_M256_WPE>;
 using Pipe128 = PipeInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK, 2,
@@ -355,6 +366,7 @@ using Pipe128 = PipeInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK, 2,
 // unit, so three waves per SIMD.
 using Pipe64x128 =
     PipeInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK, 2, 3>;
+using Pipe64 = PipeInstance<64, 64, 32, 32, SGEMM_M64_BK, 2, SGEMM_M64_WPE>;
 
 // Instances the automatic choice may launch: the spill-free ones. At four
 // waves per SIMD (128 registers) the 256x256 tile's 4-byte fills spill, and
@@ -379,6 +391,8 @@ Variant kMfma128 = {"mfma_128x128", Pipe128::check, Pipe128::launch, Pipe128::ke
 Variant kMfma64x128 = {"mfma_64x128", Pipe64x128::check, Pipe64x128::launch,
                        Pipe64x128::kernel(), Pipe64x128::NT, true, nullptr, nullptr,
                        Pipe64x128::kBM, Pipe64x128::kBN, Pipe64x128::kBK};
+Variant kMfma64 = {"mfma_64x64", Pipe64::check, Pipe64::launch, Pipe64::kernel(), Pipe64::NT,
+                   true, nullptr, nullptr, Pipe64::kBM, Pipe64::kBN, Pipe64::kBK};
 // Stream-K forms (they need a workspace: sgemm_f32_ws).
 Variant kMfma256Sk = {"mfma_256x256_sk", Pipe256::check, nullptr, Pipe256::sk_kernel(),
                       Pipe256::NT, true, Pipe256::ws_size, Pipe256::launch_ws,

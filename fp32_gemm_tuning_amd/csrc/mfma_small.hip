@@ -1,112 +1,10 @@
 // FP32 matrix-core kernels for shapes the tiled kernels serve badly:
-// mfma_64x64 (small tiles), mfma_64x64_k4 (in-workgroup K split),
-// mfma_direct (tiny products, no LDS) and mfma_skinny (M <= 32, HBM-bound).
+// mfma_64x64_k4 (in-workgroup K split), mfma_direct (tiny products, no LDS)
+// and mfma_skinny (M <= 32, HBM-bound).
 // Operand layouts and edge handling: mfma_common.hpp.
 #include "mfma_common.hpp"
 
 namespace sgemm {
-
-// ===========================================================================
-// mfma_64: 64x64 block tile, BK = 16, 4 waves in 2x2, each wave 32x32 = 2x2
-// blocks of 16x16 accumulated with v_mfma_f32_16x16x4_f32. Four times as many
-// tiles as mfma_128 for shapes whose 128x128 grid leaves compute units idle.
-// ===========================================================================
-constexpr int M64_BM = 64, M64_BN = 64, M64_BK = 16, M64_GROUP_M = 8;
-
-template <bool VEC>
-__global__ __launch_bounds__(256) void k_mfma64(Args a, int tiles_m, int tiles_n, int xcd_remap) {
-    constexpr int BM = M64_BM, BN = M64_BN, BK = M64_BK;
-    using Fill = TileFill<BM, BN, BK, 256, VEC>;
-    constexpr int BNP = Fill::BNP;
-    __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BK * BNP];
-
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, M64_GROUP_M, xcd_remap != 0, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int rows_valid = (a.M - m0) < BM ? (a.M - m0) : BM;
-    const int cols_valid = (a.N - n0) < BN ? (a.N - n0) : BN;
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int g = lane >> 4, c = lane & 15;
-
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    int aoff[2], boff[2];
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
-        const int row = wm * 32 + bi * 16 + c;
-        aoff[bi] = row * BK + ((g ^ swz16(row)) << 2);
-    }
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) boff[bj] = (4 * g) * BNP + wn * 32 + bj * 16 + c;
-
-    const int nslices = (a.K + BK - 1) / BK;
-    Fill fill;
-    fill.load(a, t, m0, n0, 0, rows_valid, cols_valid);
-    fill.store(As[0], Bs[0], t);
-    __syncthreads();
-
-    for (int s = 0; s < nslices; ++s) {
-        const int cur = s & 1;
-        if (s + 1 < nslices) fill.load(a, t, m0, n0, (s + 1) * BK, rows_valid, cols_valid);
-        const float* Ac = As[cur];
-        const float* Bc = Bs[cur];
-        f32x4 af[2];
-        float bf[2][4];
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi) af[bi] = *(const f32x4*)&Ac[aoff[bi]];
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) bf[bj][k] = Bc[boff[bj] + k * BNP];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[bi][k], bf[bj][k],
-                                                                       acc[bi][bj], 0, 0, 0);
-        if (s + 1 < nslices) fill.store(As[cur ^ 1], Bs[cur ^ 1], t);
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = wm * 32 + bi * 16 + 4 * g + r;
-                const int j = wn * 32 + bj * 16 + c;
-                if (i < rows_valid && j < cols_valid)
-                    store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, acc[bi][bj][r]);
-            }
-}
-
-static int check_mfma64(const Args& a) {
-    if (!extents_ok(a, M64_BM, M64_BN, M64_BK)) return SGEMM_F32_ERR_TOO_LARGE;
-    const int64_t tiles = cdiv(a.M, M64_BM) * cdiv(a.N, M64_BN);
-    return tiles <= max_workgroups(256) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
-}
-
-static hipError_t launch_mfma64(const Args& a, hipStream_t s) {
-    const int tm = (int)cdiv(a.M, M64_BM), tn = (int)cdiv(a.N, M64_BN);
-    const dim3 grid((unsigned)((int64_t)tm * tn)), block(256);
-    if (vec_ok(a))
-        hipLaunchKernelGGL(k_mfma64<true>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    else
-        hipLaunchKernelGGL(k_mfma64<false>, grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
-    return hipGetLastError();
-}
-
-Variant kMfma64 = {"mfma_64x64", check_mfma64, launch_mfma64, (const void*)k_mfma64<true>,
-                   256, false, nullptr, nullptr, M64_BM, M64_BN, M64_BK};
 
 // ===========================================================================
 // mfma_64x64_k4: a 64x64 tile whose 4 waves split every 64-deep K slice four

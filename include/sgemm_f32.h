@@ -114,8 +114,9 @@ enum sgemm_f32_variant_id {
        stages filled by buffer-to-LDS loads, software-pipelined as
        MFMA_256 */
     SGEMM_F32_MFMA_128 = 7,
-    /* FP32 matrix-core kernel, 64x64 block tile for shapes with few 128x128
-       tiles (v_mfma_f32_16x16x4_f32) */
+    /* FP32 matrix-core kernel, 64x64 block tile of 4 waves of 32x32
+       (v_mfma_f32_32x32x2_f32), 32-deep K slices, pipelined as MFMA_256,
+       five workgroups per compute unit: for shapes with few 128x128 tiles */
     SGEMM_F32_MFMA_64 = 8,
     /* FP32 matrix-core kernel for M <= a few tens of rows (near-GEMV): 16-row
        tiles, the K loop split across the waves of a workgroup */
@@ -330,9 +331,8 @@ SGEMM_F32_API int sgemm_f32_ws_size(int variant, int layout, int transa, int tra
                                     int64_t N, int64_t K, int num_cus, size_t *bytes);
 
 /* 1 if `variant` reads transposed operands (mfma_128x128, mfma_256x256,
- * mfma_64x128, the three K-group kernels and the stream-K kernels), 0 if
- * not, or
- * SGEMM_F32_ERR_VARIANT. */
+ * mfma_64x128, mfma_64x64, the K-group kernels, the stream-K kernels,
+ * mfma_skinny and mfma_direct), 0 if not, or SGEMM_F32_ERR_VARIANT. */
 SGEMM_F32_API int sgemm_f32_variant_trans_ok(int variant);
 
 /* Geometry of a matrix-core tile kernel, the variants the dispatch model

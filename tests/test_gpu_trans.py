@@ -25,7 +25,7 @@ NT, T = sg.NO_TRANS, sg.TRANS
 COMBOS = list(itertools.product((ROW, COL), (NT, T), (NT, T)))
 TRANS_KERNELS = ["mfma_128x128", "mfma_256x256", "mfma_64x128", "mfma_64x128_kg4",
                  "mfma_64x96_kg4", "mfma_96x64_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
-                 "mfma_256x256_sk", "mfma_skinny", "mfma_direct"]
+                 "mfma_256x256_sk", "mfma_64x64", "mfma_skinny", "mfma_direct"]
 
 
 def combo_id(c):

@@ -15,7 +15,7 @@ ROW, COL = sg.ROW_MAJOR, sg.COL_MAJOR
 NT, T = sg.NO_TRANS, sg.TRANS
 TRANS_KERNELS = {"mfma_128x128", "mfma_256x256", "mfma_64x128", "mfma_64x128_kg4",
                  "mfma_64x96_kg4", "mfma_96x64_kg4", "mfma_128x128_kg4", "mfma_128x128_sk", "mfma_64x128_sk",
-                 "mfma_256x256_sk", "mfma_skinny", "mfma_direct"}
+                 "mfma_256x256_sk", "mfma_64x64", "mfma_skinny", "mfma_direct"}
 
 
 def min_lds(layout, ta, tb, M, N, K):
@@ -165,15 +165,19 @@ def test_kernels_without_transposed_reads_refuse(name):
                                    stream=0) == sg.ERR_UNSUPPORTED
 
 
-def test_transposed_plan_with_a_model_that_has_no_transposed_kernel():
+def test_transposed_plan_with_a_model_that_has_no_candidate():
+    # Every model kernel reads transposed operands; a call that the model's
+    # only entry cannot take (here mfma_256x256 with 4-byte fills, an instance
+    # that spills) falls back to mfma_128x128, transposed or not.
     try:
-        assert sg.sgemm_f32_set_model([{"variant": "mfma_64x64", "overhead_us": 1.0,
+        assert sg.sgemm_f32_set_model([{"variant": "mfma_256x256", "overhead_us": 1.0,
                                         "eff": [0.5, 0.5, 0.5, 0.5]}]) == 0
-        rc, v = sg.sgemm_f32_plan_ex(ROW, T, NT, 512, 512, 512, 1.0, P, 512, P, 512, 0.0, P, 512,
+        rc, v = sg.sgemm_f32_plan_ex(ROW, T, NT, 512, 512, 513, 1.0, P, 513, P, 512, 0.0, P, 512,
                                      256)
         assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_128x128"
-        rc, v = sg.sgemm_f32_plan(512, 512, 512, 1.0, P, 512, P, 512, 0.0, P, 512, 256)
-        assert sg.sgemm_f32_variant_name(v) == "mfma_64x64"
+        rc, v = sg.sgemm_f32_plan_ex(ROW, T, NT, 512, 512, 512, 1.0, P, 512, P, 512, 0.0, P, 512,
+                                     256)
+        assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_256x256"
     finally:
         assert sg.sgemm_f32_set_model([]) == 0
 
