@@ -111,11 +111,11 @@ __device__ __forceinline__ int sk_slot(const SkPlan& p, int jj, int st) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
-          bool TA = false, bool TB = false>
+          bool TA = false, bool TB = false, bool U16 = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
-    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB>;
+    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB, U16>;
     // One LDS object per stage, so that the compiler can tell the stage being
     // filled from the stages being read (unused stages are dropped).
     __shared__ __attribute__((aligned(16))) float As0[Core::LDS_A];
@@ -265,13 +265,18 @@ bool vec_ok(const Args& a) {
 // An instance of the pipelined kernel (k_mfma_pipe, and k_mfma_pipe_sk for
 // stream-K): block tile, wave tile, K slice, LDS stages and occupancy
 // target. Per call it picks the FULL form (tile grid and K slices exactly
-// cover the problem: no range masks) or the masked one, and the 16-byte or
-// 4-byte fill (vec_ok). The 4-byte-fill form keeps more loads in flight per
+// cover the problem: no range masks) or the masked one, and the fill: 16-byte
+// buffer-to-LDS loads when every operand row is whole 16-byte chunks
+// (vec_ok); else, with U16OK and extents that allow it (fillu_ok), 16-byte
+// loads through registers (the whole-tile kernel only); else 4-byte
+// buffer-to-LDS loads. The 4-byte-fill form keeps more loads in flight per
 // lane; it targets 3 waves per SIMD (at 4 it would spill), or as many as one
 // workgroup puts on each SIMD if that is more: the 256x256 tile's 16 waves
 // need 4, so its 4-byte forms spill and the automatic choice leaves them out
-// (auto_vec below).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE>
+// (auto_vec below); it has no registers to spare for U16 either. U16_TB:
+// U16 also when B is stored transposed (the 128x128 tile spills there).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool U16OK = false,
+          bool U16_TB = true>
 struct PipeInstance {
     static constexpr int NT = (BM / WM) * (BN / WN) * 64;
     static constexpr int kBM = BM, kBN = BN, kBK = BK;
@@ -288,26 +293,31 @@ struct PipeInstance {
         const int64_t tiles = cdiv(a.M, BM) * cdiv(a.N, BN);
         return tiles <= max_workgroups(NT) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
     }
-    // f(VEC, FULL, TA, TB), each a std::integral_constant<bool>.
+    // f(VEC, FULL, TA, TB, U16), each a std::integral_constant<bool>; U16 only
+    // with `u16`.
     template <class F>
-    static hipError_t forms(const Args& a, F&& f) {
+    static hipError_t forms(const Args& a, bool u16, F&& f) {
         using T = std::true_type;
         using N = std::false_type;
         const bool vec = vec_ok(a);
         const bool full = a.M % BM == 0 && a.N % BN == 0 && a.K % BK == 0;
+        const bool reg = U16OK && u16 && !vec && fillu_ok(a, BM, BN, BK);
         return with_trans(a, [&](auto ta, auto tb) {
-            if (vec && full) return f(T{}, T{}, ta, tb);
-            if (vec) return f(T{}, N{}, ta, tb);
-            return f(N{}, N{}, ta, tb);
+            if (vec && full) return f(T{}, T{}, ta, tb, N{});
+            if (vec) return f(T{}, N{}, ta, tb, N{});
+            if constexpr (U16OK && (U16_TB || !decltype(tb)::value))
+                if (reg) return f(N{}, N{}, ta, tb, T{});
+            return f(N{}, N{}, ta, tb, N{});
         });
     }
     static hipError_t launch(const Args& a, hipStream_t s) {
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)((int64_t)tm * tn)), block(NT);
-        return forms(a, [&](auto vec, auto full, auto ta, auto tb) {
+        return forms(a, true, [&](auto vec, auto full, auto ta, auto tb, auto u16) {
             constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
-            hipLaunchKernelGGL((k_mfma_pipe<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
-                                            decltype(ta)::value, decltype(tb)::value>),
+            constexpr bool U = decltype(u16)::value;
+            hipLaunchKernelGGL((k_mfma_pipe<BM, BN, WM, WN, BK, STAGES, (V || U) ? WPE : WPE4, V, F,
+                                            decltype(ta)::value, decltype(tb)::value, U>),
                                grid, block, 0, s, a, tm, tn, xcd_remap_enabled());
             return hipGetLastError();
         });
@@ -332,7 +342,7 @@ struct PipeInstance {
         p.partials = (float*)ws;
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(NT);
-        const hipError_t e = forms(a, [&](auto vec, auto full, auto ta, auto tb) {
+        const hipError_t e = forms(a, false, [&](auto vec, auto full, auto ta, auto tb, auto) {
             constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
             hipLaunchKernelGGL((k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
                                                decltype(ta)::value, decltype(tb)::value>),
@@ -361,12 +371,12 @@ struct PipeInstance {
 using Pipe256 = PipeInstance<SGEMM_M256_BM, SGEMM_M256_BN, SGEMM_M256_WM, SGEMM_M256_WN,
                              SGEMM_M256_BK, SGEMM_M256_STAGES, SGEMM_M256_WPE>;
 using Pipe128 = PipeInstance<M128_BM, M128_BN, M128_WM, M128_WN, M128_BK, 2,
-                             SGEMM_M128_WAVES_PER_EU>;
+                             SGEMM_M128_WAVES_PER_EU, true, false>;
 // Two 24 KiB LDS stages per 4-wave workgroup: three workgroups per compute
 // unit, so three waves per SIMD.
 using Pipe64x128 =
-    PipeInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK, 2, 3>;
-using Pipe64 = PipeInstance<64, 64, 32, 32, SGEMM_M64_BK, 2, SGEMM_M64_WPE>;
+    PipeInstance<64, 128, SGEMM_M64x128_WM, SGEMM_M64x128_WN, SGEMM_M64x128_BK, 2, 3, true>;
+using Pipe64 = PipeInstance<64, 64, 32, 32, SGEMM_M64_BK, 2, SGEMM_M64_WPE, true>;
 
 // Instances the automatic choice may launch: the spill-free ones. At four
 // waves per SIMD (128 registers) the 256x256 tile's 4-byte fills spill, and

@@ -240,6 +240,38 @@ def test_large_tiles_on_odd_shape(dev, variant, integer):
     assert rep.ok, f"{variant}: {rep}"
 
 
+# Register-staged 16-byte fills (rows that are not whole 16-byte chunks): K
+# tails ending 1-3 elements into a chunk (the lanes shift the chunk's last
+# valid elements down and zero the rest), edge tiles with 1-3 valid columns,
+# misaligned base pointers and padded leading dimensions (NaN padding, never
+# read). (M, N, K, pads, offsets)
+U16_CASES = [
+    (129, 131, 7, (1, 0, 0), (0, 0, 0)),
+    (70, 250, 5, (0, 3, 0), (0, 0, 0)),
+    (130, 129, 35, (1, 0, 2), (0, 0, 0)),
+    (200, 385, 67, (0, 0, 0), (1, 0, 0)),
+    (97, 193, 33, (2, 1, 0), (0, 2, 1)),
+    (300, 261, 250, (3, 0, 0), (0, 0, 0)),
+]
+U16_VARIANTS = ["mfma_128x128", "mfma_64x128", "mfma_64x64", "mfma_64x128_kg4", "mfma_64x96_kg4",
+                "mfma_96x64_kg4"]
+
+
+@pytest.mark.parametrize("dist", ["integer", "uniform"])
+@pytest.mark.parametrize("variant", U16_VARIANTS)
+@pytest.mark.parametrize("case", U16_CASES, ids=lambda c: "x".join(map(str, c[:3])))
+def test_register_fill_edges(dev, variant, case, dist):
+    M, N, K, pads, offsets = case
+    A, B, C0 = inputs(M, N, K, dist, 3000 + M + K, 0.5, pads)
+    v = sg.sgemm_f32_variant_by_name(variant)
+    rc, C = run(v, M, N, K, 1.0, 0.5, A, B, C0, dev, offsets, tag="u16")
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    rep = check_full(C, A, B, C0, M, N, K, 1.0, 0.5, exact=(dist == "integer"))
+    assert rep.ok, f"{variant} {case}: {rep}"
+    if pads[2]:
+        assert np.array_equal(C[:, N:], C0[:, N:], equal_nan=True)
+
+
 @pytest.mark.parametrize("kind", [0, 1, 2])
 def test_peak_probe_runs(dev, kind):
     out = torch.zeros(256 * 256, dtype=torch.float32, device=dev)

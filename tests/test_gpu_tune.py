@@ -41,7 +41,8 @@ def test_tune_fit_install_and_run(dev):
     A, B, C0 = make_inputs(w)
     _, v = sg.sgemm_f32_plan(w.M, w.N, w.K, w.alpha, 0x1000, w.K, 0x1000, w.N, w.beta, 0x1000,
                              w.N, cus)
-    assert sg.sgemm_f32_variant_name(v) == tune.choose(model, w.M, w.N, w.K, cus)
+    assert sg.sgemm_f32_variant_name(v) == tune.choose(model, w.M, w.N, w.K, cus,
+                                                       vec=tune.packed_vec(w.M, w.N, w.K))
     dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
     dC = torch.from_numpy(C0).to(dev)
     print(f"[gpu] R_odd under tuned model with {sg.sgemm_f32_variant_name(v)}", flush=True)

@@ -26,7 +26,8 @@ CUS = 256
 WS = 1 << 40
 P = 1 << 20       # fake, 16-byte aligned device address (plans read no memory)
 
-PIPE = {(256, 256): "mfma_256x256", (128, 128): "mfma_128x128", (64, 128): "mfma_64x128"}
+PIPE = {(256, 256): "mfma_256x256", (128, 128): "mfma_128x128", (64, 128): "mfma_64x128",
+        (64, 64): "mfma_64x64"}
 KGROUP = {(64, 128): "mfma_64x128_kg4", (64, 96): "mfma_64x96_kg4", (96, 64): "mfma_96x64_kg4",
           (128, 128): "mfma_128x128_kg4"}
 
@@ -55,12 +56,14 @@ def parse(name):
     """(variant, form) of a model kernel instance, else None. form: dict with
     fill ('vec', 'u16', 'dma4'), full (bool), ta, tb."""
     m = re.match(r"void sgemm::k_mfma_pipe(_sk)?<(\d+), (\d+), \d+, \d+, (\d+), \d+, \d+, "
-                 r"(true|false), (true|false), (true|false), (true|false)>", name)
+                 r"(true|false), (true|false), (true|false), (true|false)(, (true|false))?>", name)
     if m:
         sk, bm, bn, bk = m.group(1), int(m.group(2)), int(m.group(3)), int(m.group(4))
         vec, full, ta, tb = (m.group(i) == "true" for i in range(5, 9))
+        u16 = m.group(10) == "true"
         v = PIPE[(bm, bn)] + ("_sk" if sk else "")
-        return v, dict(fill="vec" if vec else "dma4", full=full, ta=ta, tb=tb, bm=bm, bn=bn, bk=bk)
+        fill = "vec" if vec else "u16" if u16 else "dma4"
+        return v, dict(fill=fill, full=full, ta=ta, tb=tb, bm=bm, bn=bn, bk=bk)
     m = re.match(r"void sgemm::k_mfma_kgroup<(\d+), (\d+), \d+, \d+, (\d+), (\d), "
                  r"(true|false), (true|false)>", name)
     if m:
@@ -80,9 +83,11 @@ def call_for(variant, form):
     tm, tn = (16, 19) if variant.endswith("_sk") else (16, 16)
     M, N = tm * bm, tn * bn
     K = 64 * bk
-    if form["fill"] == "dma4" and variant in KGROUP.values():
+    if form["fill"] == "dma4":
         K = 3                       # a contiguous extent below 4: no 16-byte fill at all
         M, N = 64 * bm, 64 * bn     # keeps the product out of the tiny-shape path
+        if variant.endswith("_sk"):
+            N += bn                 # 64 x 65 tiles: not a multiple of the units
     if not form["full"] and variant in PIPE.values() or variant.endswith("_sk") and not form["full"]:
         M += 4                      # a partial tile row (keeps every extent a multiple of 4)
     # stored extents: A is M x K (K x M if ta), B is K x N (N x K if tb)
@@ -134,6 +139,8 @@ def test_no_spilling_instance_is_chosen_automatically():
     ("mfma_128x128_sk", dict(fill="vec", full=False, ta=False, tb=False)),
     ("mfma_64x96_kg4", dict(fill="u16", full=False, ta=False, tb=False)),
     ("mfma_128x128_kg4", dict(fill="vec", full=False, ta=True, tb=False)),
+    ("mfma_128x128", dict(fill="u16", full=False, ta=False, tb=False)),
+    ("mfma_64x64", dict(fill="u16", full=False, ta=True, tb=True)),
 ])
 def test_spill_free_forms_are_still_chosen(variant, form):
     bm, bn, bk = sg.sgemm_f32_variant_tile(sg.sgemm_f32_variant_by_name(variant))[1:]
