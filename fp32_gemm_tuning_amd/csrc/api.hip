@@ -67,15 +67,16 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // the prediction is a fixed cost (launch, first fill, epilogue) plus that
 // unit's n * 2*BM*BN*K FLOP at a fraction of its peak that depends on n
 // (few tiles per unit leave the matrix cores waiting on fills and barriers),
-// times a per-kernel factor when the operands need 4-byte fills, plus a
-// fixed cost per tile on that unit (a tile's first fill and epilogue). All
-// four were fitted per kernel to interleaved timings of every candidate on
-// 30 shapes from 512^3 to 8192^3, square, flat, tall and odd, on MI355X
-// (fp32_gemm_tuning_amd/tune.py); mfma_96x64_kg4's row comes from a later
-// fit of the same kind. On a later, independent timing of the 30 shapes the
-// model picks the fastest whole-tile kernel on 26 of them without a
-// workspace and the fastest of all on 22 with one, in both cases one within
-// 5% on the rest (0.3% and 0.5% lost on average).
+// times a per-kernel factor when the operand rows are not whole 16-byte
+// chunks (register-staged or 4-byte fills), plus a fixed cost per tile on
+// that unit (a tile's first fill and epilogue). All four were fitted per
+// kernel to interleaved timings of every candidate on 30 shapes from 512^3
+// to 8192^3, square, flat, tall and odd, on MI355X
+// (fp32_gemm_tuning_amd/tune.py): in sample the model picks the fastest
+// kernel on 27 of them (worst 2.3% lost). On 24 random shapes it was not
+// fitted to (sides log-uniform in [300, 6000]) it picks the fastest
+// whole-tile kernel on 18 without a workspace and the fastest of all on 20
+// with one, losing 0.5% and 0.6% on average (worst 4.5% and 8.6%).
 // ---------------------------------------------------------------------------
 struct Candidate {
     int variant;
@@ -109,17 +110,17 @@ struct Model {
 // Built-in model, listed in order of preference when predictions tie.
 static const Model kDefaultModel = {11,
                                     {
-                                        {SGEMM_F32_MFMA_128, 0.0, {0.903, 0.919, 0.952, 0.920}, 0.84, 6.0},
-                                        {SGEMM_F32_MFMA_256, 0.0, {0.996, 0.953, 0.962, 0.962}, 0.86, 12.0},
-                                        {SGEMM_F32_MFMA_64x128, 0.5, {0.754, 0.866, 0.884, 0.909}, 0.70, 3.0},
-                                        {SGEMM_F32_MFMA_64, 3.5, {0.450, 0.627, 0.682, 0.785}, 0.86, 1.0},
-                                        {SGEMM_F32_MFMA_64x128_KG4, 0.5, {0.786, 0.817, 0.833, 0.861}, 0.82, 5.5},
-                                        {SGEMM_F32_MFMA_64x96_KG4, 3.0, {0.742, 0.771, 0.771, 0.806}, 0.84, 5.0},
-                                        {SGEMM_F32_MFMA_96x64_KG4, 1.0, {0.730, 0.788, 0.811, 0.815}, 0.82, 5.5},
-                                        {SGEMM_F32_MFMA_128x128_KG4, 0.0, {0.911, 0.908, 0.941, 0.916}, 0.84, 10.5},
-                                        {SGEMM_F32_MFMA_128_SK, 11.5, {0.801, 0.941, 0.959, 0.907}, 0.80, 4.5},
-                                        {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.713, 0.869, 1.000, 0.903}, 0.70, 2.5},
-                                        {SGEMM_F32_MFMA_256_SK, 9.5, {0.919, 0.917, 0.970, 0.970}, 0.78, 20.0},
+                                        {SGEMM_F32_MFMA_128, 0.0, {0.919, 0.949, 0.970, 0.967}, 0.88, 6.5},
+                                        {SGEMM_F32_MFMA_256, 0.0, {0.993, 0.959, 0.976, 0.976}, 0.86, 13.0},
+                                        {SGEMM_F32_MFMA_64x128, 0.5, {0.748, 0.838, 0.905, 0.922}, 0.78, 3.0},
+                                        {SGEMM_F32_MFMA_64, 2.5, {0.703, 0.801, 0.822, 0.909}, 0.82, 1.5},
+                                        {SGEMM_F32_MFMA_64x128_KG4, 1.5, {0.774, 0.784, 0.828, 0.861}, 0.96, 5.5},
+                                        {SGEMM_F32_MFMA_64x96_KG4, 4.0, {0.748, 0.770, 0.756, 0.799}, 0.90, 4.5},
+                                        {SGEMM_F32_MFMA_96x64_KG4, 3.5, {0.762, 0.785, 0.770, 0.814}, 0.94, 5.0},
+                                        {SGEMM_F32_MFMA_128x128_KG4, 0.5, {0.910, 0.922, 0.943, 0.934}, 0.84, 10.0},
+                                        {SGEMM_F32_MFMA_128_SK, 11.5, {0.794, 0.983, 0.967, 0.925}, 0.88, 4.5},
+                                        {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.720, 0.844, 1.000, 0.917}, 0.78, 2.5},
+                                        {SGEMM_F32_MFMA_256_SK, 10.0, {0.961, 0.937, 0.977, 0.977}, 0.80, 20.0},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a

@@ -143,11 +143,11 @@ void k_mfma_pipe(Args a, int tiles_m, int tiles_n, int xcd_remap) {
 // covering a whole tile writing C, the others their partial tiles (summed by
 // k_sk_fixup).
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int WPE, bool VEC, bool FULL,
-          bool TA = false, bool TB = false>
+          bool TA = false, bool TB = false, bool U16 = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void k_mfma_pipe_sk(Args a, int tiles_m, int tiles_n, int xcd_remap, SkPlan p) {
-    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB>;
+    using Core = PipeCore<BM, BN, WM, WN, BK, STAGES, VEC, FULL, TA, TB, U16>;
     using Io = PartialIo<Core::BI, Core::BJ, Core::NT>;
     __shared__ __attribute__((aligned(16))) float As0[Core::LDS_A];
     __shared__ __attribute__((aligned(16))) float Bs0[Core::LDS_B];
@@ -268,8 +268,7 @@ bool vec_ok(const Args& a) {
 // cover the problem: no range masks) or the masked one, and the fill: 16-byte
 // buffer-to-LDS loads when every operand row is whole 16-byte chunks
 // (vec_ok); else, with U16OK and extents that allow it (fillu_ok), 16-byte
-// loads through registers (the whole-tile kernel only); else 4-byte
-// buffer-to-LDS loads. The 4-byte-fill form keeps more loads in flight per
+// loads through registers; else 4-byte buffer-to-LDS loads. The 4-byte-fill form keeps more loads in flight per
 // lane; it targets 3 waves per SIMD (at 4 it would spill), or as many as one
 // workgroup puts on each SIMD if that is more: the 256x256 tile's 16 waves
 // need 4, so its 4-byte forms spill and the automatic choice leaves them out
@@ -342,10 +341,11 @@ struct PipeInstance {
         p.partials = (float*)ws;
         const int tm = (int)cdiv(a.M, BM), tn = (int)cdiv(a.N, BN);
         const dim3 grid((unsigned)(p.dp_tiles + p.sk_wgs)), block(NT);
-        const hipError_t e = forms(a, false, [&](auto vec, auto full, auto ta, auto tb, auto) {
+        const hipError_t e = forms(a, true, [&](auto vec, auto full, auto ta, auto tb, auto u16) {
             constexpr bool V = decltype(vec)::value, F = decltype(full)::value;
-            hipLaunchKernelGGL((k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, V ? WPE : WPE4, V, F,
-                                               decltype(ta)::value, decltype(tb)::value>),
+            constexpr bool U = decltype(u16)::value;
+            hipLaunchKernelGGL((k_mfma_pipe_sk<BM, BN, WM, WN, BK, STAGES, (V || U) ? WPE : WPE4, V,
+                                               F, decltype(ta)::value, decltype(tb)::value, U>),
                                grid, block, 0, s, a, tm, tn, xcd_remap_enabled(), p);
             return hipGetLastError();
         });
@@ -381,14 +381,15 @@ using Pipe64 = PipeInstance<64, 64, 32, 32, SGEMM_M64_BK, 2, SGEMM_M64_WPE, true
 // Instances the automatic choice may launch: the spill-free ones. At four
 // waves per SIMD (128 registers) the 256x256 tile's 4-byte fills spill, and
 // so do its stream-K form's 4-byte fills and masked 16-byte fills (except
-// with only B transposed); the 64x128 stream-K kernel's 4-byte fills spill
-// when A is read untransposed.
+// with only B transposed); the 64x128 stream-K kernel's 4-byte fills (taken
+// only when the register-staged fill cannot run) spill when A is read
+// untransposed.
 static bool auto_vec(const Args& a) { return vec_ok(a); }
 static bool auto_256_sk(const Args& a) {
     const bool full = a.M % 256 == 0 && a.N % 256 == 0 && a.K % SGEMM_M256_BK == 0;
     return vec_ok(a) && (full || (a.tb && !a.ta));
 }
-static bool auto_64x128_sk(const Args& a) { return vec_ok(a) || a.ta; }
+static bool auto_64x128_sk(const Args& a) { return vec_ok(a) || fillu_ok(a, 64, 128, 32) || a.ta; }
 
 Variant kMfma256 = {"mfma_256x256", Pipe256::check, Pipe256::launch, Pipe256::kernel(),
                     Pipe256::NT, true, nullptr, nullptr, Pipe256::kBM, Pipe256::kBN, Pipe256::kBK,

@@ -129,13 +129,17 @@ def auto_ok(variant: str, M: int, N: int, K: int, vec: bool = True) -> bool:
     """Whether the library's automatic choice may launch `variant` for a
     packed row-major call: not when the kernel instance it would take spills
     registers (4-byte fills of the 256x256 tile, masked or 4-byte fills of
-    its stream-K form, 4-byte fills of the 64x128 stream-K kernel)."""
+    its stream-K form, 4-byte fills of the 64x128 stream-K kernel, which it
+    takes only when the register-staged 16-byte fill cannot run: a
+    contiguous extent below 4 or offsets past 2^31 bytes)."""
     if variant == "mfma_256x256":
         return vec
     if variant == "mfma_256x256_sk":
         return vec and M % 256 == 0 and N % 256 == 0 and K % SK_BK[variant] == 0
     if variant == "mfma_64x128_sk":
-        return vec
+        fillu = (K >= 4 and N >= 4 and (63 * K + K) * 4 < 2**31
+                 and (31 * N + N) * 4 < 2**31)
+        return vec or fillu
     return True
 
 
