@@ -405,6 +405,11 @@ def regimes(args, dev) -> int:
                "roofline_bound": "fp32" if roof >= FP32_PEAK_TFLOPS else "hbm(measured copy)"}
         for tag, fn in (("warm", call), ("cold", call_cold)) if cold else (("warm", call),):
             smi0 = smi_snapshot()
+            # The snapshot leaves the GPU idle for about a second; after such a
+            # gap the first tens of milliseconds of calls run slower, so warm
+            # up by time (untimed) before the timed calls.
+            fn()
+            clock_warmup(fn, 0.3)
             durs, _ = time_calls(fn, args.steps, args.warmup, stream)
             n_b2b = B2B_CALLS.get(wname, args.steps)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
