@@ -44,11 +44,11 @@ FP32_PEAK_TFLOPS = 157.3        # MI355X dense FP32 matrix peak (one 32x32x2 MFM
 FP32_VALU_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["fp32_gemm_tuning_amd/csrc/mfma_pipe.hip", "fp32_gemm_tuning_amd/csrc/mfma_kgroup.hip",
-                  "fp32_gemm_tuning_amd/csrc/mfma_small.hip", "fp32_gemm_tuning_amd/csrc/mfma_common.hpp",
-                  "fp32_gemm_tuning_amd/csrc/mfma_pipecore.hpp",
-                  "fp32_gemm_tuning_amd/csrc/valu_main.hip",
-                  "fp32_gemm_tuning_amd/csrc/common.hpp", "fp32_gemm_tuning_amd/csrc/ladder.hip"]
+# The files the traffic-measured kernel (the tiled matrix-core kernels of mfma_pipe.hip) is
+# compiled from, with the build flags: a change to any of them voids the stored traffic.
+KERNEL_SOURCES = ["fp32_gemm_tuning_amd/csrc/mfma_pipe.hip", "fp32_gemm_tuning_amd/csrc/mfma_pipecore.hpp",
+                  "fp32_gemm_tuning_amd/csrc/mfma_common.hpp", "fp32_gemm_tuning_amd/csrc/common.hpp",
+                  "fp32_gemm_tuning_amd/csrc/kernels.hpp", "fp32_gemm_tuning_amd/build.py"]
 
 
 def kernel_source_sha() -> str:

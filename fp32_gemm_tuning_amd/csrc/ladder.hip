@@ -184,55 +184,75 @@ static hipError_t launch_reg1d(const Args& a, hipStream_t s) {
 Variant kReg1d = {"reg1d", check_reg1d, launch_reg1d, (const void*)k_reg1d, 512};
 
 // ---------------------------------------------------------------------------
-// reg2d: 128x128 block tile, 8-deep slices, 256 lanes in a 16x16 grid; lane
-// (ty, tx) owns the 8x8 patch rows 8*ty.., columns 8*tx..; per k it loads 8 A
-// and 8 B values and does their 64-FMA outer product.
+// Shared by reg2d and vec4_transa: a 128x128 block of C cut into 256 patches
+// of 8x8, one per lane (lane l: patch row l / 16, patch column l % 16), held
+// in registers while 8-deep slices of A and B pass through LDS.
+// ---------------------------------------------------------------------------
+struct Patch {
+    float v[8][8];
+    __device__ void clear() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+    // One k step: the 8 A values of the patch's rows times the 8 B values of
+    // its columns, 64 FMAs.
+    __device__ void rank1(const float (&from_a)[8], const float (&from_b)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[i][j] += from_a[i] * from_b[j];
+    }
+    // Epilogue for the patch whose first output is (row0, col0); outputs
+    // past the matrix edges are skipped.
+    __device__ void store(const Args& a, int64_t row0, int64_t col0) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (row0 + i < a.M && col0 + j < a.N) store_out(a, row0 + i, col0 + j, v[i][j]);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// reg2d: A's slice kept as it is stored (128 rows x 8 k), B's as 8 k x 128
+// columns; the 1024 elements of each slice are loaded four per lane with
+// 4-byte loads, element e of a slice at (e / width, e % width).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_reg2d(Args a) {
-    __shared__ float As[128][8];
-    __shared__ float Bs[8][128];
-    const int tiles_n = (a.N + 127) / 128;
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * 128;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * 128;
-    const int t = threadIdx.x;
-    const int ty = t >> 4, tx = t & 15;
-    float acc[8][8];
+    __shared__ float slice_a[128][8];
+    __shared__ float slice_b[8][128];
+    const int cols_of_blocks = (a.N + 127) / 128;
+    const int64_t bm = (int64_t)(blockIdx.x / cols_of_blocks) * 128;
+    const int64_t bn = (int64_t)(blockIdx.x % cols_of_blocks) * 128;
+    const int lane = threadIdx.x;
+    const int pm = (lane >> 4) * 8, pn = (lane & 15) * 8;   // patch origin in the block
+    Patch acc;
+    acc.clear();
+    for (int64_t k0 = 0; k0 < a.K; k0 += 8) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] = 0.0f;
-    for (int k0 = 0; k0 < a.K; k0 += 8) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int e = t + 256 * p;
-            const int ar = e >> 3, ac = e & 7;
-            As[ar][ac] = (m0 + ar < a.M && k0 + ac < a.K) ? a.A[(m0 + ar) * a.lda + k0 + ac] : 0.0f;
-            const int br = e >> 7, bc = e & 127;
-            Bs[br][bc] = (k0 + br < a.K && n0 + bc < a.N)
-                             ? a.B[(int64_t)(k0 + br) * a.ldb + n0 + bc] : 0.0f;
+        for (int q = 0; q < 4; ++q) {
+            const int e = q * 256 + lane;
+            const int64_t am = bm + e / 8, ak = k0 + e % 8;
+            slice_a[e / 8][e % 8] = (am < a.M && ak < a.K) ? a.A[am * a.lda + ak] : 0.0f;
+            const int64_t bk = k0 + e / 128, bnn = bn + e % 128;
+            slice_b[e / 128][e % 128] = (bk < a.K && bnn < a.N) ? a.B[bk * a.ldb + bnn] : 0.0f;
         }
         __syncthreads();
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            float rm[8], rn[8];
+        for (int kk = 0; kk < 8; ++kk) {
+            float from_a[8], from_b[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) rm[r] = As[ty * 8 + r][d];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) rn[c] = Bs[d][tx * 8 + c];
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[r][c] += rm[r] * rn[c];
+            for (int u = 0; u < 8; ++u) {
+                from_a[u] = slice_a[pm + u][kk];
+                from_b[u] = slice_b[kk][pn + u];
+            }
+            acc.rank1(from_a, from_b);
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int64_t i = m0 + ty * 8 + r, j = n0 + tx * 8 + c;
-            if (i < a.M && j < a.N) store_out(a, i, j, acc[r][c]);
-        }
+    acc.store(a, bm + pm, bn + pn);
 }
 
 static int check_reg2d(const Args& a) { return check_grid(cdiv(a.M, 128) * cdiv(a.N, 128), 256); }
@@ -244,65 +264,57 @@ static hipError_t launch_reg2d(const Args& a, hipStream_t s) {
 Variant kReg2d = {"reg2d", check_reg2d, launch_reg2d, (const void*)k_reg2d, 256};
 
 // ---------------------------------------------------------------------------
-// vec4_transa: reg2d with 16-byte global loads. A's slice is stored
-// transposed (As[k][m]) so a lane's 8 A values are adjacent and read with two
-// 16-byte LDS loads; the fill scatters each 16-byte load's four floats down a
-// column of As. With two lanes per A row those scattered stores of a pair of
-// lanes land 4 rows (512 floats) apart, i.e. in the same bank: the two-way
-// store conflict the pages derive, kept here on purpose as the baseline the
-// main kernels remove.
+// vec4_transa: reg2d with 16-byte global loads, and A's slice kept k-major
+// (slice_at[k][m]) so that a patch's 8 A values for one k are adjacent: two
+// 16-byte LDS reads, like B's. Each lane loads one 16-byte chunk of A (block
+// row lane / 2, k offset 4 * (lane % 2)) and writes its four floats down
+// column m of slice_at. The two lanes of a row write rows k and k + 4 of
+// that column, 4 * 128 floats apart, which is the same LDS bank: a two-way
+// store conflict. The rung keeps it, unpadded, as the baseline the main
+// kernels remove (they never store A transposed).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_vec4_transa(Args a) {
-    __shared__ __attribute__((aligned(16))) float As[8][128];
-    __shared__ __attribute__((aligned(16))) float Bs[8][128];
-    const int tiles_n = (a.N + 127) / 128;
-    const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * 128;
-    const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * 128;
-    const int t = threadIdx.x;
-    const int ty = t >> 4, tx = t & 15;
-    const int rowA = t >> 1, colA = (t & 1) * 4;
-    const int br = t >> 5, bc = (t & 31) * 4;
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    float acc[8][8];
+    __shared__ __attribute__((aligned(16))) float slice_at[8][128];
+    __shared__ __attribute__((aligned(16))) float slice_b[8][128];
+    const int cols_of_blocks = (a.N + 127) / 128;
+    const int64_t bm = (int64_t)(blockIdx.x / cols_of_blocks) * 128;
+    const int64_t bn = (int64_t)(blockIdx.x % cols_of_blocks) * 128;
+    const int lane = threadIdx.x;
+    const int pm = (lane >> 4) * 8, pn = (lane & 15) * 8;
+    const int fill_m = lane >> 1, fill_k = (lane & 1) * 4;        // A chunk of this lane
+    const int fill_kb = lane >> 5, fill_n = (lane & 31) * 4;      // B chunk of this lane
+    Patch acc;
+    acc.clear();
+    for (int64_t k0 = 0; k0 < a.K; k0 += 8) {
+        // K and N are multiples of 4 (checked on the host), so a chunk lies
+        // wholly inside the matrix or wholly outside it.
+        f32x4 ca = {0.0f, 0.0f, 0.0f, 0.0f}, cb = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bm + fill_m < a.M && k0 + fill_k < a.K)
+            ca = *(const f32x4*)(a.A + (bm + fill_m) * a.lda + k0 + fill_k);
+        if (k0 + fill_kb < a.K && bn + fill_n < a.N)
+            cb = *(const f32x4*)(a.B + (k0 + fill_kb) * a.ldb + bn + fill_n);
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] = 0.0f;
-    for (int k0 = 0; k0 < a.K; k0 += 8) {
-        // K % 4 == 0 and N % 4 == 0 (checked on the host): a 4-wide chunk is
-        // either wholly inside the matrix or wholly outside.
-        const f32x4 va = (m0 + rowA < a.M && k0 + colA < a.K)
-                             ? *(const f32x4*)(a.A + (m0 + rowA) * a.lda + k0 + colA) : zero;
-        As[colA + 0][rowA] = va.x;
-        As[colA + 1][rowA] = va.y;
-        As[colA + 2][rowA] = va.z;
-        As[colA + 3][rowA] = va.w;
-        const f32x4 vb = (k0 + br < a.K && n0 + bc < a.N)
-                             ? *(const f32x4*)(a.B + (int64_t)(k0 + br) * a.ldb + n0 + bc) : zero;
-        *(f32x4*)&Bs[br][bc] = vb;
+        for (int c = 0; c < 4; ++c) slice_at[fill_k + c][fill_m] = ca[c];
+        *(f32x4*)&slice_b[fill_kb][fill_n] = cb;
         __syncthreads();
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const f32x4 m_lo = *(const f32x4*)&As[d][ty * 8];
-            const f32x4 m_hi = *(const f32x4*)&As[d][ty * 8 + 4];
-            const f32x4 n_lo = *(const f32x4*)&Bs[d][tx * 8];
-            const f32x4 n_hi = *(const f32x4*)&Bs[d][tx * 8 + 4];
-            const float rm[8] = {m_lo.x, m_lo.y, m_lo.z, m_lo.w, m_hi.x, m_hi.y, m_hi.z, m_hi.w};
-            const float rn[8] = {n_lo.x, n_lo.y, n_lo.z, n_lo.w, n_hi.x, n_hi.y, n_hi.z, n_hi.w};
+        for (int kk = 0; kk < 8; ++kk) {
+            float from_a[8], from_b[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 va = *(const f32x4*)&slice_at[kk][pm + 4 * h];
+                const f32x4 vb = *(const f32x4*)&slice_b[kk][pn + 4 * h];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[r][c] += rm[r] * rn[c];
+                for (int c = 0; c < 4; ++c) {
+                    from_a[4 * h + c] = va[c];
+                    from_b[4 * h + c] = vb[c];
+                }
+            }
+            acc.rank1(from_a, from_b);
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int64_t i = m0 + ty * 8 + r, j = n0 + tx * 8 + c;
-            if (i < a.M && j < a.N) store_out(a, i, j, acc[r][c]);
-        }
+    acc.store(a, bm + pm, bn + pn);
 }
 
 static int check_vec4_transa(const Args& a) {

@@ -20,8 +20,10 @@
 //    "Two ladders, one kernel").
 //  - Double-buffered K loop with a register prefetch stage and one barrier
 //    per slice ("Part 2", "Overlapping Loads and Computation").
-//  - Plain v_fma_f32: packed FP32 FMA is disabled at build time, so this
-//    kernel's ceiling is half the chip's FP32 peak.
+//  - Plain (unpacked) v_fmac_f32: packed FP32 FMA is disabled at build time.
+//    Unpacked FMAs still run above half the chip's 157.3 TFLOP/s vector
+//    peak (the peak probe and this kernel both exceed 78.6), so the kernel
+//    is priced against the full vector peak.
 #include "kernels.hpp"
 #include "sgemm_f32.h"
 
