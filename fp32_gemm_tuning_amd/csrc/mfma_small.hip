@@ -357,7 +357,10 @@ constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KU = 64;  // k per unrol
 
 template <bool VEC, bool TA = false, bool TB = false, bool TC = false>
 __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int kchunk) {
-    __shared__ float red[SK_WAVES][2][4][64];
+    // Rows padded to 68 floats: in the reduction below, the two 16-lane
+    // halves of a half-wave read the two column blocks, 4 rows apart, which
+    // the pad puts 16 banks apart (with 64 floats they shared banks).
+    __shared__ float red[SK_WAVES][2][4][68];
     const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
     const int m0 = tm * SK_BM, n0 = tn * SK_BN;
     const int rows_valid = (a.M - m0) < SK_BM ? (a.M - m0) : SK_BM;

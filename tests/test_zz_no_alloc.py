@@ -79,12 +79,12 @@ def _plan(M, N, K, ws_bytes):
 # every one is split by a stream-K kernel that fits the scratch (3584^3 would
 # take mfma_256x256_sk, 128 MiB, with an unlimited workspace).
 AUTO_PAIRS = [
-    [(3584, 3584, 3584, 1.0, 0.0, "integer"), (1024, 1024, 1024, 1.0, 0.0, "uniform")],
-    [(1536, 1536, 1536, 1.5, 0.5, "uniform"), (768, 768, 768, -1.0, 0.25, "integer")],
+    [(3584, 3584, 3584, 1.0, 0.0, "integer"), (1792, 1792, 1792, 1.0, 0.0, "uniform")],
+    [(2560, 2560, 2560, 1.5, 0.5, "uniform"), (1536, 1536, 1536, -1.0, 0.25, "integer")],
 ]
 
 
-@pytest.mark.parametrize("pair", AUTO_PAIRS, ids=["3584-then-1024", "1536-then-768"])
+@pytest.mark.parametrize("pair", AUTO_PAIRS, ids=["3584-then-1792", "2560-then-1536"])
 def test_automatic_matches_ws_entry_point(dev, pair):
     for i, (M, N, K, alpha, beta, dist) in enumerate(pair):
         name = _plan(M, N, K, sg.SCRATCH_BYTES)
