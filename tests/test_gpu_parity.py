@@ -281,3 +281,21 @@ def test_peak_probe_runs(dev, kind):
     assert rc == 0 and flops > 0
     vals = out.cpu().numpy()
     assert np.all(np.isfinite(vals)) and np.any(vals != 0.0)
+
+
+def test_clock_probe_reads_a_plausible_clock(dev):
+    """Kind 3: each workgroup's shader-clock and constant-rate counter
+    differences; their ratio times the runtime's constant rate is a clock
+    between 100 MHz and twice the reported peak."""
+    wgs = 256
+    out = torch.zeros(wgs * 256, dtype=torch.float32, device=dev)
+    print("[gpu] clock probe", flush=True)
+    rc, _ = sg.sgemm_f32_peak_probe(3, wgs, 512, out)
+    torch.cuda.synchronize()
+    assert rc == 0
+    rc, wall_khz, max_khz = sg.sgemm_f32_clock_rates()
+    assert rc == 0 and wall_khz > 0 and max_khz > 0
+    v = out.view(wgs, 256)[:, :2].cpu().numpy().astype(np.float64)
+    assert np.all(v > 0) and np.all(v < 2.0 ** 24)
+    mhz = v[:, 0] / v[:, 1] * wall_khz / 1e3
+    assert 100.0 < np.median(mhz) < 2.0 * max_khz / 1e3, (np.median(mhz), max_khz)
