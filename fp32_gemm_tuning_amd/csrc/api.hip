@@ -93,7 +93,7 @@ static const int kModelVariants[] = {
     SGEMM_F32_MFMA_128,      SGEMM_F32_MFMA_256,       SGEMM_F32_MFMA_64x128,
     SGEMM_F32_MFMA_64,       SGEMM_F32_MFMA_64x128_KG4, SGEMM_F32_MFMA_64x96_KG4,
     SGEMM_F32_MFMA_96x64_KG4, SGEMM_F32_MFMA_128x128_KG4, SGEMM_F32_MFMA_128_SK, SGEMM_F32_MFMA_64x128_SK,
-    SGEMM_F32_MFMA_256_SK,
+    SGEMM_F32_MFMA_256_SK,   SGEMM_F32_MFMA_DIRECT,
 };
 static bool model_variant(int variant) {
     for (int v : kModelVariants)
@@ -108,7 +108,7 @@ struct Model {
 };
 
 // Built-in model, listed in order of preference when predictions tie.
-static const Model kDefaultModel = {11,
+static const Model kDefaultModel = {12,
                                     {
                                         {SGEMM_F32_MFMA_128, 0.0, {0.919, 0.949, 0.970, 0.967}, 0.88, 6.5},
                                         {SGEMM_F32_MFMA_256, 0.0, {0.993, 0.959, 0.976, 0.976}, 0.86, 13.0},
@@ -121,6 +121,12 @@ static const Model kDefaultModel = {11,
                                         {SGEMM_F32_MFMA_128_SK, 11.5, {0.794, 0.983, 0.967, 0.925}, 0.88, 4.5},
                                         {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.720, 0.844, 1.000, 0.917}, 0.78, 2.5},
                                         {SGEMM_F32_MFMA_256_SK, 10.0, {0.961, 0.937, 0.977, 0.977}, 0.80, 20.0},
+                                        // Fitted to per-launch timings of 13 shapes around the
+                                        // tiny-product bound; one 32x32 tile per compute unit
+                                        // fits 6.0 us + 0.0087 us per k (eff 0.376). With more
+                                        // tiles per unit the linear form over-predicts, so those
+                                        // buckets are set low and other kernels take such calls.
+                                        {SGEMM_F32_MFMA_DIRECT, 6.0, {0.376, 0.30, 0.28, 0.28}, 0.80, 0.0},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a

@@ -342,7 +342,8 @@ static hipError_t launch_direct(const Args& a, hipStream_t s) {
 }
 
 Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
-                       (const void*)k_mfma_direct<DR_TM, DR_TN, DR_KS, true>, 64 * DR_KS, true};
+                       (const void*)k_mfma_direct<DR_TM, DR_TN, DR_KS, true>, 64 * DR_KS, true,
+                       nullptr, nullptr, DR_TM, DR_TN, 16};
 
 // ===========================================================================
 // mfma_skinny: for few rows (near-GEMV, e.g. 16 x 8192 x 8192, where B is

@@ -46,6 +46,7 @@ TILE: Dict[str, Tuple[int, int]] = {
     "mfma_128x128_sk": (128, 128),
     "mfma_64x128_sk": (64, 128),
     "mfma_256x256_sk": (256, 256),
+    "mfma_direct": (32, 32),
 }
 # Stream-K kernels and their K slice: their busiest unit holds floor(T/C)
 # whole tiles plus one run of slices (sk_split in the library), and they are

@@ -363,15 +363,17 @@ SGEMM_F32_API int sgemm_f32_variant_tile(int variant, int *bm, int *bn, int *bk)
  * (a fraction of a tile), with b taken for ceil(n); stream-K entries are
  * considered only by sgemm_f32_ws, on shapes they split, and when the
  * workspace suffices; if no entry applies, mfma_128x128 runs. M <= 32 and
- * tiny products bypass the model (mfma_skinny, mfma_direct; both read
- * transposed operands). Otherwise a call with a transposed operand (after
+ * products of fewer than 64 Mi multiply-adds bypass the model (mfma_skinny,
+ * mfma_direct; both read transposed operands); mfma_direct is also a model
+ * entry for larger products. Otherwise a call with a transposed operand (after
  * the column-major swap) is restricted to the model's entries that read
  * transposed operands (mfma_128x128 if there are none). */
 #define SGEMM_F32_MODEL_MAX 16
 typedef struct {
     int variant;        /* a tiled matrix-core variant: MFMA_128, MFMA_256, MFMA_64x128, MFMA_64,
                            MFMA_64x128_KG4, MFMA_64x96_KG4, MFMA_96x64_KG4, MFMA_128x128_KG4,
-                           MFMA_128_SK, MFMA_64x128_SK or MFMA_256_SK */
+                           MFMA_128_SK, MFMA_64x128_SK, MFMA_256_SK or MFMA_DIRECT (32x32
+                           tiles, no LDS tile: its K split is inside the workgroup) */
     double overhead_us; /* fixed cost per call, microseconds, in [0, 1e6] */
     double eff[4];      /* fraction of peak per tiles-per-CU bucket, in (0, 1.5] */
     double fill4;       /* factor on eff for calls that need the 4-byte fill, in (0, 1.5] */
