@@ -317,24 +317,34 @@ def torch_cus(t) -> int:
 
 
 def smi_snapshot() -> dict:
-    """Current graphics clock (MHz), and socket power (W) where reported, from
-    rocm-smi (read-only); empty when the tool is unavailable."""
+    """Current graphics clock (MHz) from rocm-smi and socket power (W) from
+    amd-smi (rocm-smi reports no power on every system), both read-only;
+    fields a tool does not report are left out."""
     import subprocess
+    res = {}
     try:
         out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
                              capture_output=True, text=True, timeout=20).stdout
         card = next(iter(json.loads(out[out.index("{"):]).values()))
+        for k, v in card.items():
+            kl = k.lower()
+            try:
+                if kl.startswith("sclk") and "speed" in kl:
+                    res["sclk_mhz"] = float(str(v).strip("() ").lower().replace("mhz", ""))
+                elif "power" in kl and "(w)" in kl:
+                    res["power_w"] = float(v)
+            except ValueError:
+                pass
     except Exception:
-        return {}
-    res = {}
-    for k, v in card.items():
-        kl = k.lower()
+        pass
+    if "power_w" not in res:
         try:
-            if kl.startswith("sclk") and "speed" in kl:
-                res["sclk_mhz"] = float(str(v).strip("() ").lower().replace("mhz", ""))
-            elif "power" in kl and "(w)" in kl:
-                res["power_w"] = float(v)
-        except ValueError:
+            out = subprocess.run(["amd-smi", "metric", "--power", "--json"],
+                                 capture_output=True, text=True, timeout=20).stdout
+            d = json.loads(out[out.index("{"):])
+            gpus = d["gpu_data"] if isinstance(d, dict) else d
+            res["power_w"] = float(gpus[0]["power"]["socket_power"]["value"])
+        except Exception:
             pass
     return res
 
