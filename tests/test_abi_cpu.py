@@ -165,6 +165,23 @@ def test_plan_busiest_cu_rule():
     assert _plan(1000, 1000, 1000, cus=1) == "mfma_256x256"
 
 
+def test_plan_direct_kernel_where_its_grid_fits_one_tile_per_cu():
+    # The direct kernel's 32x32 grid fits one tile per CU (at most 256 tiles):
+    # it keeps every CU busy where the 64x64 grid uses a quarter of them
+    # (measured per launch: 512^3 10.5 against 13.3 us for mfma_64x64,
+    # 512x512x2048 23.9 against 37.7, 256x1024x1024 15.0 against 21.3).
+    for M, N, K in [(448, 448, 448), (512, 512, 512), (512, 512, 2048), (256, 1024, 1024),
+                    (384, 640, 1536), (442, 347, 2477)]:
+        assert _plan(M, N, K) == "mfma_direct", (M, N, K)
+    # past one tile per CU, or with short K, mfma_64x64 (1024x1024x256: 7.6
+    # against 13.5 us back to back; 576^3 within 2%).
+    for M, N, K in [(1024, 1024, 256), (1000, 1000, 100), (576, 576, 576), (768, 768, 768),
+                    (1024, 1024, 1024)]:
+        assert _plan(M, N, K) == "mfma_64x64", (M, N, K)
+    # below 64 Mi multiply-adds the direct kernel runs whatever the grid
+    assert _plan(1000, 1000, 60) == "mfma_direct"
+
+
 def test_plan_falls_back_when_offsets_exceed_32_bits():
     # leading dimensions so large that even a 32-row (or 16-row) panel spans
     # more than 2^31 bytes
