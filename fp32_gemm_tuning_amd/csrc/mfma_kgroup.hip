@@ -195,6 +195,64 @@ void k_mfma_kgroup(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     // above, so a wave's accesses are consecutive. Slot 0 is stage 0 and slot
     // 1 stage 1: each half of a slot is its B part when a whole partial tile
     // fits in it, else the A part and the B part.
+    // Where they fit in the stages (every tile but the 64x64-wave one), the
+    // four groups split the tile by row quarters instead: quarter q is the
+    // accumulators 4q .. 4q+3 of every 32x32 block (rows 8q .. 8q+7 of the
+    // block), and group q owns it. Each group writes its partial sums of the
+    // three quarters it does not own, one barrier, and each group adds the
+    // other three groups' partials of its quarter in the same fixed order,
+    // (p0 + p2) + (p1 + p3), and stores it: one barrier instead of three,
+    // and all waves store. Region (q, s) holds source group s's partials of
+    // quarter q (s < q: region 3q + s, else 3q + s - 1), 16 bytes per thread
+    // of a group, block by block: a wave's accesses are consecutive.
+    constexpr int QQ = BI * BJ;                                 // blocks per lane
+    constexpr int RS = QQ * GT * 4;                             // floats per region
+    constexpr int NA = (KG * BM * BK) / RS, NB = (KG * BK * BNP) / RS;
+    if constexpr (2 * (NA + NB) >= 12) {
+        auto region = [&](int r) -> float* {
+            return r < NA ? As0 + r * RS
+                 : r < NA + NB ? Bs0 + (r - NA) * RS
+                 : r < 2 * NA + NB ? As1 + (r - NA - NB) * RS
+                 : Bs1 + (r - 2 * NA - NB) * RS;
+        };
+#pragma unroll
+        for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < BJ; ++bj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (q == g) continue;
+                    float* dst = region(3 * q + (g < q ? g : g - 1)) + ((bi * BJ + bj) * GT + tl) * 4;
+                    *(f32x4*)dst = f32x4{acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1],
+                                         acc[bi][bj][4 * q + 2], acc[bi][bj][4 * q + 3]};
+                }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q != g) continue;
+#pragma unroll
+            for (int bi = 0; bi < BI; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < BJ; ++bj) {
+                    f32x4 p[KG];
+#pragma unroll
+                    for (int src = 0; src < KG; ++src)
+                        p[src] = src == q ? f32x4{acc[bi][bj][4 * q], acc[bi][bj][4 * q + 1],
+                                                  acc[bi][bj][4 * q + 2], acc[bi][bj][4 * q + 3]}
+                                          : *(const f32x4*)(region(3 * q + (src < q ? src : src - 1)) +
+                                                            ((bi * BJ + bj) * GT + tl) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = (p[0][e] + p[2][e]) + (p[1][e] + p[3][e]);
+                        const int i = wm * WM + bi * 32 + 8 * q + 4 * h + e;
+                        const int j = wn * WN + bj * 32 + c;
+                        if (i < rows_valid && j < cols_valid)
+                            store_out(a, (int64_t)m0 + i, (int64_t)n0 + j, v);
+                    }
+                }
+        }
+        return;
+    }
     constexpr int Q = PER_LANE / 4;
     constexpr bool IN_B = KG * BK * BNP >= PER_LANE * GT;
     static_assert(IN_B || (KG * BK * BNP >= PER_LANE / 2 * GT && KG * BM * BK >= PER_LANE / 2 * GT),
