@@ -123,10 +123,10 @@ static const Model kDefaultModel = {12,
                                         {SGEMM_F32_MFMA_256_SK, 10.0, {0.961, 0.937, 0.977, 0.977}, 0.80, 20.0},
                                         // Fitted to per-launch timings of 13 shapes around the
                                         // tiny-product bound; one 32x32 tile per compute unit
-                                        // fits 6.0 us + 0.0087 us per k (eff 0.376). With more
+                                        // fits 4.9 us + 0.0087 us per k (eff 0.376). With more
                                         // tiles per unit the linear form over-predicts, so those
                                         // buckets are set low and other kernels take such calls.
-                                        {SGEMM_F32_MFMA_DIRECT, 6.0, {0.376, 0.30, 0.28, 0.28}, 0.80, 0.0},
+                                        {SGEMM_F32_MFMA_DIRECT, 4.9, {0.376, 0.30, 0.28, 0.28}, 0.80, 0.0},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a

@@ -284,18 +284,18 @@ __global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, in
             for (int r = 0; r < 16; ++r)
                 red[((w * NB + bi * BJ + bj) * 16 + r) * 64 + lane] = acc[bi][bj][r];
     __syncthreads();
-    for (int blk = w; blk < NB; blk += KS) {
+    // The NB * 16 accumulators of a lane are shared out among the waves
+    // (item it to wave it mod KS), each summed over the waves in order.
+    for (int it = w; it < NB * 16; it += KS) {
+        const int blk = it >> 4, r = it & 15;
         const int bi = blk / BJ, bj = blk % BJ;
+        float v = red[((0 * NB + blk) * 16 + r) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float v = red[((0 * NB + blk) * 16 + r) * 64 + lane];
-#pragma unroll
-            for (int ww = 1; ww < KS; ++ww) v += red[((ww * NB + blk) * 16 + r) * 64 + lane];
-            const int i = bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const int jj = bj * 32 + c;
-            if (i < rows_valid && jj < cols_valid)
-                store_out(a, (int64_t)m0 + i, (int64_t)n0 + jj, v);
-        }
+        for (int ww = 1; ww < KS; ++ww) v += red[((ww * NB + blk) * 16 + r) * 64 + lane];
+        const int i = bi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int jj = bj * 32 + c;
+        if (i < rows_valid && jj < cols_valid)
+            store_out(a, (int64_t)m0 + i, (int64_t)n0 + jj, v);
     }
 }
 
