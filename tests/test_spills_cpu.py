@@ -8,9 +8,9 @@ not zero, this test works out which variant and which form (16-byte,
 register-staged or 4-byte fill; whole tiles or masked; transpositions) it is,
 builds a call that takes exactly that form, installs a one-entry dispatch
 model holding that variant, and checks that sgemm_f32_plan_ws does not
-choose it. Every kernel outside the dispatch model (the skinny and direct
-kernels, the fallbacks, the stream-K fix-up) must not spill at all. A
-positive control checks that spill-free forms are still chosen.
+choose it. Every other kernel (the skinny and direct kernels, the
+fallbacks, the stream-K fix-up) must not spill at all. A positive control
+checks that spill-free forms are still chosen.
 """
 import os
 import re
