@@ -121,12 +121,12 @@ static const Model kDefaultModel = {12,
                                         {SGEMM_F32_MFMA_128_SK, 11.5, {0.794, 0.983, 0.967, 0.925}, 0.88, 4.5},
                                         {SGEMM_F32_MFMA_64x128_SK, 10.0, {0.720, 0.844, 1.000, 0.917}, 0.78, 2.5},
                                         {SGEMM_F32_MFMA_256_SK, 10.0, {0.961, 0.937, 0.977, 0.977}, 0.80, 20.0},
-                                        // Fitted to per-launch timings of 13 shapes around the
-                                        // tiny-product bound; one 32x32 tile per compute unit
-                                        // fits 4.9 us + 0.0087 us per k (eff 0.376). With more
-                                        // tiles per unit the linear form over-predicts, so those
-                                        // buckets are set low and other kernels take such calls.
-                                        {SGEMM_F32_MFMA_DIRECT, 4.9, {0.376, 0.30, 0.28, 0.28}, 0.80, 0.0},
+                                        // Fitted to per-launch timings around the tiny-product
+                                        // bound: one 32x32 tile per compute unit fits 4.9 us +
+                                        // 0.0087 us per k (eff 0.376), two tiles eff 0.40-0.44
+                                        // (7 shapes); three or more are set low (measured
+                                        // 0.30-0.43), where mfma_64x64 mostly wins.
+                                        {SGEMM_F32_MFMA_DIRECT, 4.9, {0.376, 0.42, 0.35, 0.31}, 0.63, 0.0},
                                     }};
 // The active model. A replacement is published by swapping this pointer;
 // superseded models are never freed, so a concurrent reader never sees a

@@ -165,17 +165,20 @@ def test_plan_busiest_cu_rule():
     assert _plan(1000, 1000, 1000, cus=1) == "mfma_256x256"
 
 
-def test_plan_direct_kernel_where_its_grid_fits_one_tile_per_cu():
-    # The direct kernel's 32x32 grid fits one tile per CU (at most 256 tiles):
-    # it keeps every CU busy where the 64x64 grid uses a quarter of them
-    # (measured per launch: 512^3 10.5 against 13.3 us for mfma_64x64,
-    # 512x512x2048 23.9 against 37.7, 256x1024x1024 15.0 against 21.3).
+def test_plan_direct_kernel_where_its_grid_fits_one_or_two_tiles_per_cu():
+    # The direct kernel's 32x32 grid holds one or two tiles per CU (at most
+    # 512 tiles): it keeps every CU busy where the 64x64 grid uses a quarter
+    # of them (measured per launch: 512^3 10.5 against 13.3 us for
+    # mfma_64x64, 512x512x2048 23.9 against 37.7, 576^3 13.6 against 14.5,
+    # 600x600x1200 23.3 against 28.0, 1416x324x588 14.7 against 16.8).
     for M, N, K in [(448, 448, 448), (512, 512, 512), (512, 512, 2048), (256, 1024, 1024),
-                    (384, 640, 1536), (442, 347, 2477)]:
+                    (384, 640, 1536), (442, 347, 2477), (576, 576, 576), (704, 704, 704),
+                    (600, 600, 1200), (1416, 324, 588)]:
         assert _plan(M, N, K) == "mfma_direct", (M, N, K)
-    # past one tile per CU, or with short K, mfma_64x64 (1024x1024x256: 7.6
-    # against 13.5 us back to back; 576^3 within 2%).
-    for M, N, K in [(1024, 1024, 256), (1000, 1000, 100), (576, 576, 576), (768, 768, 768),
+    # three or more tiles per CU, or short K: mfma_64x64 (768^3 17.6 against
+    # 23.0 us, 300x2000x300 11.5 against 12.8, 1024x1024x256 7.6 against 13.5
+    # back to back).
+    for M, N, K in [(1024, 1024, 256), (1000, 1000, 100), (300, 2000, 300), (768, 768, 768),
                     (1024, 1024, 1024)]:
         assert _plan(M, N, K) == "mfma_64x64", (M, N, K)
     # below 64 Mi multiply-adds the direct kernel runs whatever the grid
