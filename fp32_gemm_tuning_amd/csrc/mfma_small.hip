@@ -1,6 +1,6 @@
 // FP32 matrix-core kernels for shapes the tiled kernels serve badly:
-// mfma_64x64_k4 (in-workgroup K split), mfma_direct (tiny products, no LDS)
-// and mfma_skinny (M <= 32, HBM-bound).
+// mfma_64x64_k4 (in-workgroup K split), mfma_direct (small products and few
+// tiles, no LDS tile) and mfma_skinny (M <= 32, HBM-bound).
 // Operand layouts and edge handling: mfma_common.hpp.
 #include "mfma_common.hpp"
 

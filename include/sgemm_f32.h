@@ -125,10 +125,11 @@ enum sgemm_f32_variant_id {
        slice four ways and sum their partial tiles in a fixed order (few tiles,
        long K) */
     SGEMM_F32_MFMA_64_K4 = 10,
-    /* FP32 matrix-core kernel for small shapes: 32x32 tiles, four
+    /* FP32 matrix-core kernel for small shapes: 32x32 tiles, eight
        waves split K and load their operands straight into matrix-core
        registers (no LDS tile, no barrier in the K loop), fixed-order
-       reduction at the end */
+       reduction at the end; also a dispatch-model kernel where its grid
+       holds one or two tiles per compute unit */
     SGEMM_F32_MFMA_DIRECT = 11,
     /* FP32 matrix-core kernel, 64x128 block tile (4 waves of 64x32,
        v_mfma_f32_32x32x2_f32, 32-deep K slices), pipelined as MFMA_256:
