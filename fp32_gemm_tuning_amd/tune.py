@@ -54,8 +54,10 @@ TILE: Dict[str, Tuple[int, int]] = {
 SK_BK: Dict[str, int] = {"mfma_128x128_sk": 32, "mfma_64x128_sk": 32, "mfma_256x256_sk": 16}
 PEAK_PER_CU = 4 * 64 * 2.4e9   # FP32 matrix FLOP/s of one MI355X compute unit
 
-# Shapes the built-in model was fitted on: square, flat, tall, odd, short-K,
-# and the two 8-way row shards of 4096^3 and 8192^3.
+# Shapes a fit times: square, flat, tall, odd, short-K, the two 8-way row
+# shards of 4096^3 and 8192^3 (the 30 the built-in model's tile-kernel rows
+# were fitted on), and five where the direct kernel's 32x32 grid holds one or
+# two tiles per compute unit.
 DEFAULT_SHAPES: List[Tuple[int, int, int]] = [
     (512, 512, 512), (768, 768, 768), (1024, 1024, 1024), (1280, 1280, 1280),
     (1536, 1536, 1536), (2048, 2048, 2048), (2560, 2560, 2560), (3072, 3072, 3072),
@@ -65,6 +67,8 @@ DEFAULT_SHAPES: List[Tuple[int, int, int]] = [
     (3000, 3000, 500), (500, 3000, 3000), (4000, 4000, 256), (2048, 2048, 8192),
     (1024, 1024, 4096), (2048, 4096, 2048), (1531, 1000, 777), (2050, 2050, 2050),
     (512, 4096, 4096), (1024, 8192, 8192),
+    # where the direct kernel's 32x32 grid holds one or two tiles per unit
+    (448, 448, 448), (512, 512, 2048), (256, 1024, 1024), (640, 640, 640), (600, 600, 1200),
 ]
 QUICK_SHAPES: List[Tuple[int, int, int]] = [
     (1024, 1024, 1024), (1000, 1531, 777), (2048, 2048, 2048), (3072, 3072, 3072),
