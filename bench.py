@@ -205,6 +205,8 @@ def sweep(args, dev) -> int:
                 else:
                     torch.mm(dA, dB, out=dC)
                 return 0
+            if not args.no_clock_warmup:
+                clock_warmup(ctx, 0.3)
             durs, _ = time_calls(ctx, args.steps, args.warmup, stream)
             kms = float(durs.mean())
             print(json.dumps({"sweep": True, "workload": wname, "variant": "context:torch.mm fp32",
@@ -255,6 +257,11 @@ def sweep(args, dev) -> int:
                 print(json.dumps({"sweep": True, "workload": wname, "variant": label,
                                   "skipped": sg.sgemm_f32_strerror(rc)}), flush=True)
                 continue
+            # Each fast row gets its own untimed warm-up: a row timed right
+            # after the slow rungs (or after a kernel that draws less power)
+            # otherwise runs part of its calls on a lower clock.
+            if not slow and not args.no_clock_warmup:
+                clock_warmup(call, 0.15)
             durs, region = time_calls(call, 3 if slow else args.steps,
                                       1 if slow else args.warmup, stream)
             kms = float(durs.mean())
