@@ -348,19 +348,34 @@ Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
 // ===========================================================================
 // mfma_skinny: for few rows (near-GEMV, e.g. 16 x 8192 x 8192, where B is
 // read once and the shape is bound by HBM bandwidth). A workgroup owns a
-// 16x32 tile of C and all of K; its 16 waves each take one contiguous 1/16 of
-// K, so 16 independent streams of B loads are in flight per compute unit.
+// 16x32 tile of C and all of K, cut into blocks of 32 k; its 16 waves take
+// the blocks in turn (wave w: blocks w, w + 16, w + 32, ...), so at any time
+// the waves of every workgroup read one band of a few hundred consecutive
+// rows of B and the whole chip streams B band by band. (With each wave
+// owning one contiguous 1/16 of K instead, every workgroup reads 16 bands
+// far apart, 128 bytes per row of each: on MI355X a cold 16 x 8192 x 8192
+// call then read B at 3.9 TB/s, in the banded order at 5.0 TB/s.) B stored
+// transposed keeps the contiguous runs: there a workgroup's 32 columns are
+// one contiguous region of memory already. Each wave keeps two blocks in
+// flight: the loads of its next block are issued before the MFMAs of the
+// current one.
 // Operands go straight from global memory into MFMA registers (no LDS tile):
-// lane l of a wave reads row k = 4*(l/16) + s of its K run at column l%16 of
-// each 16-column block, 64 contiguous bytes per quarter-wave, and a 16-byte
-// run of 4 consecutive k of row l%16 of A. At the end the 16 partial tiles
-// are summed in a fixed order through LDS (deterministic) and the epilogue
-// writes C.
+// lane l of a wave reads rows k = 4*(l/16) + s of a 16-k step at column l%16
+// of each 16-column block -- or, when B is read along N 8 bytes at a time,
+// at columns 2(l%16) and 2(l%16) + 1, the two accumulators then holding the
+// even and the odd columns -- and a 16-byte run of 4 consecutive k of row
+// l%16 of A. At the end the 16 partial tiles are summed in a fixed order
+// through LDS (deterministic) and the epilogue writes C.
 // ===========================================================================
-constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KU = 64;  // k per unrolled step
+constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KB = 32;  // k per block
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 
 template <bool VEC, bool TA = false, bool TB = false, bool TC = false>
-__global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int kchunk) {
+__global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n) {
     // Rows padded to 68 floats: in the reduction below, the two 16-lane
     // halves of a half-wave read the two column blocks, 4 rows apart, which
     // the pad puts 16 banks apart (with 64 floats they shared banks).
@@ -369,77 +384,138 @@ __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int k
     const int m0 = tm * SK_BM, n0 = tn * SK_BN;
     const int rows_valid = (a.M - m0) < SK_BM ? (a.M - m0) : SK_BM;
     const int cols_valid = (a.N - n0) < SK_BN ? (a.N - n0) : SK_BN;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // The wave index in a scalar register: the blocks a wave takes, and so
+    // each block's buffer resources, derive from it, and a resource held in
+    // vector registers costs a per-lane loop around every load.
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int g = lane >> 4, c = lane & 15;
-    const int kbeg = w * kchunk;
-    const int kend = (a.K - kbeg) < kchunk ? a.K : kbeg + kchunk;
 
-    // With both operands transposed and 4-byte loads, a 64-deep step's
-    // addresses and values exceed the 128 registers of a 1024-lane
-    // workgroup: such calls step 32 deep.
-    constexpr int KU = (!VEC && TA && TB) ? SK_KU / 2 : SK_KU;
-    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = kbeg; k0 < kend; k0 += KU) {
-        const int kk = (a.K - k0) < KU ? (a.K - k0) : KU;  // rows present in memory
-        const int klim = kend - k0;                              // rows this wave owns
+    // With both operands transposed and 4-byte loads, the addresses and
+    // values of two blocks of 32 k exceed the 128 registers of a 1024-lane
+    // workgroup: such calls take blocks of 16 k.
+    constexpr int KB = (!VEC && TA && TB) ? SK_KB / 2 : SK_KB;
+    const int nblocks = (a.K + KB - 1) / KB;
+    struct Regs {
+        f32x4 af[KB / 16];
+        float b0[KB / 4], b1[KB / 4];
+    };
+    // PAIR: B is read along N 8 bytes at a time (see `pair` below): b0 holds
+    // column 2c, b1 column 2c + 1; otherwise columns c and c + 16.
+    auto load = [&](int blk, Regs& r, auto pair) {
+        constexpr bool PAIR = decltype(pair)::value;
+        // A block at or past the end of K (kk = 0) has empty resources:
+        // every load reads zero and nothing is fetched.
+        // (Wave-uniform; the clamps below compile to vector instructions,
+        // and readfirstlane keeps the resources in scalar registers.)
+        const int k0 = __builtin_amdgcn_readfirstlane(blk * KB);
+        const int kr = a.K - k0;
+        const int kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < KB ? kr : KB));  // rows present
         const __amdgpu_buffer_rsrc_t rA =
             TA ? make_rsrc(a.A + (int64_t)k0 * a.lda + m0,
-                           (uint32_t)(((int64_t)(kk - 1) * a.lda + rows_valid) * 4))
+                           kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a.lda + rows_valid) * 4) : 0u)
                : make_rsrc(a.A + (int64_t)m0 * a.lda + k0,
-                           (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4));
+                           kk > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * a.lda + kk) * 4) : 0u);
         const __amdgpu_buffer_rsrc_t rB =
             TB ? make_rsrc(a.B + (int64_t)n0 * a.ldb + k0,
-                           (uint32_t)(((int64_t)(cols_valid - 1) * a.ldb + kk) * 4))
+                           kk > 0 ? (uint32_t)(((int64_t)(cols_valid - 1) * a.ldb + kk) * 4) : 0u)
                : make_rsrc(a.B + (int64_t)k0 * a.ldb + n0,
-                           (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4));
-        f32x4 af[KU / 16];
-        float b0[KU / 4], b1[KU / 4];
+                           kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a.ldb + cols_valid) * 4) : 0u);
 #pragma unroll
-        for (int u = 0; u < KU / 16; ++u) {
+        for (int u = 0; u < KB / 16; ++u) {
             const int kq = 16 * u + 4 * g;  // this lane's 4 consecutive k
             if (VEC && !TA) {
-                const bool ok = c < rows_valid && kq + 4 <= klim;
-                af[u] = buf_load4(rA, ok ? (uint32_t)((c * (int)a.lda + kq) * 4) : OOB);
+                const bool ok = c < rows_valid && kq + 4 <= kk;
+                r.af[u] = buf_load4(rA, ok ? (uint32_t)((c * (int)a.lda + kq) * 4) : OOB);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bool ok = c < rows_valid && kq + e < klim;
+                    const bool ok = c < rows_valid && kq + e < kk;
                     const int off = TA ? (kq + e) * (int)a.lda + c : c * (int)a.lda + kq + e;
-                    af[u][e] = buf_load1(rA, ok ? (uint32_t)(off * 4) : OOB);
+                    r.af[u][e] = buf_load1(rA, ok ? (uint32_t)(off * 4) : OOB);
                 }
             }
             if (VEC && TB) {
                 // Columns c and c + 16 of B are rows of the stored matrix:
                 // 4 consecutive k in one 16-byte load each.
-                const bool ok = kq + 4 <= klim;
+                const bool ok = kq + 4 <= kk;
                 const f32x4 x0 = buf_load4(rB, ok && c < cols_valid ? (uint32_t)((c * (int)a.ldb + kq) * 4) : OOB);
                 const f32x4 x1 = buf_load4(rB, ok && c + 16 < cols_valid
                                                    ? (uint32_t)(((c + 16) * (int)a.ldb + kq) * 4) : OOB);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    b0[4 * u + e] = x0[e];
-                    b1[4 * u + e] = x1[e];
+                    r.b0[4 * u + e] = x0[e];
+                    r.b1[4 * u + e] = x1[e];
+                }
+            } else if (PAIR) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kq_e = kq + e;
+                    const f32x2 x = buf_load2(rB, kq_e < kk ? (uint32_t)((kq_e * (int)a.ldb + 2 * c) * 4) : OOB);
+                    r.b0[4 * u + e] = x.x;
+                    r.b1[4 * u + e] = x.y;
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int kr = kq + e;
-                    const bool okr = kr < klim;
-                    const int o0 = TB ? c * (int)a.ldb + kr : kr * (int)a.ldb + c;
-                    const int o1 = TB ? (c + 16) * (int)a.ldb + kr : kr * (int)a.ldb + c + 16;
-                    b0[4 * u + e] = buf_load1(rB, okr && c < cols_valid ? (uint32_t)(o0 * 4) : OOB);
-                    b1[4 * u + e] = buf_load1(rB, okr && c + 16 < cols_valid ? (uint32_t)(o1 * 4) : OOB);
+                    const int kq_e = kq + e;
+                    const bool okr = kq_e < kk;
+                    const int o0 = TB ? c * (int)a.ldb + kq_e : kq_e * (int)a.ldb + c;
+                    const int o1 = TB ? (c + 16) * (int)a.ldb + kq_e : kq_e * (int)a.ldb + c + 16;
+                    r.b0[4 * u + e] = buf_load1(rB, okr && c < cols_valid ? (uint32_t)(o0 * 4) : OOB);
+                    r.b1[4 * u + e] = buf_load1(rB, okr && c + 16 < cols_valid ? (uint32_t)(o1 * 4) : OOB);
                 }
             }
         }
+    };
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto mma = [&](const Regs& r) {
 #pragma unroll
-        for (int u = 0; u < KU / 16; ++u)
+        for (int u = 0; u < KB / 16; ++u)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b0[4 * u + e], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(af[u][e], b1[4 * u + e], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(r.af[u][e], r.b0[4 * u + e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(r.af[u][e], r.b1[4 * u + e], acc1, 0, 0, 0);
             }
-    }
+    };
+    // This wave's blocks (w, w + 16, ...: see BANDED), two in flight: the
+    // loads of its next block go out before the MFMAs of the current one
+    // (register sets r0, r1). The
+    // loads are unconditional (past the end of K they read zeros), and
+    // scheduling fences keep each block's loads ahead of the other block's
+    // MFMAs: loads issued on only some paths, or sunk below the MFMAs, make
+    // the compiler wait for every load in flight, the prefetched ones
+    // included, before a block's MFMAs.
+    // With B stored transposed a workgroup's 32 columns are 32 whole rows
+    // of the stored matrix, one contiguous region, which streams best with
+    // each wave taking one contiguous run of blocks instead (wave w: blocks
+    // w * per .. w * per + per - 1).
+    constexpr bool BANDED = !TB;
+    const int per = (nblocks + SK_WAVES - 1) / SK_WAVES;
+    const int count = BANDED ? (nblocks > w ? (nblocks - w + SK_WAVES - 1) / SK_WAVES : 0)
+                             : (nblocks - w * per < per ? (nblocks - w * per > 0 ? nblocks - w * per : 0) : per);
+    // The wave's i-th block; past its last one, a block past the end of K.
+    auto blk = [&](int i) { return i >= count ? nblocks : BANDED ? w + SK_WAVES * i : w * per + i; };
+    auto run = [&](auto pair) {
+        Regs r0, r1;
+        load(blk(0), r0, pair);
+        for (int i = 0; i < count; i += 2) {
+            load(blk(i + 1), r1, pair);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(r0);
+            __builtin_amdgcn_sched_barrier(0);
+            load(blk(i + 2), r0, pair);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < count) mma(r1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Pair reads need untransposed B with 8-byte aligned rows and a tile
+    // wholly inside N (at the edge a pair would straddle the last column).
+    const bool pair = !TB && VEC && (a.ldb & 1) == 0 && ((uintptr_t)a.B & 7) == 0 && cols_valid == SK_BN;
+    if (pair)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -452,7 +528,8 @@ __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int k
         // consecutive rows of a column-major one (TC).
         const int i = TC ? threadIdx.x % SK_BM : threadIdx.x / SK_BN;
         const int j = TC ? threadIdx.x / SK_BM : threadIdx.x % SK_BN;
-        const int bj = j >> 4, src = (i >> 2) * 16 + (j & 15), r = i & 3;
+        const int bj = pair ? (j & 1) : (j >> 4), cj = pair ? (j >> 1) : (j & 15);
+        const int src = (i >> 2) * 16 + cj, r = i & 3;
         float v = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < SK_WAVES; ++ww) v += red[ww][bj][r][src];
@@ -465,15 +542,9 @@ __global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n, int k
     }
 }
 
-static int skinny_kchunk(const Args& a) {
-    // Equal K runs per wave, each a multiple of 16.
-    const int64_t per = cdiv(a.K, SK_WAVES);
-    return (int)(cdiv(per, 16) * 16);
-}
-
 static int check_skinny(const Args& a) {
-    const int64_t ea = extent_a(a, SK_BM, SK_KU);
-    const int64_t eb = extent_b(a, SK_KU, SK_BN);
+    const int64_t ea = extent_a(a, SK_BM, SK_KB);
+    const int64_t eb = extent_b(a, SK_KB, SK_BN);
     if (ea >= (int64_t)OOB || eb >= (int64_t)OOB) return SGEMM_F32_ERR_TOO_LARGE;
     const int64_t tiles = cdiv(a.M, SK_BM) * cdiv(a.N, SK_BN);
     return tiles <= max_workgroups(1024) ? 0 : SGEMM_F32_ERR_TOO_LARGE;
@@ -483,18 +554,17 @@ static hipError_t launch_skinny(const Args& a, hipStream_t s) {
     const int tn = (int)cdiv(a.N, SK_BN);
     const dim3 grid((unsigned)(cdiv(a.M, SK_BM) * tn)), block(1024);
     const bool vec = small_vec_ok(a);
-    const int kchunk = skinny_kchunk(a);
     return with_trans(a, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (a.tc) {
             if (vec)
-                hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB, true>), grid, block, 0, s, a, tn, kchunk);
+                hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB, true>), grid, block, 0, s, a, tn);
             else
-                hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB, true>), grid, block, 0, s, a, tn, kchunk);
+                hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB, true>), grid, block, 0, s, a, tn);
         } else if (vec) {
-            hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB>), grid, block, 0, s, a, tn, kchunk);
+            hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB>), grid, block, 0, s, a, tn);
         } else {
-            hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB>), grid, block, 0, s, a, tn, kchunk);
+            hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB>), grid, block, 0, s, a, tn);
         }
         return hipGetLastError();
     });

@@ -130,10 +130,11 @@ def test_column_major_few_rows_take_the_skinny_kernel(ta, tb):
         rc, v = sg.sgemm_f32_plan_ex(COL, ta, tb, M, N, K, 1.0, P, lda, P, ldb, 0.0, P, ldc, 256)
         assert rc == 0 and sg.sgemm_f32_variant_name(v) == "mfma_skinny", (M, N, K)
     # A leading dimension too large for the skinny kernel's 32-bit buffer
-    # offsets (63 rows of the stored A^T span more than 2^31 bytes): the call
-    # keeps the swapped plan instead.
+    # offsets (the 31 rows a 32-deep block of the stored A^T spans past its
+    # first cover more than 2^31 bytes): the call keeps the swapped plan
+    # instead.
     if (ta, tb) == (NT, NT):
-        rc, v = sg.sgemm_f32_plan_ex(COL, NT, NT, 16, 8192, 8192, 1.0, P, 1 << 24, P, 8192, 0.0, P,
+        rc, v = sg.sgemm_f32_plan_ex(COL, NT, NT, 16, 8192, 8192, 1.0, P, 1 << 25, P, 8192, 0.0, P,
                                      16, 256)
         assert rc == 0 and sg.sgemm_f32_variant_name(v) != "mfma_skinny"
     # Row-major with few columns is the same transposed problem.
