@@ -179,19 +179,25 @@ struct DirectFrag {
     // Element (m, k) of A sits at m*lda + k, or at k*lda + m when A is stored
     // transposed (TA); element (k, n) of B at k*ldb + n, or at n*ldb + k (TB).
     // VEC: the k-contiguous operands (A unless TA, B if TB) take 16-byte loads.
-    __device__ __forceinline__ void load(const Args& a_, int m0, int n0, int k0, int rows_valid,
+    // A step at or past the end of K (kk = 0) has empty resources: every
+    // load reads zero and nothing is fetched. k0 and kk are wave-uniform;
+    // readfirstlane keeps the resources in scalar registers (built from
+    // vector registers, each load would run in a per-lane loop).
+    __device__ __forceinline__ void load(const Args& a_, int m0, int n0, int k0_, int rows_valid,
                                          int cols_valid, int h, int c) {
-        const int kk = (a_.K - k0) < 16 ? (a_.K - k0) : 16;
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_);
+        const int kr = a_.K - k0;
+        const int kk = __builtin_amdgcn_readfirstlane(kr <= 0 ? 0 : (kr < 16 ? kr : 16));
         const __amdgpu_buffer_rsrc_t rA =
             TA ? make_rsrc(a_.A + (int64_t)k0 * a_.lda + m0,
-                           (uint32_t)(((int64_t)(kk - 1) * a_.lda + rows_valid) * 4))
+                           kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a_.lda + rows_valid) * 4) : 0u)
                : make_rsrc(a_.A + (int64_t)m0 * a_.lda + k0,
-                           (uint32_t)(((int64_t)(rows_valid - 1) * a_.lda + kk) * 4));
+                           kk > 0 ? (uint32_t)(((int64_t)(rows_valid - 1) * a_.lda + kk) * 4) : 0u);
         const __amdgpu_buffer_rsrc_t rB =
             TB ? make_rsrc(a_.B + (int64_t)n0 * a_.ldb + k0,
-                           (uint32_t)(((int64_t)(cols_valid - 1) * a_.ldb + kk) * 4))
+                           kk > 0 ? (uint32_t)(((int64_t)(cols_valid - 1) * a_.ldb + kk) * 4) : 0u)
                : make_rsrc(a_.B + (int64_t)k0 * a_.ldb + n0,
-                           (uint32_t)(((int64_t)(kk - 1) * a_.ldb + cols_valid) * 4));
+                           kk > 0 ? (uint32_t)(((int64_t)(kk - 1) * a_.ldb + cols_valid) * 4) : 0u);
 #pragma unroll
         for (int bi = 0; bi < BI; ++bi) {
             const int row = 32 * bi + c;
@@ -245,10 +251,12 @@ __global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, in
 
     int tm, tn;
     tile_of(blockIdx.x, tiles_m, tiles_n, DR_GROUP_M, xcd_remap != 0, tm, tn);
-    const int m0 = tm * TM, n0 = tn * TN;
+    // Workgroup- and wave-uniform values in scalar registers (the tile
+    // mapping's divisions and the thread index leave them in vector ones).
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * TM), n0 = __builtin_amdgcn_readfirstlane(tn * TN);
     const int rows_valid = (a.M - m0) < TM ? (a.M - m0) : TM;
     const int cols_valid = (a.N - n0) < TN ? (a.N - n0) : TN;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int h = lane >> 5, c = lane & 31;
 
     f32x16 acc[BI][BJ];
@@ -260,19 +268,33 @@ __global__ __launch_bounds__(64 * KS) void k_mfma_direct(Args a, int tiles_m, in
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nsteps = (a.K + 15) / 16;
-    DirectFrag<TM, TN, VEC, TA, TB> cur, nxt;
-    if (w < nsteps) cur.load(a, m0, n0, 16 * w, rows_valid, cols_valid, h, c);
-    for (int j = w; j < nsteps; j += KS) {
-        if (j + KS < nsteps) nxt.load(a, m0, n0, 16 * (j + KS), rows_valid, cols_valid, h, c);
+    using Frag = DirectFrag<TM, TN, VEC, TA, TB>;
+    auto mma = [&](const Frag& f) {
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
             for (int bi = 0; bi < BI; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < BJ; ++bj)
-                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[bi][s], cur.b[bj][s],
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[bi][s], f.b[bj][s],
                                                                        acc[bi][bj], 0, 0, 0);
-        cur = nxt;
+    };
+    // Steps j and j + KS alternate between two register sets. The loads are
+    // unconditional (past the end of K they read zeros) and fenced ahead of
+    // the other set's MFMAs: loads issued on only some paths, or sunk below
+    // the MFMAs, make the compiler wait for every load in flight before a
+    // step's MFMAs.
+    Frag f0, f1;
+    f0.load(a, m0, n0, 16 * w, rows_valid, cols_valid, h, c);
+    for (int j = w; j < nsteps; j += 2 * KS) {
+        f1.load(a, m0, n0, 16 * (j + KS), rows_valid, cols_valid, h, c);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        f0.load(a, m0, n0, 16 * (j + 2 * KS), rows_valid, cols_valid, h, c);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + KS < nsteps) mma(f1);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Fixed-order reduction over the KS waves: red[w][block][r][lane].
