@@ -141,6 +141,37 @@ def test_small_cases(dev, variant, case):
         assert np.array_equal(C[:, N:], C0[:, N:], equal_nan=True)
 
 
+# The near-GEMV kernel (mfma_skinny) deals K out in blocks of 32 to its 16
+# waves in turn, keeps two blocks in flight per wave, and reads B 8 bytes at
+# a time on whole tiles of an untransposed B with 8-byte aligned rows (4 bytes
+# otherwise). Cases: fewer blocks than waves, a K tail, a narrow last tile
+# beside whole ones, an odd pitch and a misaligned base for B (4-byte reads),
+# beta != 0 on two tile rows, K = 1, and a wave with one more block than the
+# others (an odd number of blocks per wave).
+SKINNY = [
+    (16, 4128, 96, 1.0, 0.0, "uniform", (0, 0, 0), (0, 0, 0)),
+    (16, 4100, 4100, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
+    (31, 1000, 3000, 2.0, 0.5, "integer", (0, 0, 0), (0, 0, 0)),
+    (16, 2048, 8192, 1.0, 0.0, "uniform", (0, 1, 0), (0, 0, 0)),
+    (16, 2048, 2048, 1.0, 0.0, "integer", (0, 0, 0), (0, 1, 0)),
+    (5, 96, 1, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
+    (16, 64, 33, 1.0, -1.0, "uniform", (0, 2, 0), (0, 0, 0)),
+    (16, 512, 16 * 32 * 3 + 32, 1.0, 0.0, "integer", (0, 0, 0), (0, 0, 0)),
+]
+
+
+@pytest.mark.parametrize("case", SKINNY, ids=lambda c: "x".join(map(str, c[:3])) + f"-{c[5]}")
+def test_skinny_block_order(dev, case):
+    M, N, K, alpha, beta, dist, pads, offsets = case
+    variant = sg.sgemm_f32_variant_by_name("mfma_skinny")
+    A, B, C0 = inputs(M, N, K, dist, 3000 + M + N + K, beta, pads)
+    rc, C = run(variant, M, N, K, alpha, beta, A, B, C0, dev, offsets, tag="skinny-blocks")
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    rep = check_full(C, A, B, C0, M, N, K, alpha, beta, exact=(dist == "integer"))
+    print(f"[gpu] skinny {case[:3]}: {rep}", flush=True)
+    assert rep.ok, f"mfma_skinny {case}: {rep}"
+
+
 @pytest.mark.parametrize("variant", [None] + ALL,
                          ids=lambda v: "auto" if v is None else sg.sgemm_f32_variant_name(v))
 def test_quick_returns(dev, variant):
