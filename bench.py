@@ -356,6 +356,26 @@ def smi_snapshot() -> dict:
     return res
 
 
+def smi_under_load(call, seconds_first: float = 0.3, cap_s: float = 20.0) -> dict:
+    """smi_snapshot() read while `call` keeps running back to back (untimed):
+    the tools take about a second, and read after a synchronisation they see
+    an idle GPU and its idle power. A thread runs the read; this one keeps
+    the GPU busy until it returns."""
+    import threading
+    import torch
+    res = {}
+    clock_warmup(call, seconds_first)
+    th = threading.Thread(target=lambda: res.update(smi_snapshot()), daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < cap_s:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    return res
+
+
 def copy_bandwidth_gbs(dev, mib: int = 1024, reps: int = 5) -> float:
     """Best device-to-device copy rate, counting bytes read plus bytes written."""
     import torch
@@ -596,6 +616,7 @@ def main() -> int:
     clk_before = clock_probe_read(clk_before_out)
     clk_after = clock_probe_read(clk_out)
     smi_after = smi_snapshot()
+    smi_load = smi_under_load(call)
     durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
     region_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = region_ms / K
@@ -637,7 +658,8 @@ def main() -> int:
         "wall_s_timed_region": round(wall, 3),
         "clock": {"warmup_untimed_s": args.clock_warmup_s,
                   "sclk_mhz_device_before": clk_before, "sclk_mhz_device_after": clk_after,
-                  "smi_before": smi_before, "smi_after": smi_after},
+                  "smi_before": smi_before, "smi_after": smi_after,
+                  "smi_under_load_after": smi_load},
     }
     peaks = measured_peaks(dev, stream, cus)
     mpk = peaks["valu_fma_f32"] if is_valu else peaks["mfma_f32_32x32x2"]
