@@ -390,6 +390,9 @@ Variant kMfmaDirect = {"mfma_direct", check_direct, launch_direct,
 // through LDS (deterministic) and the epilogue writes C.
 // ===========================================================================
 constexpr int SK_BM = 16, SK_BN = 32, SK_WAVES = 16, SK_KB = 32;  // k per block
+#ifndef SGEMM_SKINNY_XCD
+#define SGEMM_SKINNY_XCD 1
+#endif
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x2 buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -397,13 +400,18 @@ __device__ __forceinline__ f32x2 buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 template <bool VEC, bool TA = false, bool TB = false, bool TC = false>
-__global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_n) {
+__global__ __launch_bounds__(1024) void k_mfma_skinny(Args a, int tiles_m, int tiles_n, int xcd_remap) {
     // Rows padded to 68 floats: in the reduction below, the two 16-lane
     // halves of a half-wave read the two column blocks, 4 rows apart, which
     // the pad puts 16 banks apart (with 64 floats they shared banks).
     __shared__ float red[SK_WAVES][2][4][68];
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-    const int m0 = tm * SK_BM, n0 = tn * SK_BN;
+    // With xcd_remap, neighbouring tiles on one XCD (workgroup i runs on XCD
+    // i mod 8): two neighbours share the cache lines their rows of B straddle
+    // when a row of B is not whole 128-byte lines, and one XCD's L2 then
+    // fetches such a line once (see launch_skinny).
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, 1, xcd_remap != 0, tm, tn);
+    const int m0 = __builtin_amdgcn_readfirstlane(tm * SK_BM), n0 = __builtin_amdgcn_readfirstlane(tn * SK_BN);
     const int rows_valid = (a.M - m0) < SK_BM ? (a.M - m0) : SK_BM;
     const int cols_valid = (a.N - n0) < SK_BN ? (a.N - n0) : SK_BN;
     // The wave index in a scalar register: the blocks a wave takes, and so
@@ -573,20 +581,28 @@ static int check_skinny(const Args& a) {
 }
 
 static hipError_t launch_skinny(const Args& a, hipStream_t s) {
-    const int tn = (int)cdiv(a.N, SK_BN);
-    const dim3 grid((unsigned)(cdiv(a.M, SK_BM) * tn)), block(1024);
+    const int tm = (int)cdiv(a.M, SK_BM), tn = (int)cdiv(a.N, SK_BN);
+    const dim3 grid((unsigned)(tm * tn)), block(1024);
+    // Neighbouring tiles on one XCD when B's rows straddle 128-byte lines
+    // (a pitch or base that is not whole lines) or B is read transposed:
+    // 16x8191x8192 73.1 -> 43.4 us back to back, 8192x16x8192 (the few-column
+    // product, run transposed) 51.5 -> 45.8, B transposed 52.8 -> 50.1. With
+    // whole lines of an untransposed B the workgroups stay in dispatch order,
+    // which streams a cold B 3% faster (16x8192x8192 53.2 against 54.8 us).
+    const bool partial_lines = a.tb || (a.ldb & 31) || ((uintptr_t)a.B & 127);
+    const int xr = (SGEMM_SKINNY_XCD && partial_lines) ? xcd_remap_enabled() : 0;
     const bool vec = small_vec_ok(a);
     return with_trans(a, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (a.tc) {
             if (vec)
-                hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB, true>), grid, block, 0, s, a, tn);
+                hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB, true>), grid, block, 0, s, a, tm, tn, xr);
             else
-                hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB, true>), grid, block, 0, s, a, tn);
+                hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB, true>), grid, block, 0, s, a, tm, tn, xr);
         } else if (vec) {
-            hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB>), grid, block, 0, s, a, tn);
+            hipLaunchKernelGGL((k_mfma_skinny<true, TA, TB>), grid, block, 0, s, a, tm, tn, xr);
         } else {
-            hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB>), grid, block, 0, s, a, tn);
+            hipLaunchKernelGGL((k_mfma_skinny<false, TA, TB>), grid, block, 0, s, a, tm, tn, xr);
         }
         return hipGetLastError();
     });
