@@ -104,7 +104,10 @@ def _buf(x: Optional[np.ndarray], rows: int, cols: int, name: str) -> Tuple[int,
     if x.size == 0:                 # numpy gives empty arrays zero strides
         return x.ctypes.data, max(1, cols), x
     if x.strides[1] != 4 or x.strides[0] % 4 != 0 or x.strides[0] < 4 * x.shape[1]:
-        x = np.ascontiguousarray(x)
+        # A fresh copy: numpy calls a one-row (or one-column) view C-contiguous
+        # whatever its strides, so ascontiguousarray may hand back a row
+        # stride below the row length (a transposed (n, 1) column, say).
+        x = np.array(x, dtype=np.float32, order="C", copy=True)
     ld = x.strides[0] // 4
     return x.ctypes.data, max(ld, 1), x
 

@@ -294,3 +294,58 @@ def test_gemm_helper_takes_transposed_views(dev):
                                    2.0, -1.0)
         rep = check_exact(np.ascontiguousarray(C_dev.cpu().numpy()), Cref)
         assert rep.ok, rep
+
+
+# Seeded random calls through the automatic choice, without a workspace
+# (sgemm_f32_ex) and with one (sgemm_f32_ws): sides log-uniform in [1, 1200]
+# (eight in [1200, 3000]), every storage order and transposition, padded
+# leading dimensions, misaligned bases, alpha and beta from small sets;
+# integer inputs (bit for bit) and uniform ones (the error bound). The
+# dispatch takes every kernel family on some of them, each with its edge and
+# fill paths.
+def _random_cases(n, n_large, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n + n_large):
+        hi = 1200 if i < n else 3000
+        lo = 1 if i < n else 1200
+        M, N, K = (int(round(np.exp(rng.uniform(np.log(lo), np.log(hi))))) for _ in range(3))
+        layout, ta, tb = COMBOS[int(rng.integers(len(COMBOS)))]
+        alpha = float(rng.choice([1.0, -1.0, 2.0, 0.5]))
+        beta = float(rng.choice([0.0, 0.0, 1.0, 0.5, -2.0]))
+        dist = "integer" if i % 2 == 0 else "uniform"
+        pads = tuple(int(x) for x in rng.choice([0, 0, 1, 3, 4, 7], size=3))
+        offsets = tuple(int(x) for x in rng.choice([0, 0, 0, 1, 2, 3], size=3))
+        cases.append((M, N, K, alpha, beta, dist, pads, offsets, layout, ta, tb, bool(i % 3 == 0)))
+    return cases
+
+
+RANDOM = _random_cases(72, 8, 2026)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=lambda c: "x".join(map(str, c[:3])) + "-" +
+                         combo_id(c[8:11]) + ("-ws" if c[11] else ""))
+def test_random_calls_auto(dev, case):
+    M, N, K, alpha, beta, dist, pads, offsets, layout, ta, tb, use_ws = case
+    A, B, C, opA, opB = make_case(layout, ta, tb, M, N, K, dist, 900 + M + N + K, beta, pads)
+    if not use_ws:
+        rc, out = run_ex(None, layout, ta, tb, M, N, K, alpha, beta, A, B, C, dev, offsets,
+                         tag="random")
+    else:
+        fa, pa = to_dev(A.buf, dev, offsets[0])
+        fb, pb = to_dev(B.buf, dev, offsets[1])
+        fc, pc = to_dev(C.buf, dev, offsets[2])
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        rc, wsb = sg.sgemm_f32_ws_size(-1, layout, ta, tb, M, N, K, cus)
+        assert rc == 0
+        ws = torch.full((max(wsb, 16),), 0xFF, dtype=torch.uint8, device=dev)
+        print(f"[gpu] random ws layout={layout} ta={ta} tb={tb} M={M} N={N} K={K} "
+              f"ld=({A.ld},{B.ld},{C.ld}) off={offsets} ws={wsb}", flush=True)
+        rc = sg.sgemm_f32_ws(layout, ta, tb, M, N, K, alpha, pa, A.ld, pb, B.ld, beta, pc, C.ld,
+                             ws, wsb, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        out = fc[offsets[2]:].cpu().numpy().reshape(C.buf.shape)
+        del fa, fb, fc, ws
+    assert rc == 0, sg.sgemm_f32_strerror(rc)
+    rep = check(out, C, opA, opB, M, N, K, alpha, beta, exact=(dist == "integer"))
+    assert rep.ok, f"{case}: {rep}"

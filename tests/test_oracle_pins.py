@@ -289,3 +289,20 @@ def test_rejects_bad_arguments(lib):
         oracle.sgemm_ref_rows(A, B, None, 1.0, 0.0, [4], lib=lib)
     with pytest.raises(ValueError):
         oracle.sgemm_ref_cols(A, B, None, 1.0, 0.0, [-1], lib=lib)
+
+
+def test_views_whose_strides_numpy_does_not_canonicalise():
+    # A transposed (n, 1) column is a (1, n) view with a row stride of one
+    # float; numpy calls it C-contiguous as it stands. The oracle must still
+    # read it as a row of n values (as C0, B or A), and a (1, 1) view with a
+    # column stride of two floats as its one value.
+    n = 939
+    col = np.arange(n, dtype=np.float32).reshape(n, 1)
+    row = col.T
+    assert row.strides[0] < 4 * n
+    a = np.full((4, 2), 3.0, np.float32)[:1, ::2]          # (1, 1), strides (8, 8)
+    Cref, _ = oracle.sgemm_ref(a, row, row, 1.0, 0.5)
+    assert np.array_equal(Cref[0], 3.0 * np.arange(n) + 0.5 * np.arange(n))
+    Cref2, _ = oracle.sgemm_ref(row, col, None, 1.0, 0.0)   # 1 x n times n x 1: a dot product
+    assert Cref2.shape == (1, 1) and Cref2[0, 0] == float(np.dot(np.arange(n, dtype=np.float64),
+                                                                   np.arange(n, dtype=np.float64)))
