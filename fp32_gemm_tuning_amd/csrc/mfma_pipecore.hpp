@@ -35,10 +35,32 @@ namespace sgemm {
 // order per accumulator is unchanged). Instructions past the pattern's counts
 // (the transposed and 4-byte-fill instances read and load more) are placed
 // by the scheduler.
-template <int LOADS>
+// FRONT, for parts of at most 8 MFMAs (wave tiles of one or two 32x32
+// blocks, one or two waves per SIMD): the reads go out in pairs after each
+// of the first two MFMAs, and the loads in pairs after the next three, so
+// every read has at least six MFMAs to land instead of two. With few waves
+// per SIMD no other wave covers a read that arrives late (interleaved A/B,
+// bit-identical: 512x4096x4096 on the 64x128 tile 127.4 -> 123.8 us back
+// to back, on the 64x64 tile 127.3 -> 124.2, 3072^3 411.3 -> 406.8, 2048^3
+// 122.4 -> 121.5). The 16-MFMA parts of the 256x256 tile keep the pattern
+// above (front-loaded there, the headline instance spills).
+template <int LOADS, bool FRONT = false>
 __device__ __forceinline__ void weave_half() {
     constexpr int MFMA = 0x008, VMEM_READ = 0x020, DS_READ = 0x100;
-    if constexpr (LOADS == 0) {
+    if constexpr (FRONT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(DS_READ, 2, 0);
+        }
+        if constexpr (LOADS > 0) {
+#pragma unroll
+            for (int l = 0; l < 3; ++l) {
+                __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(VMEM_READ, 2, 0);
+            }
+        }
+    } else if constexpr (LOADS == 0) {
 #pragma unroll
         for (int i = 0; i < 6; ++i) {
             __builtin_amdgcn_sched_group_barrier(MFMA, 2, 0);
@@ -120,6 +142,9 @@ struct PipeCore {
     // count fits the 6-bit field.
     static constexpr int PROLOGUE_VMCNT = (Dma::EVEN && (STAGES - 1) * G < 64) ? (STAGES - 1) * G : 0;
     static constexpr int LDS_A = BM * APITCH, LDS_B = BK * BNP;
+    // Front-loaded weave (weave_half) for parts of at most 8 MFMAs, with the
+    // 16-byte fills: the 4-byte-fill forms of the 64x128 tile would spill.
+    static constexpr bool FRONT = 4 * BI * BJ <= 8 && (VEC || U16);
 
     int m0, n0, rows_valid, cols_valid, t, wm, wn, h, c;
 
@@ -276,7 +301,7 @@ struct PipeCore {
                     mma_part(f1);
                 else
                     mma_part(f0);
-                weave_half<0>();
+                weave_half<0, FRONT>();
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -304,7 +329,7 @@ struct PipeCore {
             read_part(f0, An, Bn, 0);   // past the last slice: read and unused
             mma_part(f1);
             issue();
-            weave_half<U16 ? 0 : 2>();
+            weave_half<U16 ? 0 : 2, FRONT>();
             __builtin_amdgcn_sched_barrier(0);
         };
         // GUARD: the last step, whose slice exists only for groups with
